@@ -1,0 +1,318 @@
+"""fp64 CPU oracle for one tensor-parallel rank's share of a Transformer layer.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import this module.  The GPU library never imports it and
+shares no code with it; the oracle takes numpy arrays and returns numpy
+arrays.  The arithmetic lives in tp_oracle.c (plain loops, fp64); this file
+only marshals arguments.
+
+Every function cites the passage of the pages it follows in tp_oracle.c.
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+(worked examples the pages print, closed forms, library routines the pages
+themselves call, brute force and invariants).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_f64p = ctypes.POINTER(ctypes.c_double)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+class RingStep(ctypes.Structure):
+    _fields_ = [("phase", ctypes.c_int), ("step", ctypes.c_int),
+                ("src", ctypes.c_int), ("dst", ctypes.c_int),
+                ("chunk", ctypes.c_int), ("offset", ctypes.c_int64),
+                ("len", ctypes.c_int64)]
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "orc_silu": (ctypes.c_double, [ctypes.c_double]),
+        "orc_f32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
+        "orc_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "orc_f32_to_bf16_array": (None, [_f32p, _i64, _u16p]),
+        "orc_bf16_to_f64_array": (None, [_u16p, _i64, _f64p]),
+        "orc_linear": (None, [_f64p, _i64, _i64, _f64p, _i64, _f64p, _f64p]),
+        "orc_mlp": (None, [_f64p, _i64, _i64, _f64p, _f64p, _i64, _f64p, _f64p]),
+        "orc_mlp_rank": (None, [_f64p, _i64, _i64, _f64p, _f64p, _i64, _f64p,
+                                _int, _int, _f64p]),
+        "orc_silu_mul": (None, [_f64p, _f64p, _i64, _f64p]),
+        "orc_narrow": (_int, [_vp, _i64, _i64, _int, _int, _i64, _i64, _vp]),
+        "orc_shard": (_int, [_vp, _i64, _i64, _int, _int, _int, _int, _vp]),
+        "orc_shard_gate_up": (_int, [_vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+        "orc_kv_heads_for_rank": (_int, [_i64, _int, _int, _i64p, _i64p]),
+        "orc_shard_qkv": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                                 _int, _int, _vp]),
+        "orc_vocab_range": (_int, [_i64, _int, _int, _i64p, _i64p]),
+        "orc_embed_full": (None, [_i64p, _i64, _vp, _i64, _i64, _int, _vp]),
+        "orc_embed_rank": (_int, [_i64p, _i64, _vp, _i64, _i64, _int, _int, _int, _vp]),
+        "orc_lm_head_rank": (_int, [_f64p, _i64, _i64, _f64p, _i64, _int, _int, _f64p]),
+        "orc_chunk_bounds": (None, [_i64, _int, _int, _i64p, _i64p]),
+        "orc_ring_schedule": (_int, [_int, _i64, ctypes.POINTER(RingStep), _int]),
+        "orc_ring_allreduce_f32": (_int, [ctypes.POINTER(_f32p), _int, _i64, _i64,
+                                          _i64, _f32p]),
+        "orc_reduce_sum_f64": (None, [ctypes.POINTER(_f64p), _int, _i64, _f64p]),
+        "orc_ring_traffic": (_int, [_int, _i64, _i64p, _i64p, ctypes.POINTER(ctypes.c_int)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what}: oracle status {rc}")
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+# --- scalar / conversion --------------------------------------------------
+
+def silu(z: float) -> float:
+    return _load().orc_silu(float(z))
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round fp32 values to bfloat16 (round-to-nearest-even); returns uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().orc_f32_to_bf16_array(_p(a, _f32p), a.size, _p(out, _u16p))
+    return out
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().orc_bf16_to_f64_array(_p(b, _u16p), b.size, _p(out, _f64p))
+    return out
+
+
+# --- linear / MLP ---------------------------------------------------------
+
+def linear(x, w, bias=None) -> np.ndarray:
+    """y = x . w^T (+ bias), weights stored [out, in]."""
+    x, w = _f64(x), _f64(w)
+    n, k = x.shape
+    m, k2 = w.shape
+    assert k == k2
+    y = np.empty((n, m), dtype=np.float64)
+    b = _f64(bias) if bias is not None else None
+    _load().orc_linear(_p(x, _f64p), n, k, _p(w, _f64p), m,
+                       _p(b, _f64p) if b is not None else None, _p(y, _f64p))
+    return y
+
+
+def mlp(x, gate, up, down) -> np.ndarray:
+    """Unsharded SwiGLU MLP: (SiLU(x gate^T) * (x up^T)) down^T."""
+    x, gate, up, down = _f64(x), _f64(gate), _f64(up), _f64(down)
+    n, h = x.shape
+    f = gate.shape[0]
+    assert gate.shape == (f, h) and up.shape == (f, h) and down.shape == (h, f)
+    y = np.empty((n, h), dtype=np.float64)
+    _load().orc_mlp(_p(x, _f64p), n, h, _p(gate, _f64p), _p(up, _f64p), f,
+                    _p(down, _f64p), _p(y, _f64p))
+    return y
+
+
+def mlp_rank(x, gate, up, down, tp_rank, tp_size) -> np.ndarray:
+    """Rank tp_rank's full-shape [n, h] partial, from the FULL weights."""
+    x, gate, up, down = _f64(x), _f64(gate), _f64(up), _f64(down)
+    n, h = x.shape
+    f = gate.shape[0]
+    assert f % tp_size == 0
+    y = np.empty((n, h), dtype=np.float64)
+    _load().orc_mlp_rank(_p(x, _f64p), n, h, _p(gate, _f64p), _p(up, _f64p), f,
+                         _p(down, _f64p), tp_rank, tp_size, _p(y, _f64p))
+    return y
+
+
+def silu_mul(g, u) -> np.ndarray:
+    g, u = _f64(g), _f64(u)
+    assert g.shape == u.shape
+    out = np.empty(g.shape, dtype=np.float64)
+    _load().orc_silu_mul(_p(g, _f64p), _p(u, _f64p), g.size, _p(out, _f64p))
+    return out
+
+
+# --- shard selection (bit-exact, any element type) -------------------------
+
+def _es(a):
+    return a.dtype.itemsize
+
+
+def narrow(full, dim, start, length) -> np.ndarray:
+    full = np.ascontiguousarray(full)
+    rows, cols = full.shape
+    shape = (length, cols) if dim == 0 else (rows, length)
+    out = np.empty(shape, dtype=full.dtype)
+    _check(_load().orc_narrow(full.ctypes.data, rows, cols, _es(full), dim, start,
+                              length, out.ctypes.data), "narrow")
+    return out
+
+
+def shard(full, dim, tp_rank, tp_size) -> np.ndarray:
+    full = np.ascontiguousarray(full)
+    rows, cols = full.shape
+    s = rows if dim == 0 else cols
+    if s % tp_size:
+        raise OracleError("shard: size not divisible by tp_size")
+    shape = (rows // tp_size, cols) if dim == 0 else (rows, cols // tp_size)
+    out = np.empty(shape, dtype=full.dtype)
+    _check(_load().orc_shard(full.ctypes.data, rows, cols, _es(full), dim, tp_rank,
+                             tp_size, out.ctypes.data), "shard")
+    return out
+
+
+def shard_gate_up(gate, up, tp_rank, tp_size) -> np.ndarray:
+    gate, up = np.ascontiguousarray(gate), np.ascontiguousarray(up)
+    assert gate.shape == up.shape and gate.dtype == up.dtype
+    f, h = gate.shape
+    out = np.empty((2 * (f // tp_size), h), dtype=gate.dtype)
+    _check(_load().orc_shard_gate_up(gate.ctypes.data, up.ctypes.data, f, h, _es(gate),
+                                     tp_rank, tp_size, out.ctypes.data), "shard_gate_up")
+    return out
+
+
+def kv_heads_for_rank(n_kv, tp_rank, tp_size):
+    first, count = ctypes.c_int64(), ctypes.c_int64()
+    _check(_load().orc_kv_heads_for_rank(n_kv, tp_rank, tp_size, ctypes.byref(first),
+                                         ctypes.byref(count)), "kv_heads_for_rank")
+    return first.value, count.value
+
+
+def shard_qkv(wq, wk, wv, n_q, n_kv, head_dim, tp_rank, tp_size) -> np.ndarray:
+    wq, wk, wv = (np.ascontiguousarray(a) for a in (wq, wk, wv))
+    h = wq.shape[1]
+    _, kvc = kv_heads_for_rank(n_kv, tp_rank, tp_size)
+    rows = (n_q // tp_size + 2 * kvc) * head_dim
+    out = np.empty((rows, h), dtype=wq.dtype)
+    _check(_load().orc_shard_qkv(wq.ctypes.data, wk.ctypes.data, wv.ctypes.data, n_q,
+                                 n_kv, head_dim, h, _es(wq), tp_rank, tp_size,
+                                 out.ctypes.data), "shard_qkv")
+    return out
+
+
+# --- vocab parallel ----------------------------------------------------------
+
+def vocab_range(vocab, tp_rank, tp_size):
+    s, e = ctypes.c_int64(), ctypes.c_int64()
+    _check(_load().orc_vocab_range(vocab, tp_rank, tp_size, ctypes.byref(s),
+                                   ctypes.byref(e)), "vocab_range")
+    return s.value, e.value
+
+
+def embed_full(ids, table) -> np.ndarray:
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    table = np.ascontiguousarray(table)
+    V, h = table.shape
+    out = np.empty((ids.size, h), dtype=table.dtype)
+    _load().orc_embed_full(_p(ids, _i64p), ids.size, table.ctypes.data, V, h,
+                           _es(table), out.ctypes.data)
+    return out
+
+
+def embed_rank(ids, table_shard, vocab, tp_rank, tp_size) -> np.ndarray:
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    table_shard = np.ascontiguousarray(table_shard)
+    h = table_shard.shape[1]
+    s, e = vocab_range(vocab, tp_rank, tp_size)
+    if table_shard.shape[0] != e - s:
+        raise OracleError("embed_rank: shard rows != end - start")
+    out = np.empty((ids.size, h), dtype=table_shard.dtype)
+    _check(_load().orc_embed_rank(_p(ids, _i64p), ids.size, table_shard.ctypes.data,
+                                  vocab, h, _es(table_shard), tp_rank, tp_size,
+                                  out.ctypes.data), "embed_rank")
+    return out
+
+
+def lm_head_rank(x, table_full, tp_rank, tp_size) -> np.ndarray:
+    x, table_full = _f64(x), _f64(table_full)
+    n, h = x.shape
+    V = table_full.shape[0]
+    s, e = vocab_range(V, tp_rank, tp_size)
+    out = np.empty((n, e - s), dtype=np.float64)
+    _check(_load().orc_lm_head_rank(_p(x, _f64p), n, h, _p(table_full, _f64p), V,
+                                     tp_rank, tp_size, _p(out, _f64p)), "lm_head_rank")
+    return out
+
+
+# --- ring all-reduce -----------------------------------------------------------
+
+def chunk_bounds(K, t, c):
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    _load().orc_chunk_bounds(K, t, c, ctypes.byref(lo), ctypes.byref(hi))
+    return lo.value, hi.value
+
+
+def ring_schedule(t, K):
+    n = 2 * t * (t - 1)
+    arr = (RingStep * max(n, 1))()
+    got = _load().orc_ring_schedule(t, K, arr, max(n, 1))
+    if got < 0:
+        raise OracleError("ring_schedule: buffer too small")
+    return [dict(phase=s.phase, step=s.step, src=s.src, dst=s.dst, chunk=s.chunk,
+                 offset=s.offset, len=s.len) for s in arr[:got]]
+
+
+def ring_traffic(t, K):
+    sent = (ctypes.c_int64 * t)()
+    recv = (ctypes.c_int64 * t)()
+    rounds = ctypes.c_int()
+    _check(_load().orc_ring_traffic(t, K, sent, recv, ctypes.byref(rounds)), "ring_traffic")
+    return list(sent), list(recv), rounds.value
+
+
+def ring_allreduce_f32(parts, lo=0, hi=None) -> np.ndarray:
+    """Simulate the ring all-reduce on t fp32 rank buffers over window [lo, hi)."""
+    parts = [np.ascontiguousarray(p, dtype=np.float32).reshape(-1) for p in parts]
+    t = len(parts)
+    K = parts[0].size
+    assert all(p.size == K for p in parts)
+    if hi is None:
+        hi = K
+    arr = (_f32p * t)(*[_p(p, _f32p) for p in parts])
+    out = np.empty(hi - lo, dtype=np.float32)
+    _check(_load().orc_ring_allreduce_f32(arr, t, K, lo, hi, _p(out, _f32p)),
+           "ring_allreduce_f32")
+    return out
+
+
+def reduce_sum_f64(parts) -> np.ndarray:
+    parts = [_f64(p).reshape(-1) for p in parts]
+    t = len(parts)
+    K = parts[0].size
+    arr = (_f64p * t)(*[_p(p, _f64p) for p in parts])
+    out = np.empty(K, dtype=np.float64)
+    _load().orc_reduce_sum_f64(arr, t, K, _p(out, _f64p))
+    return out

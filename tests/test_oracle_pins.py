@@ -1,0 +1,530 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself.  The pins are: the pages'
+printed worked examples (tests/golden/, each file names its passage), closed
+forms, the library routines the pages' own code calls (torch.nn.functional
+linear/silu/embedding, computed in float64), exactly representable integer
+cases, brute force on tiny shapes, and invariants the pages state (the row-
+parallel partials sum to the unsharded result, vocab shards sum to the full
+lookup, the ring moves 2(t-1)K/t elements per rank).  Each pin is chosen so
+that a plausible slip (a dropped term, a wrong sign or index, a transposed
+operand, SiLU on the wrong operand) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as fh:
+        return json.load(fh)
+
+
+def relf(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding: pinned to torch's own float32 -> bfloat16 conversion (RNE)
+# --------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(3.0),
+        rng.standard_normal(20000).astype(np.float32) * np.float32(1e-39),   # subnormals
+        np.clip(rng.standard_normal(20000) * 1e38, -3.4e38, 3.4e38).astype(np.float32),
+    ])
+    # exact ties: low half == 0x8000 with both parities of the kept bit
+    ties = (np.arange(0, 4096, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, -3.3895314e38,
+                        3.4028235e38, 1.0, -1.0, 1e-45], dtype=np.float32)
+    vals = np.concatenate([vals, ties, special]).astype(np.float32)
+    got = oracle.f32_to_bf16_bits(vals)
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_nan_stays_nan_and_widening_exact():
+    bits = oracle.f32_to_bf16_bits(np.array([np.nan], dtype=np.float32))
+    assert (int(bits[0]) & 0x7f80) == 0x7f80 and (int(bits[0]) & 0x7f) != 0
+    allbits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    w = oracle.bf16_bits_to_f64(allbits)
+    ref = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    finite = np.isfinite(ref)
+    assert np.array_equal(w[finite], ref[finite])
+    assert np.array_equal(np.isnan(w), np.isnan(ref))
+
+
+# --------------------------------------------------------------------------
+# SiLU: closed forms
+# --------------------------------------------------------------------------
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    # SiLU(z) - SiLU(-z) = z  (z*s(z) + z*s(-z)... rearranged: s(z) + s(-z) = 1)
+    for z in [0.3, 1.7, 5.0, 12.0]:
+        assert oracle.silu(z) - oracle.silu(-z) == pytest.approx(z, rel=1e-14)
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    assert oracle.silu(-800.0) == 0.0 or abs(oracle.silu(-800.0)) < 1e-300
+
+
+# --------------------------------------------------------------------------
+# Linear layers: the pages' printed worked examples (bit-exact integers)
+# --------------------------------------------------------------------------
+
+def test_column_parallel_worked_example():
+    g = gold("nano22_column_parallel.json")
+    full = np.repeat(np.array(g["full_row_labels"], dtype=np.float32)[:, None],
+                     g["in_features"], axis=1)
+    t = g["tp_size"]
+    for r in range(t):
+        w = oracle.shard(full, g["tp_dim"], r, t)
+        assert list(w.shape) == g["rank_weight_shape"]
+        assert w[:, 0].tolist() == g["rank_rows"][str(r)]
+        x = np.random.default_rng(r).standard_normal(g["input_shape"])
+        y = oracle.linear(x, w)
+        assert list(y.shape) == g["rank_output_shape"]
+
+
+def test_row_parallel_worked_example_with_rank0_bias():
+    g = gold("nano22_row_parallel.json")
+    W = np.array(g["weight"])
+    b = np.array(g["bias"])
+    x = np.array(g["x"])
+    t = g["tp_size"]
+    parts = []
+    for r in range(t):
+        w = oracle.shard(W, 1, r, t)
+        assert list(w.shape) == g["rank_weight_shape"]
+        assert w.tolist() == g["rank_cols"][str(r)]
+        xr = oracle.shard(x, 1, r, t)
+        parts.append(oracle.linear(xr, w, b if r == 0 else None))
+    assert parts[0].tolist() == g["partial_rank0_with_bias"]
+    assert parts[1].tolist() == g["partial_rank1_no_bias"]
+    s = oracle.reduce_sum_f64(parts).reshape(1, -1)
+    assert s.tolist() == g["all_reduce_sum"]
+    assert oracle.linear(x, W, b).tolist() == g["single_card"]
+    # the fp32 ring simulation gives the same exact integers
+    ring = oracle.ring_allreduce_f32([p.astype(np.float32) for p in parts])
+    assert ring.tolist() == g["all_reduce_sum"][0]
+
+
+def test_linear_matches_torch_functional_linear():
+    rng = np.random.default_rng(7)
+    for (n, k, m) in [(1, 1, 1), (3, 5, 7), (9, 16, 4), (2, 33, 17)]:
+        x = rng.standard_normal((n, k))
+        w = rng.standard_normal((m, k))
+        b = rng.standard_normal(m)
+        y = oracle.linear(x, w, b)
+        ref = F.linear(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b)).numpy()
+        assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+        # a transposed weight must not pass (non-square shapes chosen above)
+        if m == k and n > 1:
+            assert not np.allclose(oracle.linear(x, w.T.copy()), F.linear(
+                torch.from_numpy(x), torch.from_numpy(w)).numpy())
+
+
+# --------------------------------------------------------------------------
+# MLP
+# --------------------------------------------------------------------------
+
+def _torch_mlp(x, gate, up, down):
+    """The pages' own formulation: down(silu(gate(x)) * up(x)) with F.linear/F.silu."""
+    X, G, U, D = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (x, gate, up, down))
+    return F.linear(F.silu(F.linear(X, G)) * F.linear(X, U), D).numpy()
+
+
+@pytest.mark.parametrize("n,h,f", [(1, 8, 12), (3, 16, 24), (5, 8, 12), (4, 32, 48)])
+def test_mlp_matches_torch_functional(n, h, f):
+    rng = np.random.default_rng(n * 100 + h)
+    x = rng.standard_normal((n, h))
+    gate = rng.standard_normal((f, h)) * 0.3
+    up = rng.standard_normal((f, h)) * 0.3
+    down = rng.standard_normal((h, f)) * 0.3
+    y = oracle.mlp(x, gate, up, down)
+    assert np.allclose(y, _torch_mlp(x, gate, up, down), rtol=1e-12, atol=1e-13)
+    # SiLU on the wrong operand (up instead of gate) must fail
+    wrong = _torch_mlp(x, up, gate, down)
+    assert relf(y, wrong) > 1e-3
+
+
+def test_mlp_zero_gate_gives_exact_zero_and_tiny_closed_form():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 8))
+    up = rng.standard_normal((12, 8))
+    down = rng.standard_normal((8, 12))
+    y = oracle.mlp(x, np.zeros((12, 8)), up, down)
+    assert np.all(y == 0.0)
+    # h = f = 1: y = silu(x g) * (x u) * d
+    y1 = oracle.mlp(np.array([[1.0]]), np.array([[1.0]]), np.array([[2.0]]), np.array([[3.0]]))
+    assert y1[0, 0] == pytest.approx(6.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 4])
+@pytest.mark.parametrize("n,h,f", [(1, 8, 12), (3, 16, 24), (5, 8, 24)])
+def test_row_parallel_partials_sum_to_unsharded(t, n, h, f):
+    """AIInfraGuide 6.2 §1: Y = sum_i act(X A_i) B_i."""
+    rng = np.random.default_rng(t * 1000 + n * 10 + h)
+    x = rng.standard_normal((n, h))
+    gate = rng.standard_normal((f, h)) * 0.5
+    up = rng.standard_normal((f, h)) * 0.5
+    down = rng.standard_normal((h, f)) * 0.5
+    full = _torch_mlp(x, gate, up, down)
+    parts = [oracle.mlp_rank(x, gate, up, down, r, t) for r in range(t)]
+    assert np.allclose(sum(parts), full, rtol=1e-12, atol=1e-12)
+    if t == 1:
+        assert np.array_equal(parts[0], oracle.mlp(x, gate, up, down))
+    # each partial is the MLP restricted to the rank's slice, checked with
+    # torch on explicitly sliced weights
+    fl = f // t
+    for r in range(t):
+        sl = slice(r * fl, (r + 1) * fl)
+        ref = _torch_mlp(x, gate[sl], up[sl], down[:, sl])
+        assert np.allclose(parts[r], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_nonlinearity_before_reduce_is_wrong():
+    """vLLM source analysis 13, §2.2.2 demo: with the first matrix split along
+    its input dim the partial products must be summed BEFORE the nonlinearity;
+    applying it per rank and summing afterwards gives a different result."""
+    rng = np.random.default_rng(42)
+    n, h, f, t = 4, 16, 24, 2
+    x = rng.standard_normal((n, h))
+    gate = rng.standard_normal((f, h))
+    up = rng.standard_normal((f, h))
+    ok = oracle.silu_mul(oracle.linear(x, gate), oracle.linear(x, up))
+    wrong = 0
+    for r in range(t):
+        xr, gr, ur = oracle.shard(x, 1, r, t), oracle.shard(gate, 1, r, t), oracle.shard(up, 1, r, t)
+        wrong = wrong + oracle.silu_mul(oracle.linear(xr, gr), oracle.linear(xr, ur))
+    assert relf(wrong, ok) > 0.05
+    # while summing the pre-activation partials first is right
+    g = sum(oracle.linear(oracle.shard(x, 1, r, t), oracle.shard(gate, 1, r, t)) for r in range(t))
+    u = sum(oracle.linear(oracle.shard(x, 1, r, t), oracle.shard(up, 1, r, t)) for r in range(t))
+    assert np.allclose(oracle.silu_mul(g, u), ok, rtol=1e-12, atol=1e-12)
+
+
+def test_wrong_dim_gate_up_shard_fails_invariant():
+    """Sharding gate/up along the input dim (instead of the output dim) breaks
+    the sum of partials."""
+    rng = np.random.default_rng(5)
+    n, h, f, t = 3, 16, 16, 2
+    x = rng.standard_normal((n, h))
+    gate = rng.standard_normal((f, h))
+    up = rng.standard_normal((f, h))
+    down = rng.standard_normal((h, f))
+    full = oracle.mlp(x, gate, up, down)
+    fl = f // t
+    parts = []
+    for r in range(t):
+        xr = oracle.shard(x, 1, r, t)
+        g = oracle.linear(xr, oracle.shard(gate, 1, r, t))
+        u = oracle.linear(xr, oracle.shard(up, 1, r, t))
+        parts.append(oracle.linear(oracle.silu_mul(g, u), down))
+    assert relf(sum(parts), full) > 0.05
+
+
+# --------------------------------------------------------------------------
+# Merged tables and GQA replication
+# --------------------------------------------------------------------------
+
+def _by_head(num_heads, base, head_size, hidden):
+    rows = [[float(base + hh)] * hidden for hh in range(num_heads) for _ in range(head_size)]
+    return np.array(rows, dtype=np.float32)
+
+
+def test_merged_qkv_and_gate_up_worked_example():
+    g = gold("nano22_merged_double_cut.json")
+    q = g["qkv"]
+    wq = _by_head(q["num_q_heads"], q["q_base"], q["head_size"], q["hidden"])
+    wk = _by_head(q["num_kv_heads"], q["k_base"], q["head_size"], q["hidden"])
+    wv = _by_head(q["num_kv_heads"], q["v_base"], q["head_size"], q["hidden"])
+    t = q["tp_size"]
+    for r in range(t):
+        m = oracle.shard_qkv(wq, wk, wv, q["num_q_heads"], q["num_kv_heads"], q["head_size"], r, t)
+        c = m[:, 0].tolist()
+        exp = q[f"rank{r}"]
+        nq = len(exp["q"])
+        nk = len(exp["k"])
+        assert c[:nq] == exp["q"]
+        assert c[nq:nq + nk] == exp["k"]
+        assert c[nq + nk:] == exp["v"]
+    gu = g["gate_up"]
+    gate = np.full((gu["intermediate"], gu["hidden"]), gu["gate_fill"], dtype=np.float32)
+    up = np.full((gu["intermediate"], gu["hidden"]), gu["up_fill"], dtype=np.float32)
+    m0 = oracle.shard_gate_up(gate, up, 0, gu["tp_size"])
+    half = gu["intermediate"] // gu["tp_size"]
+    assert m0[:half, 0].tolist() == gu["rank0"]["gate_segment"]
+    assert m0[half:2 * half, 0].tolist() == gu["rank0"]["up_segment"]
+
+
+def test_gate_up_double_cut_is_not_a_cut_of_the_concatenation():
+    f, h, t = 8, 3, 4
+    gate = np.arange(f, dtype=np.float32)[:, None].repeat(h, 1)
+    up = 100 + np.arange(f, dtype=np.float32)[:, None].repeat(h, 1)
+    for r in range(t):
+        m = oracle.shard_gate_up(gate, up, r, t)
+        fl = f // t
+        assert m[:fl, 0].tolist() == list(range(r * fl, (r + 1) * fl))
+        assert m[fl:, 0].tolist() == [100 + v for v in range(r * fl, (r + 1) * fl)]
+
+
+def test_kv_head_counts_from_pages():
+    g = gold("kv_head_counts.json")
+    for c in g["cases"]:
+        t = c["tp"]
+        heads = []
+        for r in range(t):
+            first, count = oracle.kv_heads_for_rank(c["n_kv"], r, t)
+            assert count == c["kv_per_rank"]
+            heads.extend(range(first, first + count))
+        # every KV head stored exactly `replicas` times
+        for hh in range(c["n_kv"]):
+            assert heads.count(hh) == c["replicas"]
+        assert c["n_q"] // t == c["q_per_rank"]
+        if "f" in c:
+            assert c["f"] // t == c["f_per_rank"]
+
+
+@pytest.mark.parametrize("n_q,n_kv,t", [(64, 8, 16), (8, 2, 4), (8, 2, 8), (16, 8, 2), (4, 2, 2)])
+def test_gqa_replica_matches_query_group(n_q, n_kv, t):
+    """Rank r's KV head must be the one its own Q heads attend with (Q head j
+    reads KV head j // (n_q // n_kv))."""
+    qpr = n_q // t
+    group = n_q // n_kv
+    for r in range(t):
+        first, count = oracle.kv_heads_for_rank(n_kv, r, t)
+        need = sorted({j // group for j in range(r * qpr, (r + 1) * qpr)})
+        assert list(range(first, first + count)) == need
+
+
+def test_qkv_shard_outputs_are_slices_of_unsharded_projections():
+    rng = np.random.default_rng(11)
+    n, h, hd, nq, nkv, t = 5, 16, 4, 8, 2, 4
+    x = rng.standard_normal((n, h))
+    wq = rng.standard_normal((nq * hd, h))
+    wk = rng.standard_normal((nkv * hd, h))
+    wv = rng.standard_normal((nkv * hd, h))
+    Q = F.linear(torch.from_numpy(x), torch.from_numpy(wq)).numpy()
+    K = F.linear(torch.from_numpy(x), torch.from_numpy(wk)).numpy()
+    V = F.linear(torch.from_numpy(x), torch.from_numpy(wv)).numpy()
+    qpr = nq // t
+    for r in range(t):
+        first, count = oracle.kv_heads_for_rank(nkv, r, t)
+        y = oracle.linear(x, oracle.shard_qkv(wq, wk, wv, nq, nkv, hd, r, t))
+        qn = qpr * hd
+        kn = count * hd
+        assert np.allclose(y[:, :qn], Q[:, r * qn:(r + 1) * qn], rtol=1e-12, atol=1e-12)
+        assert np.allclose(y[:, qn:qn + kn], K[:, first * hd:(first + count) * hd], rtol=1e-12, atol=1e-12)
+        assert np.allclose(y[:, qn + kn:], V[:, first * hd:(first + count) * hd], rtol=1e-12, atol=1e-12)
+
+
+def test_o_proj_row_parallel_partials_sum_to_full():
+    """vLLM source analysis 13 §2.3: concatenating the heads' outputs and
+    projecting equals summing each rank's projection of its own heads."""
+    rng = np.random.default_rng(12)
+    n, hd, nq, h, t = 6, 4, 8, 12, 4
+    A = rng.standard_normal((n, nq * hd))
+    Wo = rng.standard_normal((h, nq * hd))
+    full = F.linear(torch.from_numpy(A), torch.from_numpy(Wo)).numpy()
+    parts = [oracle.linear(oracle.shard(A, 1, r, t), oracle.shard(Wo, 1, r, t)) for r in range(t)]
+    assert np.allclose(oracle.reduce_sum_f64(parts).reshape(n, h), full, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Vocab-parallel embedding and LM head
+# --------------------------------------------------------------------------
+
+def test_vocab_range_rule():
+    assert [oracle.vocab_range(151936, r, 2) for r in range(2)] == [(0, 75968), (75968, 151936)]
+    assert [oracle.vocab_range(11, r, 4) for r in range(4)] == [(0, 3), (3, 6), (6, 9), (9, 11)]
+    assert [oracle.vocab_range(10, r, 2) for r in range(2)] == [(0, 5), (5, 10)]
+    rs = [oracle.vocab_range(10, r, 8) for r in range(8)]
+    assert rs[:5] == [(0, 2), (2, 4), (4, 6), (6, 8), (8, 10)]
+    assert all(e - s == 0 for s, e in rs[5:])
+
+
+def test_vocab_embedding_demo_structure():
+    g = gold("vllm13_vocab_embedding.json")
+    V, h, t = g["vocab"], g["hidden"], g["tp_size"]
+    table = np.random.default_rng(42).standard_normal((V, h))
+    ids = np.array(g["ids"], dtype=np.int64).reshape(-1)
+    outs = []
+    for r in range(t):
+        s, e = oracle.vocab_range(V, r, t)
+        assert [s, e] == g["ranges"][r]
+        o = oracle.embed_rank(ids, table[s:e], V, r, t)
+        nz = np.any(o != 0, axis=1).reshape(np.array(g["ids"]).shape)
+        assert nz.tolist() == g[f"rank{r}_nonzero"]
+        outs.append(o)
+    assert np.array_equal(outs[0] + outs[1], table[ids])
+    ref = F.embedding(torch.from_numpy(ids), torch.from_numpy(table)).numpy()
+    assert np.array_equal(oracle.embed_full(ids, table), ref)
+
+
+@pytest.mark.parametrize("V", [10, 11])
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 8])
+def test_vocab_embedding_brute_force_edges(V, t):
+    h = 3
+    table = (np.arange(V * h, dtype=np.float32).reshape(V, h) + 1.0)
+    ids_set = set()
+    for r in range(t):
+        s, e = oracle.vocab_range(V, r, t)
+        ids_set |= {s - 1, s, e - 1, e}
+    ids_set |= {-1, 0, V - 1, V, V + 7, -(1 << 40)}
+    ids = np.array(sorted(ids_set), dtype=np.int64)
+    total = np.zeros((ids.size, h), dtype=np.float64)
+    owners = np.zeros(ids.size, dtype=np.int64)
+    for r in range(t):
+        s, e = oracle.vocab_range(V, r, t)
+        o = oracle.embed_rank(ids, table[s:e], V, r, t)
+        for i, v in enumerate(ids):
+            if s <= v < e:
+                assert np.array_equal(o[i], table[v])
+                owners[i] += 1
+            else:
+                assert np.all(o[i].view(np.uint32) == 0)   # +0.0 bits, never -0.0
+        total += o
+    valid = (ids >= 0) & (ids < V)
+    assert np.all(owners[valid] == 1) and np.all(owners[~valid] == 0)
+    assert np.array_equal(total.astype(np.float32), oracle.embed_full(ids, table))
+
+
+def test_masked_rows_do_not_read_the_table():
+    """Out-of-shard rows are written without reading the table: a NaN in the
+    table never leaks into a masked row (multiplying by a zero mask would)."""
+    V, h, t = 8, 4, 2
+    table = np.full((V, h), np.nan, dtype=np.float32)
+    ids = np.array([0, 5, 7, 2], dtype=np.int64)
+    o = oracle.embed_rank(ids, table[0:4], V, 0, t)
+    assert np.all(np.isnan(o[[0, 3]]))
+    assert np.all(o[[1, 2]].view(np.uint32) == 0)
+
+
+@pytest.mark.parametrize("t", [1, 2, 3])
+def test_lm_head_shards_concatenate_to_full_logits(t):
+    rng = np.random.default_rng(9)
+    n, h, V = 4, 8, 11
+    x = rng.standard_normal((n, h))
+    E = rng.standard_normal((V, h))
+    full = F.linear(torch.from_numpy(x), torch.from_numpy(E)).numpy()
+    cat = np.concatenate([oracle.lm_head_rank(x, E, r, t) for r in range(t)], axis=1)
+    assert cat.shape == full.shape
+    assert np.allclose(cat, full, rtol=1e-12, atol=1e-12)
+    # one-hot rows pick table columns exactly
+    onehot = np.eye(h)[[0, 3, 7]]
+    cat1 = np.concatenate([oracle.lm_head_rank(onehot, E, r, t) for r in range(t)], axis=1)
+    assert np.array_equal(cat1, E.T[[0, 3, 7]])
+
+
+# --------------------------------------------------------------------------
+# Ring all-reduce schedule and simulation
+# --------------------------------------------------------------------------
+
+def test_ring_rounds_and_traffic_from_pages():
+    g = gold("vllm13_ring_cost.json")
+    for N, rounds in g["rounds_at"].items():
+        N = int(N)
+        K = 8 * N * 1000
+        sent, recv, got_rounds = oracle.ring_traffic(N, K)
+        assert got_rounds == rounds
+        assert all(s == 2 * (N - 1) * K // N for s in sent)
+        assert all(r == 2 * (N - 1) * K // N for r in recv)
+    for N, rs in g["rs_rounds_at"].items():
+        sched = oracle.ring_schedule(int(N), 64)
+        assert max(s["step"] for s in sched if s["phase"] == 0) + 1 == rs
+
+
+@pytest.mark.parametrize("t,K", [(2, 16384 * 2), (4, 64 * 8192), (8, 8192 * 8192), (16, 8192 * 8192)])
+def test_ring_traffic_config_sizes(t, K):
+    sent, recv, rounds = oracle.ring_traffic(t, K)
+    assert rounds == 2 * (t - 1)
+    assert sent[0] == 2 * (t - 1) * K // t
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 5, 8])
+def test_ring_schedule_structure(t):
+    K = 37 * t + 5  # ragged chunk sizes
+    sched = oracle.ring_schedule(t, K)
+    assert len(sched) == 2 * t * (t - 1)
+    # chunk bounds partition [0, K)
+    bounds = [oracle.chunk_bounds(K, t, c) for c in range(t)]
+    assert bounds[0][0] == 0 and bounds[-1][1] == K
+    assert all(bounds[c][1] == bounds[c + 1][0] for c in range(t - 1))
+    for phase in (0, 1):
+        for s in range(t - 1):
+            step = [x for x in sched if x["phase"] == phase and x["step"] == s]
+            assert sorted(x["src"] for x in step) == list(range(t))
+            assert sorted(x["chunk"] for x in step) == list(range(t))   # all chunks move each round
+            assert all(x["dst"] == (x["src"] + 1) % t for x in step)
+    # after reduce-scatter every chunk has been added into t-1 times
+    adds = [0] * t
+    for x in sched:
+        if x["phase"] == 0:
+            adds[x["chunk"]] += 1
+    assert adds == [t - 1] * t
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 8])
+def test_ring_simulation_is_exact_on_representable_sums(t):
+    # distinct power-of-two scales per rank: every partial sum is exact in fp32
+    K = 10 * t + 3
+    parts = [np.full(K, float(1 << r), dtype=np.float32) * (1 + np.arange(K) % 7) for r in range(t)]
+    out = oracle.ring_allreduce_f32(parts)
+    assert np.array_equal(out, sum(p.astype(np.float64) for p in parts).astype(np.float32))
+
+
+def test_ring_chunk_accumulation_order():
+    """Pins the order the reading derives: chunk c is summed as
+    ((P_c + P_{c+1}) + P_{c+2}) ...  With 1 and two 2^-24 terms, 1 + 2^-24
+    rounds back to 1 (tie to even) while 2^-24 + 2^-24 + 1 is 1 + 2^-23."""
+    t, K = 3, 3
+    e = np.float32(2.0 ** -24)
+    one = np.float32(1.0)
+    # element i lies in chunk i
+    P0 = np.array([one, e, e], dtype=np.float32)
+    P1 = np.array([e, one, e], dtype=np.float32)
+    P2 = np.array([e, e, one], dtype=np.float32)
+    out = oracle.ring_allreduce_f32([P0, P1, P2])
+    # each chunk starts from the partial that holds the 1 -> result 1.0 everywhere
+    assert out.tolist() == [1.0, 1.0, 1.0]
+    # element i (chunk i) is summed (P_i + P_{i+1}) + P_{i+2}:
+    #   element 0, the 1 in P1: (e + 1) + e = 1            (both ties round to even)
+    #   element 1, the 1 in P0: (e + e) + 1 = 1 + 2^-23
+    #   element 2, the 1 in P2: (1 + e) + e = 1
+    # plain rank order (P0 + P1) + P2 would give [1, 1, 1 + 2^-23] and the
+    # reverse ring direction (P_i + P_{i-1}) + P_{i-2} would give
+    # [1 + 2^-23, 1, 1], so both slips fail.
+    P0 = np.array([e, one, e], dtype=np.float32)
+    P1 = np.array([one, e, e], dtype=np.float32)
+    P2 = np.array([e, e, one], dtype=np.float32)
+    out = oracle.ring_allreduce_f32([P0, P1, P2])
+    assert out.tolist() == [1.0, 1.0 + 2.0 ** -23, 1.0]
+
+
+@pytest.mark.parametrize("t", [2, 3, 4, 8, 16])
+def test_ring_simulation_within_sequential_sum_bound(t):
+    rng = np.random.default_rng(t)
+    K = 4096 + 5
+    parts = [rng.standard_normal(K).astype(np.float32) for _ in range(t)]
+    out = oracle.ring_allreduce_f32(parts).astype(np.float64)
+    exact = oracle.reduce_sum_f64(parts)
+    bound = (t - 1) * 2.0 ** -24 * sum(np.abs(p.astype(np.float64)) for p in parts) * 1.0001
+    assert np.all(np.abs(out - exact) <= bound)
+    # a window simulation equals the same elements of the full simulation
+    w = oracle.ring_allreduce_f32(parts, 1000, 3000)
+    assert np.array_equal(w, out[1000:3000].astype(np.float32))
