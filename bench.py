@@ -1,0 +1,422 @@
+"""Benchmark of one tensor-parallel rank's share of a Transformer layer on one MI355X.
+
+Step (the timed unit): one rank's MLP share at the Llama-3.1-70B prefill
+shape, one rank of TP=8 (n=8192 tokens, h=8192, f_local=3584, bf16):
+  fused column-parallel gate_up GEMM with the SiLU(gate)*up epilogue,
+  row-parallel down GEMM -> full-shape [8192, 8192] bf16 partial,
+  ring-order reduce of that partial with the 7 other ranks' partials.
+Inputs are resident in HBM before timing starts.  `value` is the MLP's
+TFLOP/s over its two launches (algorithmic FLOP / measured time);
+`ms_per_step` covers the whole step, reduce included.
+
+Further legs, each timed on its own with HIP events on the library's stream:
+decode MLP (n=64, one rank of TP=4, HBM-bound, weights rotated over 3
+copies so the 256 MB Infinity Cache cannot hold them), the reduce at 8 and 16
+ranks, the vocab-parallel embedding + LM head (TP=2), the attention
+projections at TP=16 and the fp32 Qwen3 MLP.  A bounded sample of the fp64
+CPU oracle is timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none|a,b]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from rank_sharded_layer_amd import tpshard as T  # noqa: E402
+
+METRIC = "rank-shard MLP TFLOP/s (n=8192) & HBM GB/s (n=64); partial-reduce GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class EventTimer:
+    """Accumulates elapsed time of bracketed regions with HIP events recorded
+    on torch's current stream (the stream every library call is issued on)."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def start(self, name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pairs.setdefault(name, []).append([ev, None])
+
+    def stop(self, name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pairs[name][-1][1] = ev
+
+    def ms(self, name):
+        """Average milliseconds per region."""
+        p = self.pairs[name]
+        return sum(a.elapsed_time(b) for a, b in p) / len(p)
+
+
+def gen(w, tid, shape, std):
+    return synth.normal(shape, std, w.seed(tid), w.dtype, device=DEV)
+
+
+# ---------------------------------------------------------------------------
+# main step: prefill MLP share + reduce
+# ---------------------------------------------------------------------------
+
+def prefill_setup():
+    w = synth.get("llama70b_prefill_tp8")
+    r = 0
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    gate = gen(w, synth.T_GATE, (w.f, w.h), 0.02)
+    up = gen(w, synth.T_UP, (w.f, w.h), 0.02)
+    down = gen(w, synth.T_DOWN, (w.h, w.f), 0.02)
+    wgu = T.tp_shard_gate_up(gate, up, r, w.tp)
+    wd = T.tp_shard_weights(down, 1, r, w.tp)
+    del gate, up, down
+    fl = w.f_local
+    act = torch.empty((w.n, fl), dtype=w.dtype, device=DEV)
+    parts = [torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)]
+    parts += [gen(w, synth.T_PARTIAL + q, (w.n, w.h), 1.0) for q in range(1, w.tp)]
+    y = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
+    ws_gu = T.tp_gate_up_workspace_bytes(w.n, w.h, fl, w.dtype)
+    ws_dn = T.tp_linear_workspace_bytes(w.n, fl, w.h, w.dtype)
+    ws = torch.empty(max(ws_gu, ws_dn, 256), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    return dict(w=w, x=x, wgu=wgu, wd=wd, act=act, parts=parts, y=y, ws=ws)
+
+
+def prefill_step(S, tm=None):
+    if tm:
+        tm.start("gate_up")
+    T.tp_gate_up_act_rank(S["x"], S["wgu"], act=S["act"], workspace=S["ws"])
+    if tm:
+        tm.stop("gate_up")
+        tm.start("down")
+    T.tp_linear_rank_forward(S["act"], S["wd"], y=S["parts"][0], workspace=S["ws"])
+    if tm:
+        tm.stop("down")
+        tm.start("reduce")
+    T.tp_partial_reduce(S["parts"], out=S["y"])
+    if tm:
+        tm.stop("reduce")
+
+
+def mlp_flops(n, h, fl):
+    return 2.0 * n * h * (2 * fl) + 2.0 * n * fl * h
+
+
+# ---------------------------------------------------------------------------
+# legs
+# ---------------------------------------------------------------------------
+
+def leg_decode(reps):
+    w = synth.get("llama70b_decode_tp4")
+    fl = w.f_local
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    gate = gen(w, synth.T_GATE, (w.f, w.h), 0.02)
+    up = gen(w, synth.T_UP, (w.f, w.h), 0.02)
+    down = gen(w, synth.T_DOWN, (w.h, w.f), 0.02)
+    # three ranks' shards as rotating copies: 3 x 352 MB, more than the 256 MB MALL
+    copies = [(T.tp_shard_gate_up(gate, up, r, w.tp), T.tp_shard_weights(down, 1, r, w.tp)) for r in range(3)]
+    del gate, up, down
+    act = torch.empty((w.n, fl), dtype=w.dtype, device=DEV)
+    part = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
+    ws = torch.empty(max(T.tp_gate_up_workspace_bytes(w.n, w.h, fl, w.dtype),
+                         T.tp_linear_workspace_bytes(w.n, fl, w.h, w.dtype), 256),
+                     dtype=torch.uint8, device=DEV)
+    parts = [gen(w, synth.T_PARTIAL + q, (w.n, w.h), 1.0) for q in range(w.tp)]
+    y = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
+    tm = EventTimer()
+    for i in range(3 + reps):
+        wgu, wd = copies[i % 3]
+        t_ = tm if i >= 3 else None
+        if t_:
+            t_.start("mlp")
+            t_.start("gate_up")
+        T.tp_gate_up_act_rank(x, wgu, act=act, workspace=ws)
+        if t_:
+            t_.stop("gate_up")
+            t_.start("down")
+        T.tp_linear_rank_forward(act, wd, y=part, workspace=ws)
+        if t_:
+            t_.stop("down")
+            t_.stop("mlp")
+            t_.start("reduce")
+        T.tp_partial_reduce(parts, out=y)
+        if t_:
+            t_.stop("reduce")
+    torch.cuda.synchronize()
+    wbytes = (2 * fl * w.h + w.h * fl) * 2
+    io = (w.n * w.h + 2 * w.n * fl + w.n * w.h) * 2      # x, act write+read, partial
+    mlp_ms = tm.ms("mlp")
+    red_bytes = (w.tp + 1) * w.n * w.h * 2
+    return {
+        "workload": w.name, "n": w.n, "h": w.h, "f_local": fl, "tp": w.tp,
+        "mlp_ms": mlp_ms, "gate_up_ms": tm.ms("gate_up"), "down_ms": tm.ms("down"),
+        "mlp_GBps": (wbytes + io) / mlp_ms / 1e6,
+        "mlp_hbm_frac": (wbytes + io) / mlp_ms / 1e6 / PEAK_HBM_GBPS,
+        "algorithmic_bytes": wbytes + io,
+        "mlp_TFLOPs": mlp_flops(w.n, w.h, fl) / mlp_ms / 1e9,
+        "reduce_ms": tm.ms("reduce"), "reduce_GBps": red_bytes / tm.ms("reduce") / 1e6,
+        "reduce_note": "4 x 1 MiB partials: launch/MALL bound, not an HBM-roofline claim",
+        "cold": "weights rotated over 3 rank copies (1.06 GB > 256 MB MALL)",
+    }
+
+
+def leg_reduce(name, reps):
+    w = synth.get(name)
+    parts = [gen(w, synth.T_PARTIAL + q, (w.n, w.h), 1.0) for q in range(w.tp)]
+    y = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
+    tm = EventTimer()
+    for i in range(2 + reps):
+        if i >= 2:
+            tm.start("reduce")
+        T.tp_partial_reduce(parts, out=y)
+        if i >= 2:
+            tm.stop("reduce")
+    torch.cuda.synchronize()
+    b = (w.tp + 1) * w.n * w.h * 2
+    ms = tm.ms("reduce")
+    del parts
+    return {"workload": name, "t": w.tp, "K": w.n * w.h, "ms": ms, "GBps": b / ms / 1e6,
+            "hbm_frac": b / ms / 1e6 / PEAK_HBM_GBPS, "algorithmic_bytes": b}
+
+
+def leg_vocab(reps):
+    w = synth.get("qwen3_vocab_tp2")
+    table = gen(w, synth.T_TABLE, (w.vocab, w.h), 0.02)
+    ids = synth.token_ids(w.n, w.vocab, w.seed(synth.T_IDS), device=DEV)
+    shards = [T.tp_shard_weights(table, 0, r, w.tp) for r in range(w.tp)]
+    del table
+    outs = [torch.empty((w.n, w.h), dtype=w.dtype, device=DEV) for _ in range(w.tp)]
+    xemb = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
+    v_local = shards[0].shape[0]
+    logits = torch.empty((w.n, v_local), dtype=torch.float32, device=DEV)
+    tm = EventTimer()
+    for i in range(2 + reps):
+        t_ = tm if i >= 2 else None
+        if t_:
+            t_.start("embed")
+        for r in range(w.tp):
+            T.tp_vocab_embed_rank(ids, shards[r], w.vocab, r, w.tp, out=outs[r])
+        if t_:
+            t_.stop("embed")
+            t_.start("reduce")
+        T.tp_partial_reduce(outs, out=xemb)
+        if t_:
+            t_.stop("reduce")
+            t_.start("lm_head")
+        T.tp_lm_head_rank(xemb, shards[1], logits=logits)
+        if t_:
+            t_.stop("lm_head")
+    torch.cuda.synchronize()
+    fl = 2.0 * w.n * w.h * v_local
+    by = v_local * w.h * 2 + w.n * w.h * 2 + w.n * v_local * 4
+    ms = tm.ms("lm_head")
+    return {"workload": w.name, "embed_ms_all_ranks": tm.ms("embed"), "reduce_ms": tm.ms("reduce"),
+            "lm_head_ms": ms, "lm_head_TFLOPs": fl / ms / 1e9, "lm_head_GBps": by / ms / 1e6,
+            "lm_head_hbm_frac": by / ms / 1e6 / PEAK_HBM_GBPS,
+            "lm_head_mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+
+
+def leg_attnproj(reps):
+    w = synth.get("llama70b_attnproj_tp16")
+    hd, t = w.head_dim, w.tp
+    r = 5
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    wq = gen(w, synth.T_WQ, (w.n_q * hd, w.h), 0.02)
+    wk = gen(w, synth.T_WK, (w.n_kv * hd, w.h), 0.02)
+    wv = gen(w, synth.T_WV, (w.n_kv * hd, w.h), 0.02)
+    wo = gen(w, synth.T_WO, (w.h, w.n_q * hd), 0.02)
+    wqkv = T.tp_shard_qkv(wq, wk, wv, w.n_q, w.n_kv, hd, r, t)
+    wo_r = T.tp_shard_weights(wo, 1, r, t)
+    del wq, wk, wv, wo
+    a_r = gen(w, synth.T_ATTN_OUT + r, (w.n, w.n_q // t * hd), 1.0)
+    qkv = torch.empty((w.n, wqkv.shape[0]), dtype=w.dtype, device=DEV)
+    part = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
+    tm = EventTimer()
+    for i in range(2 + reps):
+        t_ = tm if i >= 2 else None
+        if t_:
+            t_.start("qkv")
+        T.tp_linear_rank_forward(x, wqkv, y=qkv)
+        if t_:
+            t_.stop("qkv")
+            t_.start("o_proj")
+        T.tp_linear_rank_forward(a_r, wo_r, y=part)
+        if t_:
+            t_.stop("o_proj")
+    torch.cuda.synchronize()
+    fq = 2.0 * w.n * w.h * wqkv.shape[0]
+    fo = 2.0 * w.n * a_r.shape[1] * w.h
+    return {"workload": w.name, "qkv_ms": tm.ms("qkv"), "qkv_TFLOPs": fq / tm.ms("qkv") / 1e9,
+            "o_proj_ms": tm.ms("o_proj"), "o_proj_TFLOPs": fo / tm.ms("o_proj") / 1e9,
+            "qkv_mfma_frac": fq / tm.ms("qkv") / 1e9 / PEAK_BF16_TFLOPS,
+            "o_proj_mfma_frac": fo / tm.ms("o_proj") / 1e9 / PEAK_BF16_TFLOPS}
+
+
+def leg_qwen_fp32(reps):
+    w = synth.get("qwen3_mlp_tp2_fp32")
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    gate = gen(w, synth.T_GATE, (w.f, w.h), 0.02)
+    up = gen(w, synth.T_UP, (w.f, w.h), 0.02)
+    down = gen(w, synth.T_DOWN, (w.h, w.f), 0.02)
+    shards = [(T.tp_shard_gate_up(gate, up, r, w.tp), T.tp_shard_weights(down, 1, r, w.tp)) for r in range(w.tp)]
+    ws = torch.empty(T.tp_mlp_workspace_bytes(w.n, w.h, w.f_local, w.dtype), dtype=torch.uint8, device=DEV)
+    parts = [torch.empty((w.n, w.h), dtype=w.dtype, device=DEV) for _ in range(w.tp)]
+    y = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
+    tm = EventTimer()
+    for i in range(3 + reps):
+        t_ = tm if i >= 3 else None
+        if t_:
+            t_.start("layer")
+        for r in range(w.tp):
+            T.tp_mlp_rank_forward(x, shards[r][0], shards[r][1], partial=parts[r], workspace=ws)
+        T.tp_partial_reduce(parts, out=y)
+        if t_:
+            t_.stop("layer")
+    torch.cuda.synchronize()
+    return {"workload": w.name, "all_ranks_plus_reduce_us": tm.ms("layer") * 1e3,
+            "note": "latency bound at this size (19 MB of fp32 weights per rank)"}
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(S, budget_s=12.0):
+    """Times the fp64 oracle's rank-partial MLP on sampled token rows of the
+    same prefill workload.  Row-independent, so the rate (FLOP/s) carries
+    over to the full workload."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+    from tests.helpers import to_f64
+    w = S["w"]
+    fl = w.f_local
+    G = to_f64(S["wgu"][:fl])
+    U = to_f64(S["wgu"][fl:])
+    D = to_f64(S["wd"])
+    X = to_f64(S["x"][:256])
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    rows = max(1, min(cores, 256))
+    t0 = time.perf_counter()
+    oracle.mlp_rank(X[:rows], G, U, D, 0, 1)
+    dt = time.perf_counter() - t0
+    # scale the sample to the time budget (rows in multiples of the thread count)
+    more = int(budget_s / max(dt, 1e-3)) * rows
+    more = max(rows, min(more - more % rows, 256))
+    t0 = time.perf_counter()
+    oracle.mlp_rank(X[:more], G, U, D, 0, 1)
+    dt2 = time.perf_counter() - t0
+    flops = mlp_flops(more, w.h, fl)
+    return {"value": flops / dt2 / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{more} of {w.n} token rows of the rank's MLP share (fp64, {dt2:.1f} s)",
+            "full_workload_extrapolated_s": dt2 * w.n / more}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="all")
+    ap.add_argument("--no-cpu", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every tensor-parallel rank is emulated on a single device; "
+              "--gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    T.lib()
+
+    log("bench: setup prefill workload")
+    S = prefill_setup()
+    w = S["w"]
+    for _ in range(a.warmup):
+        prefill_step(S)
+    torch.cuda.synchronize()
+    tm = EventTimer()
+    log(f"bench: timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tm.start("step")
+    for _ in range(a.steps):
+        prefill_step(S, tm)
+    tm.stop("step")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = tm.ms("step") / a.steps
+    gu_ms, dn_ms, rd_ms = tm.ms("gate_up"), tm.ms("down"), tm.ms("reduce")
+    fl = w.f_local
+    mlp_ms = gu_ms + dn_ms
+    flops = mlp_flops(w.n, w.h, fl)
+    value = flops / mlp_ms / 1e9
+    gu_flops = 2.0 * w.n * w.h * 2 * fl
+    red_bytes = (w.tp + 1) * w.n * w.h * 2
+    log(f"bench: step {ms_step:.3f} ms (wall {wall * 1e3 / a.steps:.3f} ms): gate_up {gu_ms:.3f} "
+        f"down {dn_ms:.3f} reduce {rd_ms:.3f} -> {value:.1f} TFLOP/s")
+
+    legs = {}
+    names = ["decode", "reduce8", "reduce16", "vocab", "attnproj", "qwen_fp32"] if a.legs == "all" else \
+        ([] if a.legs == "none" else a.legs.split(","))
+    for nm in names:
+        log(f"bench: leg {nm}")
+        if nm == "decode":
+            legs[nm] = leg_decode(20)
+        elif nm == "reduce8":
+            legs[nm] = leg_reduce("llama70b_prefill_tp8", 20)
+        elif nm == "reduce16":
+            legs[nm] = leg_reduce("llama70b_attnproj_tp16", 10)
+        elif nm == "vocab":
+            legs[nm] = leg_vocab(20)
+        elif nm == "attnproj":
+            legs[nm] = leg_attnproj(10)
+        elif nm == "qwen_fp32":
+            legs[nm] = leg_qwen_fp32(50)
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not a.no_cpu:
+        log("bench: cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(S)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "h": w.h, "f_local": fl, "tp": w.tp,
+                   "step": "gate_up+SiLU*up GEMM, down GEMM, ring-order reduce of 8 partials",
+                   "value_over": "MLP launches (gate_up + down) inside the timed steps"},
+        "mlp_ms": round(mlp_ms, 4), "gate_up_ms": round(gu_ms, 4), "down_ms": round(dn_ms, 4),
+        "reduce_ms": round(rd_ms, 4), "reduce_GBps": round(red_bytes / rd_ms / 1e6, 1),
+        "step_TFLOPs_incl_reduce": round(flops / ms_step / 1e9, 2),
+        "roofline": {"kernel": "gate_up GEMM + SiLU*up epilogue", "bound": "mfma",
+                     "achieved": round(gu_flops / gu_ms / 1e9, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gu_flops / gu_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * tpshard.h -- C ABI of libtpshard: one tensor-parallel (TP) rank's share of a
+ * Transformer layer on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles shortened):
+ *   [VLLM13]  "vLLM source analysis 13 -- vLLM distributed inference: tensor
+ *             parallelism in detail"
+ *   [NANO22]  "Nano-vLLM source walkthrough no. 22 -- tensor parallelism (2):
+ *             code"
+ *   [SCRATCH] "Tensor parallelism: implemented from scratch" (AI-infra
+ *             handbook)
+ *   [GUIDE62] "AIInfraGuide 6.2 -- tensor-parallel inference"
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless the comment says HOST.  The caller
+ *     owns every buffer; the library keeps no pointer after a call returns and
+ *     allocates no device memory (scratch space comes in through `workspace`).
+ *   - Compute calls are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream).  They never synchronize the device.
+ *   - Tensors are dense and row-major.  A linear layer's weight is stored
+ *     [out, in] and the layer computes y = x . W^T ([NANO22] §2), so both GEMM
+ *     operands are contiguous along the reduction dimension.
+ *   - Element types: TP_BF16 (bfloat16 bits) and TP_F32.  Supported
+ *     (input, output) pairs: F32 -> F32, BF16 -> BF16, BF16 -> F32.  Products
+ *     accumulate in fp32; an output is rounded once (round-to-nearest-even).
+ *   - Errors: every argument is validated on the host before anything is
+ *     launched.  A failing call returns a non-zero tp_status, launches
+ *     nothing (TP_EHIP excepted: the launch itself failed), and leaves a
+ *     message in tp_last_error() (per thread).  Nothing aborts or prints.
+ *     Divisibility is an error, as the pages' divide() assertion makes it.
+ *   - Alignment: 16-byte aligned pointers and reduction sizes that are a
+ *     multiple of 8 (bf16) take the vector path; anything else takes a
+ *     slower element-wise path with identical results.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef TP_API
+#define TP_API __attribute__((visibility("default")))
+#endif
+
+#define TP_ABI_VERSION 1
+#define TP_MAX_RANKS 64
+
+typedef enum {
+    TP_OK = 0,
+    TP_EINVAL = 1,      /* bad argument: null pointer, rank outside [0, t), t outside [1, 64], n <= 0 ... */
+    TP_ESHAPE = 2,      /* sizes that do not divide, or buffers whose sizes do not match */
+    TP_EDTYPE = 3,      /* unsupported element type or (input, output) pair */
+    TP_EALIGN = 4,      /* reserved: no entry point currently requires alignment */
+    TP_EHIP = 5,        /* the HIP runtime reported an error on launch */
+    TP_EWORKSPACE = 6   /* workspace missing or smaller than the matching *_workspace_bytes query */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Summation order of tp_partial_reduce. */
+typedef enum {
+    TP_ORDER_RING = 0   /* ring reduce-scatter chunk order (see tp_partial_reduce) */
+} tp_order;
+
+/* One transfer of the ring all-reduce schedule (tp_ring_schedule). */
+typedef struct {
+    int phase;          /* 0 = reduce-scatter (receiver adds), 1 = all-gather (receiver overwrites) */
+    int step;           /* round within the phase, 0 .. t-2 */
+    int src;            /* sending rank */
+    int dst;            /* receiving rank = (src + 1) mod t */
+    int chunk;          /* chunk moved */
+    int64_t offset;     /* first element of the chunk */
+    int64_t len;        /* elements in the chunk */
+} tp_ring_step;
+
+/* ---- library ------------------------------------------------------------ */
+
+TP_API int tp_abi_version(void);                 /* TP_ABI_VERSION */
+TP_API const char* tp_last_error(void);          /* last error of this thread; "" after success; static storage */
+TP_API const char* tp_status_string(int status); /* "TP_OK", "TP_EINVAL", ... */
+
+/* ---- shard selection (load time) --------------------------------------- */
+
+/* out = full.narrow(dim, tp_rank * S/t, S/t) as a contiguous tensor, S =
+ * full.size(dim).  [NANO22] §3 (ColumnParallelLinear weight loader: dim 0,
+ * whole output rows) and §4 (RowParallelLinear: dim 1, input columns).
+ *   full [rows, cols]; out [rows/t, cols] (dim 0) or [rows, cols/t] (dim 1).
+ * TP_ESHAPE if t does not divide S; bit-exact copy. */
+TP_API tp_status tp_shard_weights(const void* full, int64_t rows, int64_t cols, tp_dtype dt,
+                           int dim, int tp_rank, int tp_size, void* out, void* stream);
+
+/* Fused gate_up table of rank r: rows [0, f/t) = gate rows [r f/t, (r+1) f/t),
+ * rows [f/t, 2f/t) = the same rows of up.  [NANO22] §5 (merged column-parallel
+ * "double cut": the projection picks the segment, the rank picks its chunk
+ * of that projection).  gate, up [f, h]; out [2 f/t, h].  TP_ESHAPE if t does
+ * not divide f. */
+TP_API tp_status tp_shard_gate_up(const void* gate, const void* up, int64_t f, int64_t h,
+                           tp_dtype dt, int tp_rank, int tp_size, void* out, void* stream);
+
+/* HOST-only.  KV heads held by rank r: for t <= n_kv, heads
+ * [r n_kv/t, (r+1) n_kv/t); for t > n_kv one head, r / (t/n_kv), each head
+ * being replicated on t/n_kv ranks ([GUIDE62] §2.2).  TP_ESHAPE if neither
+ * count divides the other. */
+TP_API tp_status tp_kv_heads_for_rank(int64_t n_kv, int tp_rank, int tp_size,
+                               int64_t* first /*HOST*/, int64_t* count /*HOST*/);
+
+/* Merged QKV table of rank r: [q heads ; k heads ; v heads], head_dim rows per
+ * head.  [NANO22] §5 (QKVParallelLinear segments q, k, v) with the GQA
+ * replication of tp_kv_heads_for_rank.  wq [n_q*hd, h], wk/wv [n_kv*hd, h];
+ * out [(n_q/t + 2*kv_count)*hd, h].  TP_ESHAPE if t does not divide n_q. */
+TP_API tp_status tp_shard_qkv(const void* wq, const void* wk, const void* wv,
+                       int64_t n_q, int64_t n_kv, int64_t head_dim, int64_t h,
+                       tp_dtype dt, int tp_rank, int tp_size, void* out, void* stream);
+
+/* ---- column-parallel gate_up with the local SiLU(gate)*up ---------------- */
+
+/* act = SiLU(x . G^T) * (x . U^T), G = w_gate_up rows [0, f_local),
+ * U = rows [f_local, 2 f_local).  [SCRATCH] "Implementation" (class TPMLP:
+ * gate/up column-parallel, SiLU(gate)*up local); [GUIDE62] §1 (the activation
+ * is element-wise, so it needs no communication).  Fused: gate and up
+ * products are never written; act is rounded once to dt.
+ *   x [n, h] dt; w_gate_up [2 f_local, h] dt; act [n, f_local] dt.
+ * workspace: at least tp_gate_up_workspace_bytes(...) bytes (may be 0). */
+TP_API tp_status tp_gate_up_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_dtype dt,
+                                     size_t* bytes /*HOST*/);
+TP_API tp_status tp_gate_up_act_rank(const void* x, int64_t n, int64_t h, const void* w_gate_up,
+                              int64_t f_local, tp_dtype dt, void* act,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- generic rank linear (row-parallel down / o_proj, column-parallel QKV) */
+
+/* y = x . w^T (+ bias).  Row-parallel layers pass the bias on rank 0 only, so
+ * that the sum over ranks adds it once ([NANO22] §4).
+ *   x [n, k] dt; w [m, k] dt; bias [m] dt or NULL; y [n, m] out_dt.
+ * workspace: at least tp_linear_workspace_bytes(...) bytes (may be 0). */
+TP_API tp_status tp_linear_workspace_bytes(int64_t n, int64_t k, int64_t m, tp_dtype dt,
+                                    size_t* bytes /*HOST*/);
+TP_API tp_status tp_linear_rank_forward(const void* x, int64_t n, int64_t k, const void* w,
+                                 int64_t m, const void* bias, tp_dtype dt, void* y,
+                                 tp_dtype out_dt, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* ---- the rank's MLP share ------------------------------------------------ */
+
+/* partial = (SiLU(x . G_r^T) * (x . U_r^T)) . D_r^T, the full-shape [n, h]
+ * partial sum of rank r ([GUIDE62] §1: Y = sum_i act(X A_i) B_i; [SCRATCH]
+ * TPMLP.forward).  Two launches: tp_gate_up_act_rank into the workspace,
+ * then tp_linear_rank_forward with the down shard.  No bias.
+ *   x [n, h] dt; w_gate_up [2 f_local, h] dt (gate rows first, as made by
+ *   tp_shard_gate_up); w_down [h, f_local] dt (tp_shard_weights dim 1);
+ *   partial [n, h] out_dt.  The activation is held in dt (bf16 for bf16).
+ * workspace: at least tp_mlp_workspace_bytes(...) bytes, 256-byte aligned. */
+TP_API tp_status tp_mlp_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_dtype dt,
+                                 size_t* bytes /*HOST*/);
+TP_API tp_status tp_mlp_rank_forward(const void* x, int64_t n, int64_t h, const void* w_gate_up,
+                              const void* w_down, int64_t f_local, tp_dtype dt,
+                              void* partial, tp_dtype out_dt,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- sum of the t partials (the all-reduce's arithmetic, one device) ----- */
+
+/* out = sum_r partials[r], element-wise over K elements, in the order a ring
+ * reduce-scatter adds them ([VLLM13] §1.1.1): the K elements are cut into t
+ * chunks [floor(c K/t), floor((c+1) K/t)); chunk c is accumulated in fp32 as
+ * ((P_c + P_{c+1}) + P_{c+2}) + ... + P_{c+t-1} (indices mod t) and rounded
+ * once to out_dt.  Deterministic and bit-reproducible; no atomics.
+ *   partials: HOST array of t device pointers, each [K] in_dt; out [K] out_dt
+ *   (may alias partials[c] only if t == 1).  1 <= t <= TP_MAX_RANKS. */
+TP_API tp_status tp_partial_reduce(const void* const* partials /*HOST array*/, int t, int64_t K,
+                            tp_dtype in_dt, void* out, tp_dtype out_dt, tp_order order,
+                            void* stream);
+
+/* HOST-only.  The ring all-reduce schedule that order follows: reduce-scatter
+ * round s, rank r sends chunk (r - s) mod t to (r+1) mod t, which adds it;
+ * all-gather round s, rank r sends chunk (r + 1 - s) mod t, which the
+ * receiver copies.  2 t (t-1) steps; each rank sends 2(t-1) K/t elements in
+ * 2(t-1) rounds ([VLLM13] §1.2).  steps: HOST array of max_steps entries. */
+TP_API tp_status tp_ring_schedule(int t, int64_t K, tp_ring_step* steps /*HOST*/, int max_steps,
+                           int* n_steps /*HOST*/);
+
+/* ---- vocab-parallel embedding and LM head -------------------------------- */
+
+/* HOST-only.  Rank r's vocab range: per = ceil(V/t), start = r per,
+ * end = min((r+1) per, V) ([SCRATCH] class VocabParallelEmbedding); a
+ * trailing rank may get an empty range. */
+TP_API tp_status tp_vocab_range(int64_t vocab, int tp_rank, int tp_size,
+                         int64_t* start /*HOST*/, int64_t* end /*HOST*/);
+
+/* out[i, :] = table_shard[ids[i] - start, :] if start <= ids[i] < end, else
+ * +0.0 (the table is not read for such rows).  [VLLM13] §2.4.1; [SCRATCH]
+ * VocabParallelEmbedding.forward.  Summing the t ranks' outputs (for example
+ * with tp_partial_reduce) gives the full lookup.  Ids outside [0, V) are not
+ * an error: every rank writes a zero row for them.
+ *   ids [n] int64; table_shard [end - start, h] dt; out [n, h] dt. */
+TP_API tp_status tp_vocab_embed_rank(const int64_t* ids, int64_t n, const void* table_shard,
+                              int64_t vocab, int64_t h, int tp_rank, int tp_size,
+                              tp_dtype dt, void* out, void* stream);
+
+/* logits_r = x . T_r^T, the rank's slice of the logits along vocab
+ * ([VLLM13] §2.4.2: Y_i = X E_i^T; the full logits are the concatenation).
+ *   x [n, h] dt; table_shard [v_local, h] dt; logits [n, v_local] out_dt. */
+TP_API tp_status tp_lm_head_rank(const void* x, int64_t n, int64_t h, const void* table_shard,
+                          int64_t v_local, tp_dtype dt, void* logits, tp_dtype out_dt,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

@@ -1,0 +1,359 @@
+// C entry points of libtpshard: argument validation, workspace layout and
+// kernel launches.  Every check happens on the host before anything is
+// launched; a failing check returns a status and leaves a message in a
+// per-thread buffer.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tp_status fail(tp_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+tp_status ok() {
+    g_err[0] = '\0';
+    return TP_OK;
+}
+
+tp_status hip_status(hipError_t e, const char* where) {
+    if (e != hipSuccess) return fail(TP_EHIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+    return ok();
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool valid_dt(tp_dtype dt) { return dt == TP_F32 || dt == TP_BF16; }
+
+bool valid_pair(tp_dtype in, tp_dtype out) {
+    return (in == TP_F32 && out == TP_F32) || (in == TP_BF16 && (out == TP_BF16 || out == TP_F32));
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 48;
+
+tp_status check_rank(int tp_rank, int tp_size) {
+    if (tp_size < 1 || tp_size > TP_MAX_RANKS)
+        return fail(TP_EINVAL, "tp_size %d outside [1, %d]", tp_size, TP_MAX_RANKS);
+    if (tp_rank < 0 || tp_rank >= tp_size)
+        return fail(TP_EINVAL, "tp_rank %d outside [0, %d)", tp_rank, tp_size);
+    return TP_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// workspace of the two MLP launches: act [n, f_local] then the split-K area
+struct MlpLayout {
+    tpk::GemmPlan gu, down;
+    size_t act_bytes, total;
+};
+
+MlpLayout mlp_layout(int64_t n, int64_t h, int64_t f_local, tp_dtype dt) {
+    MlpLayout L;
+    L.gu = tpk::plan_gemm(n, f_local, h, true, dt);
+    L.down = tpk::plan_gemm(n, h, f_local, false, dt);
+    L.act_bytes = align256((size_t)n * (size_t)f_local * tpk::dtype_size(dt));
+    size_t split = L.gu.ws_bytes > L.down.ws_bytes ? L.gu.ws_bytes : L.down.ws_bytes;
+    L.total = L.act_bytes + align256(split);
+    return L;
+}
+
+tp_status check_gemm_dims(int64_t n, int64_t k, int64_t m, const char* fn) {
+    if (n <= 0 || k <= 0 || m <= 0) return fail(TP_EINVAL, "%s: sizes must be positive (n=%lld k=%lld m=%lld)", fn,
+                                                (long long)n, (long long)k, (long long)m);
+    if (n > INT32_MAX / 2 || m > INT32_MAX / 2 || k > INT32_MAX / 2 || n * k > kMaxElems || m * k > kMaxElems ||
+        n * m > kMaxElems)
+        return fail(TP_ESHAPE, "%s: sizes too large", fn);
+    return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return TP_ABI_VERSION; }
+
+const char* tp_last_error(void) { return g_err; }
+
+const char* tp_status_string(int st) {
+    switch (st) {
+        case TP_OK: return "TP_OK";
+        case TP_EINVAL: return "TP_EINVAL";
+        case TP_ESHAPE: return "TP_ESHAPE";
+        case TP_EDTYPE: return "TP_EDTYPE";
+        case TP_EALIGN: return "TP_EALIGN";
+        case TP_EHIP: return "TP_EHIP";
+        case TP_EWORKSPACE: return "TP_EWORKSPACE";
+        default: return "TP_UNKNOWN";
+    }
+}
+
+// ---- shard selection -------------------------------------------------------
+
+tp_status tp_shard_weights(const void* full, int64_t rows, int64_t cols, tp_dtype dt, int dim, int tp_rank,
+                           int tp_size, void* out, void* stream) {
+    if (!full || !out) return fail(TP_EINVAL, "tp_shard_weights: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_shard_weights: bad dtype %d", (int)dt);
+    if (dim != 0 && dim != 1) return fail(TP_EINVAL, "tp_shard_weights: dim %d not 0 or 1", dim);
+    if (tp_status st = check_rank(tp_rank, tp_size)) return st;
+    if (rows <= 0 || cols <= 0 || rows * cols > kMaxElems)
+        return fail(TP_EINVAL, "tp_shard_weights: bad shape [%lld, %lld]", (long long)rows, (long long)cols);
+    const int64_t S = dim == 0 ? rows : cols;
+    if (S % tp_size) return fail(TP_ESHAPE, "tp_shard_weights: size %lld of dim %d not divisible by tp_size %d",
+                                 (long long)S, dim, tp_size);
+    const int64_t es = (int64_t)tpk::dtype_size(dt);
+    const int64_t sh = S / tp_size;
+    hipError_t e;
+    if (dim == 0) {
+        // whole rows: one contiguous block
+        const char* src = static_cast<const char*>(full) + (int64_t)tp_rank * sh * cols * es;
+        e = tpk::launch_copy2d(src, sh * cols * es, out, sh * cols * es, 1, sh * cols * es, as_stream(stream));
+    } else {
+        const char* src = static_cast<const char*>(full) + (int64_t)tp_rank * sh * es;
+        e = tpk::launch_copy2d(src, cols * es, out, sh * es, rows, sh * es, as_stream(stream));
+    }
+    return hip_status(e, "tp_shard_weights");
+}
+
+tp_status tp_shard_gate_up(const void* gate, const void* up, int64_t f, int64_t h, tp_dtype dt, int tp_rank,
+                           int tp_size, void* out, void* stream) {
+    if (!gate || !up || !out) return fail(TP_EINVAL, "tp_shard_gate_up: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_shard_gate_up: bad dtype %d", (int)dt);
+    if (tp_status st = check_rank(tp_rank, tp_size)) return st;
+    if (f <= 0 || h <= 0 || f * h > kMaxElems) return fail(TP_EINVAL, "tp_shard_gate_up: bad shape");
+    if (f % tp_size) return fail(TP_ESHAPE, "tp_shard_gate_up: f %lld not divisible by tp_size %d", (long long)f,
+                                 tp_size);
+    const int64_t es = (int64_t)tpk::dtype_size(dt);
+    const int64_t fl = f / tp_size;
+    const int64_t seg = fl * h * es;  // bytes of one projection's rank chunk
+    // segment 0 (gate) then segment 1 (up); each is the rank's chunk of the projection
+    hipError_t e = tpk::launch_copy2d(static_cast<const char*>(gate) + tp_rank * seg, seg, out, seg, 1, seg,
+                                      as_stream(stream));
+    if (e == hipSuccess)
+        e = tpk::launch_copy2d(static_cast<const char*>(up) + tp_rank * seg, seg, static_cast<char*>(out) + seg, seg,
+                               1, seg, as_stream(stream));
+    return hip_status(e, "tp_shard_gate_up");
+}
+
+tp_status tp_kv_heads_for_rank(int64_t n_kv, int tp_rank, int tp_size, int64_t* first, int64_t* count) {
+    if (!first || !count) return fail(TP_EINVAL, "tp_kv_heads_for_rank: null pointer");
+    if (tp_status st = check_rank(tp_rank, tp_size)) return st;
+    if (n_kv < 1) return fail(TP_EINVAL, "tp_kv_heads_for_rank: n_kv %lld < 1", (long long)n_kv);
+    if (tp_size <= n_kv) {
+        if (n_kv % tp_size)
+            return fail(TP_ESHAPE, "tp_kv_heads_for_rank: n_kv %lld not divisible by tp_size %d", (long long)n_kv,
+                        tp_size);
+        *count = n_kv / tp_size;
+        *first = tp_rank * (*count);
+    } else {
+        if (tp_size % n_kv)
+            return fail(TP_ESHAPE, "tp_kv_heads_for_rank: tp_size %d not divisible by n_kv %lld", tp_size,
+                        (long long)n_kv);
+        *count = 1;
+        *first = tp_rank / (tp_size / n_kv);
+    }
+    return ok();
+}
+
+tp_status tp_shard_qkv(const void* wq, const void* wk, const void* wv, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                       int64_t h, tp_dtype dt, int tp_rank, int tp_size, void* out, void* stream) {
+    if (!wq || !wk || !wv || !out) return fail(TP_EINVAL, "tp_shard_qkv: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_shard_qkv: bad dtype %d", (int)dt);
+    if (tp_status st = check_rank(tp_rank, tp_size)) return st;
+    if (n_q < 1 || n_kv < 1 || head_dim < 1 || h < 1 || n_q * head_dim * h > kMaxElems)
+        return fail(TP_EINVAL, "tp_shard_qkv: bad shape");
+    if (n_q % tp_size)
+        return fail(TP_ESHAPE, "tp_shard_qkv: n_q %lld not divisible by tp_size %d", (long long)n_q, tp_size);
+    int64_t kv0, kvc;
+    if (tp_status st = tp_kv_heads_for_rank(n_kv, tp_rank, tp_size, &kv0, &kvc)) return st;
+    const int64_t es = (int64_t)tpk::dtype_size(dt);
+    const int64_t head_bytes = head_dim * h * es;
+    const int64_t qc = n_q / tp_size;
+    char* o = static_cast<char*>(out);
+    hipStream_t s = as_stream(stream);
+    hipError_t e = tpk::launch_copy2d(static_cast<const char*>(wq) + tp_rank * qc * head_bytes, qc * head_bytes, o,
+                                      qc * head_bytes, 1, qc * head_bytes, s);
+    o += qc * head_bytes;
+    if (e == hipSuccess)
+        e = tpk::launch_copy2d(static_cast<const char*>(wk) + kv0 * head_bytes, kvc * head_bytes, o,
+                               kvc * head_bytes, 1, kvc * head_bytes, s);
+    o += kvc * head_bytes;
+    if (e == hipSuccess)
+        e = tpk::launch_copy2d(static_cast<const char*>(wv) + kv0 * head_bytes, kvc * head_bytes, o,
+                               kvc * head_bytes, 1, kvc * head_bytes, s);
+    return hip_status(e, "tp_shard_qkv");
+}
+
+// ---- GEMMs --------------------------------------------------------------------
+
+tp_status tp_gate_up_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_dtype dt, size_t* bytes) {
+    if (!bytes) return fail(TP_EINVAL, "tp_gate_up_workspace_bytes: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_gate_up_workspace_bytes: bad dtype %d", (int)dt);
+    if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_gate_up_workspace_bytes")) return st;
+    *bytes = tpk::plan_gemm(n, f_local, h, true, dt).ws_bytes;
+    return ok();
+}
+
+tp_status tp_gate_up_act_rank(const void* x, int64_t n, int64_t h, const void* w_gate_up, int64_t f_local,
+                              tp_dtype dt, void* act, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !w_gate_up || !act) return fail(TP_EINVAL, "tp_gate_up_act_rank: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_gate_up_act_rank: bad dtype %d", (int)dt);
+    if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_gate_up_act_rank")) return st;
+    tpk::GemmPlan pl = tpk::plan_gemm(n, f_local, h, true, dt);
+    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes))
+        return fail(TP_EWORKSPACE, "tp_gate_up_act_rank: workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(tpk::launch_gemm(pl, x, w_gate_up, nullptr, act, n, f_local, h, true, dt, dt, workspace,
+                                       as_stream(stream)),
+                      "tp_gate_up_act_rank");
+}
+
+tp_status tp_linear_workspace_bytes(int64_t n, int64_t k, int64_t m, tp_dtype dt, size_t* bytes) {
+    if (!bytes) return fail(TP_EINVAL, "tp_linear_workspace_bytes: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_linear_workspace_bytes: bad dtype %d", (int)dt);
+    if (tp_status st = check_gemm_dims(n, k, m, "tp_linear_workspace_bytes")) return st;
+    *bytes = tpk::plan_gemm(n, m, k, false, dt).ws_bytes;
+    return ok();
+}
+
+tp_status tp_linear_rank_forward(const void* x, int64_t n, int64_t k, const void* w, int64_t m, const void* bias,
+                                 tp_dtype dt, void* y, tp_dtype out_dt, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    if (!x || !w || !y) return fail(TP_EINVAL, "tp_linear_rank_forward: null pointer");
+    if (!valid_dt(dt) || !valid_dt(out_dt) || !valid_pair(dt, out_dt))
+        return fail(TP_EDTYPE, "tp_linear_rank_forward: unsupported dtype pair (%d -> %d)", (int)dt, (int)out_dt);
+    if (tp_status st = check_gemm_dims(n, k, m, "tp_linear_rank_forward")) return st;
+    tpk::GemmPlan pl = tpk::plan_gemm(n, m, k, false, dt);
+    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes))
+        return fail(TP_EWORKSPACE, "tp_linear_rank_forward: workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(tpk::launch_gemm(pl, x, w, bias, y, n, m, k, false, dt, out_dt, workspace, as_stream(stream)),
+                      "tp_linear_rank_forward");
+}
+
+tp_status tp_mlp_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_dtype dt, size_t* bytes) {
+    if (!bytes) return fail(TP_EINVAL, "tp_mlp_workspace_bytes: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_mlp_workspace_bytes: bad dtype %d", (int)dt);
+    if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_mlp_workspace_bytes")) return st;
+    *bytes = mlp_layout(n, h, f_local, dt).total;
+    return ok();
+}
+
+tp_status tp_mlp_rank_forward(const void* x, int64_t n, int64_t h, const void* w_gate_up, const void* w_down,
+                              int64_t f_local, tp_dtype dt, void* partial, tp_dtype out_dt, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (!x || !w_gate_up || !w_down || !partial) return fail(TP_EINVAL, "tp_mlp_rank_forward: null pointer");
+    if (!valid_dt(dt) || !valid_dt(out_dt) || !valid_pair(dt, out_dt))
+        return fail(TP_EDTYPE, "tp_mlp_rank_forward: unsupported dtype pair (%d -> %d)", (int)dt, (int)out_dt);
+    if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_mlp_rank_forward")) return st;
+    MlpLayout L = mlp_layout(n, h, f_local, dt);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(TP_EWORKSPACE, "tp_mlp_rank_forward: workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) & 255u) return fail(TP_EINVAL, "tp_mlp_rank_forward: workspace not 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    void* act = ws;
+    void* split = ws + L.act_bytes;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = tpk::launch_gemm(L.gu, x, w_gate_up, nullptr, act, n, f_local, h, true, dt, dt, split, s);
+    if (e == hipSuccess) e = tpk::launch_gemm(L.down, act, w_down, nullptr, partial, n, h, f_local, false, dt, out_dt, split, s);
+    return hip_status(e, "tp_mlp_rank_forward");
+}
+
+// ---- reduce -------------------------------------------------------------------
+
+tp_status tp_partial_reduce(const void* const* partials, int t, int64_t K, tp_dtype in_dt, void* out, tp_dtype out_dt,
+                            tp_order order, void* stream) {
+    if (!partials || !out) return fail(TP_EINVAL, "tp_partial_reduce: null pointer");
+    if (t < 1 || t > TP_MAX_RANKS) return fail(TP_EINVAL, "tp_partial_reduce: t %d outside [1, %d]", t, TP_MAX_RANKS);
+    for (int r = 0; r < t; ++r)
+        if (!partials[r]) return fail(TP_EINVAL, "tp_partial_reduce: partials[%d] is null", r);
+    if (K < 0 || K > kMaxElems) return fail(TP_EINVAL, "tp_partial_reduce: K %lld out of range", (long long)K);
+    if (!valid_dt(in_dt) || !valid_dt(out_dt) || !valid_pair(in_dt, out_dt))
+        return fail(TP_EDTYPE, "tp_partial_reduce: unsupported dtype pair (%d -> %d)", (int)in_dt, (int)out_dt);
+    if (order != TP_ORDER_RING) return fail(TP_EINVAL, "tp_partial_reduce: unknown order %d", (int)order);
+    return hip_status(tpk::launch_ring_reduce(partials, t, K, in_dt, out, out_dt, as_stream(stream)),
+                      "tp_partial_reduce");
+}
+
+tp_status tp_ring_schedule(int t, int64_t K, tp_ring_step* steps, int max_steps, int* n_steps) {
+    if (!steps || !n_steps) return fail(TP_EINVAL, "tp_ring_schedule: null pointer");
+    if (t < 1 || t > TP_MAX_RANKS) return fail(TP_EINVAL, "tp_ring_schedule: t %d outside [1, %d]", t, TP_MAX_RANKS);
+    if (K < 0 || K > kMaxElems) return fail(TP_EINVAL, "tp_ring_schedule: K out of range");
+    const int need = 2 * t * (t - 1);
+    if (max_steps < need) return fail(TP_ESHAPE, "tp_ring_schedule: %d steps needed, room for %d", need, max_steps);
+    int k = 0;
+    for (int phase = 0; phase < 2; ++phase)
+        for (int s = 0; s < t - 1; ++s)
+            for (int r = 0; r < t; ++r) {
+                // reduce-scatter: rank r forwards the partially reduced chunk it
+                // received last round (its own chunk at s = 0); all-gather: it
+                // forwards the finished chunk it owns / just received.
+                const int c = phase == 0 ? (((r - s) % t) + t) % t : (((r + 1 - s) % t) + t) % t;
+                tp_ring_step& st = steps[k++];
+                st.phase = phase;
+                st.step = s;
+                st.src = r;
+                st.dst = (r + 1) % t;
+                st.chunk = c;
+                const int64_t lo = (int64_t)(((__int128)c * K) / t);
+                const int64_t hi = (int64_t)(((__int128)(c + 1) * K) / t);
+                st.offset = lo;
+                st.len = hi - lo;
+            }
+    *n_steps = k;
+    return ok();
+}
+
+// ---- vocab parallel ---------------------------------------------------------
+
+tp_status tp_vocab_range(int64_t vocab, int tp_rank, int tp_size, int64_t* start, int64_t* end) {
+    if (!start || !end) return fail(TP_EINVAL, "tp_vocab_range: null pointer");
+    if (tp_status st = check_rank(tp_rank, tp_size)) return st;
+    if (vocab < 1 || vocab > kMaxElems) return fail(TP_EINVAL, "tp_vocab_range: vocab %lld out of range", (long long)vocab);
+    const int64_t per = (vocab + tp_size - 1) / tp_size;
+    int64_t s = tp_rank * per, e = (tp_rank + 1) * per;
+    if (e > vocab) e = vocab;
+    if (s > e) s = e;
+    *start = s;
+    *end = e;
+    return ok();
+}
+
+tp_status tp_vocab_embed_rank(const int64_t* ids, int64_t n, const void* table_shard, int64_t vocab, int64_t h,
+                              int tp_rank, int tp_size, tp_dtype dt, void* out, void* stream) {
+    if (!ids || !out) return fail(TP_EINVAL, "tp_vocab_embed_rank: null pointer");
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_vocab_embed_rank: bad dtype %d", (int)dt);
+    if (n <= 0 || h <= 0 || n * h > kMaxElems) return fail(TP_EINVAL, "tp_vocab_embed_rank: bad shape");
+    int64_t s, e;
+    if (tp_status st = tp_vocab_range(vocab, tp_rank, tp_size, &s, &e)) return st;
+    if (e > s && !table_shard) return fail(TP_EINVAL, "tp_vocab_embed_rank: null table for a non-empty shard");
+    return hip_status(tpk::launch_vocab_embed(ids, n, table_shard, s, e, h, (int)tpk::dtype_size(dt), out,
+                                              as_stream(stream)),
+                      "tp_vocab_embed_rank");
+}
+
+tp_status tp_lm_head_rank(const void* x, int64_t n, int64_t h, const void* table_shard, int64_t v_local, tp_dtype dt,
+                          void* logits, tp_dtype out_dt, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !table_shard || !logits) return fail(TP_EINVAL, "tp_lm_head_rank: null pointer");
+    if (!valid_dt(dt) || !valid_dt(out_dt) || !valid_pair(dt, out_dt))
+        return fail(TP_EDTYPE, "tp_lm_head_rank: unsupported dtype pair (%d -> %d)", (int)dt, (int)out_dt);
+    if (tp_status st = check_gemm_dims(n, h, v_local, "tp_lm_head_rank")) return st;
+    tpk::GemmPlan pl = tpk::plan_gemm(n, v_local, h, false, dt);
+    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes))
+        return fail(TP_EWORKSPACE, "tp_lm_head_rank: workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(tpk::launch_gemm(pl, x, table_shard, nullptr, logits, n, v_local, h, false, dt, out_dt,
+                                       workspace, as_stream(stream)),
+                      "tp_lm_head_rank");
+}
+
+}  // extern "C"

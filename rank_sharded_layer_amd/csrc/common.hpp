@@ -1,0 +1,83 @@
+// Internal helpers shared by the libtpshard kernels and host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tpshard.h"
+
+namespace tpk {
+
+// ---- bf16 helpers (device) ----------------------------------------------
+
+// bf16 -> fp32 is exact: the 16 bits are the top half of the fp32 encoding.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// pack two fp32 into two bf16 (lo in the low half)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---- element load/store by dtype ----------------------------------------
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p) { return *p; }
+    static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+    static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// SiLU(g) * u in fp32: g * sigmoid(g) * u.  For g -> -inf, exp(-g) -> inf and
+// the quotient goes to -0; for g -> +inf the quotient goes to g.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+__host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline size_t dtype_size(tp_dtype dt) { return dt == TP_F32 ? 4 : 2; }
+
+}  // namespace tpk
+
+// ---- host-side launchers implemented in the kernel translation units ------
+
+namespace tpk {
+
+hipError_t launch_copy2d(const void* src, int64_t src_ld_bytes, void* dst, int64_t dst_ld_bytes,
+                         int64_t rows, int64_t row_bytes, hipStream_t s);
+
+hipError_t launch_ring_reduce(const void* const* parts, int t, int64_t K, tp_dtype in_dt,
+                              void* out, tp_dtype out_dt, hipStream_t s);
+
+hipError_t launch_vocab_embed(const int64_t* ids, int64_t n, const void* table, int64_t start,
+                              int64_t end, int64_t h, int esize, void* out, hipStream_t s);
+
+// GEMM planning and launch.  C[M, N] = A[M, K] . B[Nb, K]^T (+bias), or for a
+// gated call act[M, N] = SiLU(A . B[0:N]^T) * (A . B[N:2N]^T) with Nb = 2N.
+struct GemmPlan {
+    int kernel;       // which tile configuration
+    int splits;       // split-K factor (1 = none)
+    int64_t k_split;  // K elements per split (multiple of the tile K) when splits > 1
+    size_t ws_bytes;  // fp32 workspace for split-K partial sums
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt);
+
+hipError_t launch_gemm(const GemmPlan& plan, const void* A, const void* B, const void* bias,
+                       void* C, int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt,
+                       tp_dtype out_dt, void* ws, hipStream_t s);
+
+}  // namespace tpk

@@ -1,0 +1,322 @@
+"""Thin Python binding of libtpshard (argument marshalling only).
+
+Every function has the name of the C entry point it calls and does three
+things: checks that the tensors it is given are contiguous, on the GPU and of
+matching shapes and dtypes (the C library receives raw pointers and cannot
+check buffer extents); allocates outputs/workspace with torch when the caller
+does not pass them; and calls the C function on torch's current stream.  All
+arithmetic happens in the library's HIP kernels.  There is no fallback: if
+the library is not built, or the GPU is missing, the call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpshard.so")
+
+TP_F32, TP_BF16 = 0, 1
+TP_ORDER_RING = 0
+TP_MAX_RANKS = 64
+STATUS_NAMES = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_ESHAPE", 3: "TP_EDTYPE", 4: "TP_EALIGN",
+                5: "TP_EHIP", 6: "TP_EWORKSPACE"}
+
+
+class TPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class RingStep(ctypes.Structure):
+    _fields_ = [("phase", ctypes.c_int), ("step", ctypes.c_int), ("src", ctypes.c_int),
+                ("dst", ctypes.c_int), ("chunk", ctypes.c_int), ("offset", ctypes.c_int64),
+                ("len", ctypes.c_int64)]
+
+
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_szp = ctypes.POINTER(ctypes.c_size_t)
+
+_SIGS = {
+    "tp_abi_version": (ctypes.c_int, []),
+    "tp_last_error": (ctypes.c_char_p, []),
+    "tp_status_string": (ctypes.c_char_p, [_int]),
+    "tp_shard_weights": (_int, [_vp, _i64, _i64, _int, _int, _int, _int, _vp, _vp]),
+    "tp_shard_gate_up": (_int, [_vp, _vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
+    "tp_kv_heads_for_rank": (_int, [_i64, _int, _int, _i64p, _i64p]),
+    "tp_shard_qkv": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp]),
+    "tp_gate_up_workspace_bytes": (_int, [_i64, _i64, _i64, _int, _szp]),
+    "tp_gate_up_act_rank": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp, _sz, _vp]),
+    "tp_linear_workspace_bytes": (_int, [_i64, _i64, _i64, _int, _szp]),
+    "tp_linear_rank_forward": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp, _int, _vp, _sz, _vp]),
+    "tp_mlp_workspace_bytes": (_int, [_i64, _i64, _i64, _int, _szp]),
+    "tp_mlp_rank_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _sz, _vp]),
+    "tp_partial_reduce": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _vp, _int, _int, _vp]),
+    "tp_ring_schedule": (_int, [_int, _i64, ctypes.POINTER(RingStep), _int, ctypes.POINTER(_int)]),
+    "tp_vocab_range": (_int, [_i64, _int, _int, _i64p, _i64p]),
+    "tp_vocab_embed_rank": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
+    "tp_lm_head_rank": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _int, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libtpshard.so (after torch, so that it binds torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_names():
+    return list(_SIGS)
+
+
+def _check(status: int):
+    if status != 0:
+        raise TPError(status, lib().tp_last_error().decode())
+
+
+def _dt(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return TP_BF16
+    if dtype == torch.float32:
+        return TP_F32
+    raise TPError(3, f"unsupported dtype {dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise TPError(6, f"workspace of {nbytes} bytes needed")
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+# ---- library ---------------------------------------------------------------
+
+def tp_abi_version() -> int:
+    return lib().tp_abi_version()
+
+
+def tp_last_error() -> str:
+    return lib().tp_last_error().decode()
+
+
+# ---- shard selection -------------------------------------------------------
+
+def tp_shard_weights(full, dim, tp_rank, tp_size, out=None, stream=None):
+    rows, cols = full.shape
+    shape = (rows // max(tp_size, 1), cols) if dim == 0 else (rows, cols // max(tp_size, 1))
+    if out is None:
+        out = torch.empty(shape, dtype=full.dtype, device=full.device)
+    p_full = _dev(full, "full")
+    p_out = _dev(out, "out", full.dtype, shape)
+    _check(lib().tp_shard_weights(p_full, rows, cols, _dt(full.dtype), dim, tp_rank, tp_size,
+                                  p_out, _stream(stream)))
+    return out
+
+
+def tp_shard_gate_up(gate, up, tp_rank, tp_size, out=None, stream=None):
+    f, h = gate.shape
+    shape = (2 * (f // max(tp_size, 1)), h)
+    if out is None:
+        out = torch.empty(shape, dtype=gate.dtype, device=gate.device)
+    pg = _dev(gate, "gate")
+    pu = _dev(up, "up", gate.dtype, gate.shape)
+    po = _dev(out, "out", gate.dtype, shape)
+    _check(lib().tp_shard_gate_up(pg, pu, f, h, _dt(gate.dtype), tp_rank, tp_size, po,
+                                  _stream(stream)))
+    return out
+
+
+def tp_kv_heads_for_rank(n_kv, tp_rank, tp_size):
+    first, count = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().tp_kv_heads_for_rank(n_kv, tp_rank, tp_size, ctypes.byref(first), ctypes.byref(count)))
+    return first.value, count.value
+
+
+def tp_shard_qkv(wq, wk, wv, n_q, n_kv, head_dim, tp_rank, tp_size, out=None, stream=None):
+    h = wq.shape[1]
+    if tuple(wq.shape) != (n_q * head_dim, h):
+        raise ValueError("wq must be [n_q*head_dim, h]")
+    _, kvc = tp_kv_heads_for_rank(n_kv, tp_rank, tp_size)
+    shape = ((n_q // tp_size + 2 * kvc) * head_dim, h)
+    if out is None:
+        out = torch.empty(shape, dtype=wq.dtype, device=wq.device)
+    pq = _dev(wq, "wq")
+    pk = _dev(wk, "wk", wq.dtype, (n_kv * head_dim, h))
+    pv = _dev(wv, "wv", wq.dtype, (n_kv * head_dim, h))
+    po = _dev(out, "out", wq.dtype, shape)
+    _check(lib().tp_shard_qkv(pq, pk, pv, n_q, n_kv, head_dim, h, _dt(wq.dtype), tp_rank, tp_size,
+                              po, _stream(stream)))
+    return out
+
+
+# ---- GEMMs -----------------------------------------------------------------
+
+def tp_gate_up_workspace_bytes(n, h, f_local, dtype) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().tp_gate_up_workspace_bytes(n, h, f_local, _dt(dtype), ctypes.byref(b)))
+    return b.value
+
+
+def tp_gate_up_act_rank(x, w_gate_up, act=None, workspace=None, stream=None):
+    n, h = x.shape
+    f_local = w_gate_up.shape[0] // 2
+    px = _dev(x, "x")
+    pw = _dev(w_gate_up, "w_gate_up", x.dtype, (2 * f_local, h))
+    if act is None:
+        act = torch.empty((n, f_local), dtype=x.dtype, device=x.device)
+    pa = _dev(act, "act", x.dtype, (n, f_local))
+    pws, nws = _workspace(tp_gate_up_workspace_bytes(n, h, f_local, x.dtype), x.device, workspace)
+    _check(lib().tp_gate_up_act_rank(px, n, h, pw, f_local, _dt(x.dtype), pa, pws, nws,
+                                     _stream(stream)))
+    return act
+
+
+def tp_linear_workspace_bytes(n, k, m, dtype) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().tp_linear_workspace_bytes(n, k, m, _dt(dtype), ctypes.byref(b)))
+    return b.value
+
+
+def tp_linear_rank_forward(x, w, bias=None, out_dtype=None, y=None, workspace=None, stream=None):
+    n, k = x.shape
+    m = w.shape[0]
+    out_dtype = out_dtype or x.dtype
+    px = _dev(x, "x")
+    pw = _dev(w, "w", x.dtype, (m, k))
+    pb = _dev(bias, "bias", x.dtype, (m,)) if bias is not None else None
+    if y is None:
+        y = torch.empty((n, m), dtype=out_dtype, device=x.device)
+    py = _dev(y, "y", out_dtype, (n, m))
+    pws, nws = _workspace(tp_linear_workspace_bytes(n, k, m, x.dtype), x.device, workspace)
+    _check(lib().tp_linear_rank_forward(px, n, k, pw, m, pb, _dt(x.dtype), py, _dt(out_dtype),
+                                        pws, nws, _stream(stream)))
+    return y
+
+
+def tp_mlp_workspace_bytes(n, h, f_local, dtype) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().tp_mlp_workspace_bytes(n, h, f_local, _dt(dtype), ctypes.byref(b)))
+    return b.value
+
+
+def tp_mlp_rank_forward(x, w_gate_up, w_down, out_dtype=None, partial=None, workspace=None,
+                        stream=None):
+    n, h = x.shape
+    f_local = w_gate_up.shape[0] // 2
+    out_dtype = out_dtype or x.dtype
+    px = _dev(x, "x")
+    pgu = _dev(w_gate_up, "w_gate_up", x.dtype, (2 * f_local, h))
+    pd = _dev(w_down, "w_down", x.dtype, (h, f_local))
+    if partial is None:
+        partial = torch.empty((n, h), dtype=out_dtype, device=x.device)
+    pp = _dev(partial, "partial", out_dtype, (n, h))
+    need = tp_mlp_workspace_bytes(n, h, f_local, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    pws = _dev(workspace, "workspace")
+    nws = workspace.numel() * workspace.element_size()
+    _check(lib().tp_mlp_rank_forward(px, n, h, pgu, pd, f_local, _dt(x.dtype), pp, _dt(out_dtype),
+                                     pws, nws, _stream(stream)))
+    return partial
+
+
+# ---- reduce ------------------------------------------------------------------
+
+def tp_partial_reduce(partials, out=None, out_dtype=None, order=TP_ORDER_RING, stream=None):
+    t = len(partials)
+    if t < 1:
+        raise TPError(1, "no partials")
+    p0 = partials[0]
+    out_dtype = out_dtype or p0.dtype
+    ptrs = (ctypes.c_void_p * t)(*[_dev(p, f"partials[{i}]", p0.dtype, p0.shape).value
+                                   for i, p in enumerate(partials)])
+    if out is None:
+        out = torch.empty(p0.shape, dtype=out_dtype, device=p0.device)
+    po = _dev(out, "out", out_dtype, p0.shape)
+    _check(lib().tp_partial_reduce(ptrs, t, p0.numel(), _dt(p0.dtype), po, _dt(out_dtype), order,
+                                   _stream(stream)))
+    return out
+
+
+def tp_ring_schedule(t, K):
+    n = max(2 * t * (t - 1), 1)
+    arr = (RingStep * n)()
+    got = ctypes.c_int()
+    _check(lib().tp_ring_schedule(t, K, arr, n, ctypes.byref(got)))
+    return [dict(phase=s.phase, step=s.step, src=s.src, dst=s.dst, chunk=s.chunk, offset=s.offset,
+                 len=s.len) for s in arr[:got.value]]
+
+
+# ---- vocab parallel -----------------------------------------------------------
+
+def tp_vocab_range(vocab, tp_rank, tp_size):
+    s, e = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().tp_vocab_range(vocab, tp_rank, tp_size, ctypes.byref(s), ctypes.byref(e)))
+    return s.value, e.value
+
+
+def tp_vocab_embed_rank(ids, table_shard, vocab, tp_rank, tp_size, out=None, stream=None):
+    n = ids.numel()
+    h = table_shard.shape[1]
+    s, e = tp_vocab_range(vocab, tp_rank, tp_size)
+    pi = _dev(ids, "ids", torch.int64)
+    pt = _dev(table_shard, "table_shard", None, (e - s, h))
+    if out is None:
+        out = torch.empty((n, h), dtype=table_shard.dtype, device=ids.device)
+    po = _dev(out, "out", table_shard.dtype, (n, h))
+    _check(lib().tp_vocab_embed_rank(pi, n, pt, vocab, h, tp_rank, tp_size, _dt(table_shard.dtype),
+                                     po, _stream(stream)))
+    return out
+
+
+def tp_lm_head_rank(x, table_shard, out_dtype=torch.float32, logits=None, workspace=None, stream=None):
+    n, h = x.shape
+    v_local = table_shard.shape[0]
+    px = _dev(x, "x")
+    pt = _dev(table_shard, "table_shard", x.dtype, (v_local, h))
+    if logits is None:
+        logits = torch.empty((n, v_local), dtype=out_dtype, device=x.device)
+    pl = _dev(logits, "logits", out_dtype, (n, v_local))
+    pws, nws = _workspace(tp_linear_workspace_bytes(n, h, v_local, x.dtype), x.device, workspace)
+    _check(lib().tp_lm_head_rank(px, n, h, pt, v_local, _dt(x.dtype), pl, _dt(out_dtype), pws, nws,
+                                 _stream(stream)))
+    return logits

@@ -1,0 +1,172 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol the
+header declares, its host-only entry points agree with the oracle, and every
+argument error is reported with a status and message before any launch.
+
+No compute call reaches the GPU here.  The error-path cases pass dummy
+(non-null, never dereferenced) pointers, so they run only where no GPU is
+present: a validation slip must not turn into a launch with a bogus address.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+from rank_sharded_layer_amd import tpshard as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="dummy-pointer error paths run on a GPU-less host only")
+
+
+def header_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"TP_API\s+[\w\s\*]*?\b(tp_\w+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_header_symbol():
+    L = T.lib()
+    syms = header_symbols()
+    assert len(syms) >= 17
+    for s in syms:
+        assert hasattr(L, s), s
+    assert sorted(T.exported_names()) == syms
+    assert T.tp_abi_version() == 1
+
+
+def test_status_strings():
+    L = T.lib()
+    for k, v in T.STATUS_NAMES.items():
+        assert L.tp_status_string(k).decode() == v
+
+
+@pytest.mark.parametrize("V,t", [(151936, 2), (10, 2), (11, 4), (10, 8), (7, 3), (1, 1), (5, 64)])
+def test_vocab_range_matches_oracle(V, t):
+    for r in range(t):
+        assert T.tp_vocab_range(V, r, t) == oracle.vocab_range(V, r, t)
+
+
+@pytest.mark.parametrize("n_kv,t", [(8, 1), (8, 2), (8, 4), (8, 8), (8, 16), (2, 4), (2, 8), (1, 64)])
+def test_kv_heads_match_oracle(n_kv, t):
+    for r in range(t):
+        assert T.tp_kv_heads_for_rank(n_kv, r, t) == oracle.kv_heads_for_rank(n_kv, r, t)
+
+
+@pytest.mark.parametrize("t,K", [(1, 10), (2, 32768), (3, 1000), (4, 524288), (5, 7), (8, 67108864),
+                                 (16, 67108864), (64, 1 << 20)])
+def test_ring_schedule_matches_oracle(t, K):
+    assert T.tp_ring_schedule(t, K) == oracle.ring_schedule(t, K)
+
+
+def test_workspace_queries():
+    # large-M shapes need no split-K workspace, decode shapes do
+    assert T.tp_linear_workspace_bytes(8192, 3584, 8192, torch.bfloat16) == 0
+    assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 0
+    assert T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16) > 0
+    mlp = T.tp_mlp_workspace_bytes(64, 8192, 7168, torch.bfloat16)
+    act = 64 * 7168 * 2
+    assert mlp >= act + T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16)
+    assert mlp >= act + T.tp_linear_workspace_bytes(64, 7168, 8192, torch.bfloat16)
+    assert T.tp_mlp_workspace_bytes(16, 1024, 1536, torch.float32) >= 16 * 1536 * 4
+
+
+def _status(fn, *args):
+    return fn(*args), T.lib().tp_last_error().decode()
+
+
+DUMMY = ctypes.c_void_p(0x1000)
+NULL = None
+
+
+@no_gpu
+def test_shard_errors():
+    L = T.lib()
+    st, msg = _status(L.tp_shard_weights, NULL, 4, 4, 1, 0, 0, 2, DUMMY, NULL)
+    assert st == 1 and "null" in msg
+    st, msg = _status(L.tp_shard_weights, DUMMY, 5, 4, 1, 0, 0, 2, DUMMY, NULL)
+    assert st == 2 and "divisible" in msg
+    st, msg = _status(L.tp_shard_weights, DUMMY, 4, 5, 1, 1, 0, 2, DUMMY, NULL)
+    assert st == 2
+    st, _ = _status(L.tp_shard_weights, DUMMY, 4, 4, 1, 2, 0, 2, DUMMY, NULL)
+    assert st == 1                    # dim not 0/1
+    st, _ = _status(L.tp_shard_weights, DUMMY, 4, 4, 1, 0, 2, 2, DUMMY, NULL)
+    assert st == 1                    # rank >= size
+    st, _ = _status(L.tp_shard_weights, DUMMY, 4, 4, 1, 0, -1, 2, DUMMY, NULL)
+    assert st == 1
+    st, _ = _status(L.tp_shard_weights, DUMMY, 4, 4, 1, 0, 0, 65, DUMMY, NULL)
+    assert st == 1                    # t > 64
+    st, _ = _status(L.tp_shard_weights, DUMMY, 4, 4, 7, 0, 0, 2, DUMMY, NULL)
+    assert st == 3                    # dtype
+    st, _ = _status(L.tp_shard_gate_up, DUMMY, DUMMY, 6, 4, 1, 0, 4, DUMMY, NULL)
+    assert st == 2
+    st, _ = _status(L.tp_shard_qkv, DUMMY, DUMMY, DUMMY, 6, 2, 4, 8, 1, 0, 4, DUMMY, NULL)
+    assert st == 2                    # n_q 6 not divisible by 4
+    st, _ = _status(L.tp_shard_qkv, DUMMY, DUMMY, DUMMY, 12, 8, 4, 8, 1, 0, 3, DUMMY, NULL)
+    assert st == 2                    # 8 kv heads over 3 ranks
+    st, _ = _status(L.tp_shard_qkv, DUMMY, DUMMY, DUMMY, 12, 4, 4, 8, 1, 0, 6, DUMMY, NULL)
+    assert st == 2                    # 6 ranks, 4 kv heads: neither divides
+
+
+@no_gpu
+def test_gemm_errors():
+    L = T.lib()
+    st, _ = _status(L.tp_linear_rank_forward, NULL, 4, 4, DUMMY, 4, NULL, 1, DUMMY, 1, NULL, 0, NULL)
+    assert st == 1
+    st, _ = _status(L.tp_linear_rank_forward, DUMMY, 0, 4, DUMMY, 4, NULL, 1, DUMMY, 1, NULL, 0, NULL)
+    assert st == 1                    # n = 0
+    st, _ = _status(L.tp_linear_rank_forward, DUMMY, 4, 4, DUMMY, 4, NULL, 0, DUMMY, 1, NULL, 0, NULL)
+    assert st == 3                    # f32 -> bf16 unsupported
+    st, msg = _status(L.tp_linear_rank_forward, DUMMY, 64, 7168, DUMMY, 8192, NULL, 1, DUMMY, 1, NULL, 0, NULL)
+    assert st == 6 and "workspace" in msg   # split-K shape without workspace
+    st, _ = _status(L.tp_gate_up_act_rank, DUMMY, 64, 8192, DUMMY, 7168, 1, DUMMY, NULL, 0, NULL)
+    assert st == 6
+    st, _ = _status(L.tp_mlp_rank_forward, DUMMY, 4, 8, DUMMY, DUMMY, 6, 1, DUMMY, 1, NULL, 0, NULL)
+    assert st == 6
+    st, _ = _status(L.tp_mlp_rank_forward, DUMMY, 4, 8, DUMMY, DUMMY, 6, 1, DUMMY, 1,
+                    ctypes.c_void_p(0x1001), 1 << 20, NULL)
+    assert st == 1                    # misaligned workspace
+    st, _ = _status(L.tp_lm_head_rank, DUMMY, 4, 8, NULL, 16, 1, DUMMY, 0, NULL, 0, NULL)
+    assert st == 1
+
+
+@no_gpu
+def test_reduce_and_vocab_errors():
+    L = T.lib()
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    st, _ = _status(L.tp_partial_reduce, arr, 0, 8, 1, DUMMY, 1, 0, NULL)
+    assert st == 1                    # t = 0
+    st, _ = _status(L.tp_partial_reduce, arr, 65, 8, 1, DUMMY, 1, 0, NULL)
+    assert st == 1                    # t > 64
+    arr2 = (ctypes.c_void_p * 2)(0x1000, None)
+    st, msg = _status(L.tp_partial_reduce, arr2, 2, 8, 1, DUMMY, 1, 0, NULL)
+    assert st == 1 and "partials[1]" in msg
+    st, _ = _status(L.tp_partial_reduce, arr, 2, 8, 0, DUMMY, 1, 0, NULL)
+    assert st == 3
+    st, _ = _status(L.tp_partial_reduce, arr, 2, 8, 1, DUMMY, 1, 5, NULL)
+    assert st == 1                    # unknown order
+    st, _ = _status(L.tp_vocab_embed_rank, NULL, 4, DUMMY, 10, 4, 0, 2, 1, DUMMY, NULL)
+    assert st == 1
+    st, _ = _status(L.tp_vocab_embed_rank, DUMMY, 4, NULL, 10, 4, 0, 2, 1, DUMMY, NULL)
+    assert st == 1                    # null table for a non-empty shard
+    st, _ = _status(L.tp_vocab_embed_rank, DUMMY, 4, DUMMY, 10, 4, 3, 2, 1, DUMMY, NULL)
+    assert st == 1
+    first, count = ctypes.c_int64(), ctypes.c_int64()
+    assert L.tp_kv_heads_for_rank(0, 0, 1, ctypes.byref(first), ctypes.byref(count)) == 1
+    steps = (T.RingStep * 2)()
+    n = ctypes.c_int()
+    assert L.tp_ring_schedule(3, 9, steps, 2, ctypes.byref(n)) == 2   # room for 2 < 12
+    assert T.tp_last_error() != ""
+    # success clears the message
+    assert L.tp_ring_schedule(1, 9, steps, 2, ctypes.byref(n)) == 0
+    assert T.tp_last_error() == ""
+
+
+def test_binding_rejects_host_tensors():
+    with pytest.raises(ValueError):
+        T.tp_partial_reduce([torch.zeros(8), torch.zeros(8)])
+    with pytest.raises(ValueError):
+        T.tp_shard_weights(torch.zeros(4, 4), 0, 0, 2)

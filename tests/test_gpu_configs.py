@@ -1,0 +1,196 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  The oracle checks sampled token rows (every step of the
+path is row-independent, so a sampled row is checked exactly) and windows of
+the reduce around every chunk boundary (each element's ring order depends
+only on its chunk).
+
+Workloads (shapes of the pages' examples; seeded synthetic values):
+  qwen3_mlp_tp2_fp32       h=1024, f=3072, t=2, n=16, fp32
+  qwen3_vocab_tp2          V=151936, h=1024, t=2, n=512, bf16
+  llama70b_decode_tp4      h=8192, f=28672, t=4, n=64, bf16
+  llama70b_prefill_tp8     h=8192, f=28672, t=8, n=8192, bf16
+  llama70b_attnproj_tp16   h=8192, 64 Q / 8 KV heads of 128, t=16, n=8192, bf16
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from rank_sharded_layer_amd import tpshard as T
+from tests.helpers import TOL, bits, relf, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def gen(w, tensor_id, shape, std, device=DEV):
+    return synth.normal(shape, std, w.seed(tensor_id), w.dtype, device=device)
+
+
+def f64_bits(b, dtype):
+    return oracle.bf16_bits_to_f64(b) if dtype == torch.bfloat16 else b.view(np.float32).astype(np.float64)
+
+
+def ring_windows(K, t, width=4096):
+    """Element windows straddling every chunk boundary, plus the two ends."""
+    wins = []
+    for c in range(t + 1):
+        lo, _ = oracle.chunk_bounds(K, t, c) if c < t else (K, K)
+        a, b = max(0, lo - width // 2), min(K, lo + width // 2)
+        if b > a:
+            wins.append((a, b))
+    return wins
+
+
+def check_reduce_windows(parts, out, out_dtype):
+    t = len(parts)
+    K = parts[0].numel()
+    host = [to_f64(p).astype(np.float32).reshape(-1) for p in parts]
+    got = bits(out).reshape(-1)
+    for a, b in ring_windows(K, t):
+        s = oracle.ring_allreduce_f32(host, a, b)
+        ref = oracle.f32_to_bf16_bits(s) if out_dtype == torch.bfloat16 else s.view(np.uint32)
+        assert np.array_equal(got[a:b], ref), (a, b)
+
+
+# --------------------------------------------------------------------------
+
+def test_qwen3_mlp_tp2_fp32_full():
+    w = synth.get("qwen3_mlp_tp2_fp32")
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    gate = gen(w, synth.T_GATE, (w.f, w.h), 0.02)
+    up = gen(w, synth.T_UP, (w.f, w.h), 0.02)
+    down = gen(w, synth.T_DOWN, (w.h, w.f), 0.02)
+    parts = []
+    X, G, U, D = to_f64(x), to_f64(gate), to_f64(up), to_f64(down)
+    for r in range(w.tp):
+        wgu = T.tp_shard_gate_up(gate, up, r, w.tp)
+        wd = T.tp_shard_weights(down, 1, r, w.tp)
+        parts.append(T.tp_mlp_rank_forward(x, wgu, wd))
+        assert relf(to_f64(parts[-1]), oracle.mlp_rank(X, G, U, D, r, w.tp)) <= TOL[torch.float32]
+    y = T.tp_partial_reduce(parts)
+    assert relf(to_f64(y), oracle.mlp(X, G, U, D)) <= TOL[torch.float32]
+    check_reduce_windows(parts, y, torch.float32)
+
+
+def test_qwen3_vocab_tp2_full():
+    w = synth.get("qwen3_vocab_tp2")
+    table = gen(w, synth.T_TABLE, (w.vocab, w.h), 0.02)
+    ids = synth.token_ids(w.n, w.vocab, w.seed(synth.T_IDS), device=DEV)
+    # edge ids at the ends of the sequence
+    ids[0], ids[1], ids[2], ids[-1] = 0, w.vocab - 1, w.vocab // w.tp, w.vocab // w.tp - 1
+    table_bits = bits(table)
+    ids_h = ids.cpu().numpy()
+    outs, shards = [], []
+    for r in range(w.tp):
+        s, e = T.tp_vocab_range(w.vocab, r, w.tp)
+        shard = T.tp_shard_weights(table, 0, r, w.tp)
+        assert shard.shape[0] == e - s
+        shards.append(shard)
+        out = T.tp_vocab_embed_rank(ids, shard, w.vocab, r, w.tp)
+        ref = oracle.embed_rank(ids_h, oracle.shard(table_bits, 0, r, w.tp), w.vocab, r, w.tp)
+        assert np.array_equal(bits(out), ref)
+        outs.append(out)
+    xemb = T.tp_partial_reduce(outs)
+    full = oracle.embed_full(ids_h, table_bits)
+    assert np.array_equal(to_f64(xemb), f64_bits(full, torch.bfloat16))
+    check_reduce_windows(outs, xemb, torch.bfloat16)
+    # LM head shard on the summed embedding (tied table), sampled rows
+    rows = synth.sample_rows(w.n, 8, w.seed(77))
+    Xr = to_f64(xemb)[rows]
+    T64 = oracle.bf16_bits_to_f64(table_bits)
+    for r in range(w.tp):
+        logits = T.tp_lm_head_rank(xemb, shards[r])
+        ref = oracle.lm_head_rank(Xr, T64, r, w.tp)
+        assert relf(to_f64(logits)[rows], ref) <= TOL[torch.bfloat16]
+
+
+def _mlp_full_weights(w):
+    gate = gen(w, synth.T_GATE, (w.f, w.h), 0.02)
+    up = gen(w, synth.T_UP, (w.f, w.h), 0.02)
+    down = gen(w, synth.T_DOWN, (w.h, w.f), 0.02)
+    return gate, up, down
+
+
+def test_llama70b_decode_tp4_full():
+    w = synth.get("llama70b_decode_tp4")
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    gate, up, down = _mlp_full_weights(w)
+    parts = []
+    for r in range(w.tp):
+        wgu = T.tp_shard_gate_up(gate, up, r, w.tp)
+        wd = T.tp_shard_weights(down, 1, r, w.tp)
+        parts.append(T.tp_mlp_rank_forward(x, wgu, wd))
+        del wgu, wd
+    y = T.tp_partial_reduce(parts)
+    rows = synth.sample_rows(w.n, 6, w.seed(78))
+    X = to_f64(x)[rows]
+    G, U, D = to_f64(gate), to_f64(up), to_f64(down)
+    for r in range(w.tp):
+        ref_r = oracle.mlp_rank(X, G, U, D, r, w.tp)
+        assert relf(to_f64(parts[r])[rows], ref_r) <= TOL[torch.bfloat16]
+    assert relf(to_f64(y)[rows], oracle.mlp(X, G, U, D)) <= TOL[torch.bfloat16]
+
+
+def test_llama70b_prefill_tp8_rank_full():
+    """One rank's MLP share at n=8192 (the benchmarked launch), sampled rows
+    checked against the oracle's rank partial computed from the full weights."""
+    w = synth.get("llama70b_prefill_tp8")
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    gate, up, down = _mlp_full_weights(w)
+    r = 3
+    wgu = T.tp_shard_gate_up(gate, up, r, w.tp)
+    wd = T.tp_shard_weights(down, 1, r, w.tp)
+    partial = T.tp_mlp_rank_forward(x, wgu, wd)
+    act = T.tp_gate_up_act_rank(x, wgu)
+    rows = synth.sample_rows(w.n, 8, w.seed(79))
+    X = to_f64(x[rows])
+    gb, ub, db = bits(gate), bits(up), bits(down)
+    G = oracle.bf16_bits_to_f64(oracle.shard(gb, 0, r, w.tp))
+    U = oracle.bf16_bits_to_f64(oracle.shard(ub, 0, r, w.tp))
+    D = oracle.bf16_bits_to_f64(oracle.shard(db, 1, r, w.tp))
+    ref_act = oracle.silu_mul(oracle.linear(X, G), oracle.linear(X, U))
+    assert relf(to_f64(act[rows]), ref_act) <= TOL[torch.bfloat16]
+    ref = oracle.mlp_rank(X, G, U, D, 0, 1)
+    assert relf(to_f64(partial[rows]), ref) <= TOL[torch.bfloat16]
+
+
+def test_llama70b_prefill_tp8_reduce_windows():
+    w = synth.get("llama70b_prefill_tp8")
+    parts = [gen(w, synth.T_PARTIAL + r, (w.n, w.h), 1.0) for r in range(w.tp)]
+    y = T.tp_partial_reduce(parts)
+    check_reduce_windows(parts, y, torch.bfloat16)
+
+
+def test_llama70b_attnproj_tp16_full():
+    w = synth.get("llama70b_attnproj_tp16")
+    hd, nq, nkv, t = w.head_dim, w.n_q, w.n_kv, w.tp
+    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
+    wq = gen(w, synth.T_WQ, (nq * hd, w.h), 0.02)
+    wk = gen(w, synth.T_WK, (nkv * hd, w.h), 0.02)
+    wv = gen(w, synth.T_WV, (nkv * hd, w.h), 0.02)
+    wo = gen(w, synth.T_WO, (w.h, nq * hd), 0.02)
+    rows = synth.sample_rows(w.n, 8, w.seed(80))
+    X = to_f64(x[rows])
+    qb, kb, vb, ob = bits(wq), bits(wk), bits(wv), bits(wo)
+    # column-parallel QKV for an odd rank (its KV head is shared with rank r-1)
+    for r in (5, 15):
+        wqkv = T.tp_shard_qkv(wq, wk, wv, nq, nkv, hd, r, t)
+        assert wqkv.shape == ((nq // t + 2) * hd, w.h)
+        qkv = T.tp_linear_rank_forward(x, wqkv)
+        ref = oracle.linear(X, oracle.bf16_bits_to_f64(oracle.shard_qkv(qb, kb, vb, nq, nkv, hd, r, t)))
+        assert relf(to_f64(qkv[rows]), ref) <= TOL[torch.bfloat16]
+    # row-parallel o_proj on per-rank stand-ins for the attention output, then the reduce
+    attn = [gen(w, synth.T_ATTN_OUT + r, (w.n, nq // t * hd), 1.0) for r in range(t)]
+    parts = []
+    for r in range(t):
+        wo_r = T.tp_shard_weights(wo, 1, r, t)
+        parts.append(T.tp_linear_rank_forward(attn[r], wo_r))
+    y = T.tp_partial_reduce(parts)
+    A = np.concatenate([to_f64(a[rows]) for a in attn], axis=1)
+    ref = oracle.linear(A, oracle.bf16_bits_to_f64(ob))
+    assert relf(to_f64(y[rows]), ref) <= TOL[torch.bfloat16]
+    for r in (0, 9):
+        ref_r = oracle.linear(to_f64(attn[r][rows]), oracle.bf16_bits_to_f64(oracle.shard(ob, 1, r, t)))
+        assert relf(to_f64(parts[r][rows]), ref_r) <= TOL[torch.bfloat16]
