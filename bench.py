@@ -308,15 +308,16 @@ def cpu_baseline(S, budget_s=12.0):
     G = to_f64(S["wgu"][:fl])
     U = to_f64(S["wgu"][fl:])
     D = to_f64(S["wd"])
-    X = to_f64(S["x"][:256])
+    cap = 4096
+    X = to_f64(S["x"][:cap])
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    rows = max(1, min(cores, 256))
+    rows = max(1, min(cores, cap))
     t0 = time.perf_counter()
     oracle.mlp_rank(X[:rows], G, U, D, 0, 1)
     dt = time.perf_counter() - t0
     # scale the sample to the time budget (rows in multiples of the thread count)
     more = int(budget_s / max(dt, 1e-3)) * rows
-    more = max(rows, min(more - more % rows, 256))
+    more = max(rows, min(more - more % rows, cap))
     t0 = time.perf_counter()
     oracle.mlp_rank(X[:more], G, U, D, 0, 1)
     dt2 = time.perf_counter() - t0
@@ -335,6 +336,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one 512 MiB device copy (tp_shard_weights, t=1) to calibrate HBM counters")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every tensor-parallel rank is emulated on a single device; "
@@ -391,6 +394,15 @@ def main():
         elif nm == "qwen_fp32":
             legs[nm] = leg_qwen_fp32(50)
         torch.cuda.empty_cache()
+
+    if a.copy_calib:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device=DEV)
+        dst = torch.empty_like(src).view(1, -1)
+        torch.cuda.synchronize()
+        T.tp_shard_weights(src.view(1, -1), 0, 0, 1, out=dst)
+        torch.cuda.synchronize()
+        log("bench: copy calibration: 512 MiB read + 512 MiB written by copy2d_kernel")
+        del src, dst
 
     cpu = None
     if not a.no_cpu:

@@ -25,6 +25,10 @@
 //     activation tiles a run shares stay in that XCD's L2.
 //
 // fp32 path: VALU FMA tiles (no reduced-precision fp32 modes).
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tpk {
@@ -44,6 +48,7 @@ struct GemmArgs {
     int64_t M, N, K, Nb;    // N = output columns (act columns when gated)
     int64_t k_split;        // K elements per split
     int tiles_m, tiles_n;
+    int vec_out;            // 1: output row length and base allow 8/16-byte stores
 };
 
 constexpr int GROUP_M = 8;
@@ -66,8 +71,15 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
-template <int BM, int BN, int BK, int WM, int WN, int EPI, bool VEC>
+// Output tile of one workgroup: BM rows of A (tokens) x BN rows of B
+// (weight rows = output columns; gated: BN/2 gate rows + the same BN/2 up
+// rows).  The weight fragment is the MFMA's A operand and the token fragment
+// its B operand, so in each 32x32 result lane l holds token row (l & 31) and
+// output columns 8g + 4(l >> 5) + q, q = 0..3: four consecutive columns per
+// group g, written with one 8-byte (bf16) or 16-byte (fp32) store.
+template <int BM, int BN, int WM, int WN, int EPI, bool VEC>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
+    constexpr int BK = 64;
     constexpr int NT = WM * WN * 64;
     constexpr int KC = BK / 8;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -79,8 +91,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
     static_assert(BM * KC % NT == 0 && BN * KC % NT == 0, "tile/threads mismatch");
     static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up MFMA tiles");
     constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
+    constexpr uint32_t SENT = 0x80000000u;   // buffer offset past num_records: the load returns 0
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (A_ELEMS + B_ELEMS)];
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -98,9 +111,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
     const uint16_t* __restrict__ A = p.A;
     const uint16_t* __restrict__ B = p.B;
 
-    // ---- global -> register staging ------------------------------------
-    u32x4 ra[A_LD], rb[B_LD];
-
+    // global row of B for local tile row lr (gated: gate rows then the same up rows)
     auto b_row = [&](int lr, bool& ok) -> int64_t {
         if (GATED) {
             const int half = BN / 2;
@@ -113,29 +124,70 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
         return r;
     };
 
+    // ---- global -> register staging ------------------------------------
+    // Vector path: raw buffer loads.  Each thread's chunks keep a fixed byte
+    // offset from a per-tile base that advances by BK per K step; chunks of
+    // rows outside the matrix (or past the K end in the last step) use an
+    // offset beyond num_records, for which the hardware returns zeros, so the
+    // loop has no per-load branches.
+    u32x4 ra[A_LD], rb[B_LD];
+    uint32_t offa[A_LD], offb[B_LD];
+    int kca[A_LD], kcb[B_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int v = tid + i * NT;
+        const int row = v / KC;
+        kca[i] = v % KC;
+        offa[i] = m0 + row < p.M ? (uint32_t)(((int64_t)row * p.K + kca[i] * 8) * 2) : SENT;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int v = tid + i * NT;
+        const int row = v / KC;
+        kcb[i] = v % KC;
+        bool ok;
+        const int64_t gb = b_row(row, ok);
+        offb[i] = ok ? (uint32_t)(((gb - n0) * p.K + kcb[i] * 8) * 2) : SENT;
+    }
+    const uint16_t* a_tile = A + m0 * p.K;
+    const uint16_t* b_tile = B + n0 * p.K;
+
     auto load_tile = [&](int64_t k0) {
+        if (VEC) {
+            const bool tail = k0 + BK > k_end;
+            __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+            __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < A_LD; ++i) {
+                const uint32_t o = (tail && k0 + kca[i] * 8 >= k_end) ? SENT : offa[i];
+                ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, o, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i) {
+                const uint32_t o = (tail && k0 + kcb[i] * 8 >= k_end) ? SENT : offb[i];
+                rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rs, o, 0, 0);
+            }
+            return;
+        }
+        // element-wise path (K not a multiple of 8 or unaligned operands)
+        auto load_chunk = [&](const uint16_t* src, int64_t row, bool ok, int64_t k) -> u32x4 {
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t lo = 0, hi = 0;
+                if (ok && k + 2 * q < k_end) lo = src[row * p.K + k + 2 * q];
+                if (ok && k + 2 * q + 1 < k_end) hi = src[row * p.K + k + 2 * q + 1];
+                w[q] = lo | (hi << 16);
+            }
+            return u32x4{w[0], w[1], w[2], w[3]};
+        };
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
             const int v = tid + i * NT;
             const int row = v / KC, kc = v % KC;
-            const int64_t gm = m0 + row;
-            const int64_t k = k0 + kc * 8;
-            if (VEC) {
-                if (gm < p.M && k < k_end)
-                    ra[i] = *reinterpret_cast<const u32x4*>(A + gm * p.K + k);
-                else
-                    ra[i] = u32x4{0u, 0u, 0u, 0u};
-            } else {
-                uint32_t w[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t lo = 0, hi = 0;
-                    if (gm < p.M && k + 2 * q < k_end) lo = A[gm * p.K + k + 2 * q];
-                    if (gm < p.M && k + 2 * q + 1 < k_end) hi = A[gm * p.K + k + 2 * q + 1];
-                    w[q] = lo | (hi << 16);
-                }
-                ra[i] = u32x4{w[0], w[1], w[2], w[3]};
-            }
+            ra[i] = load_chunk(A, m0 + row, m0 + row < p.M, k0 + kc * 8);
         }
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
@@ -143,23 +195,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
             const int row = v / KC, kc = v % KC;
             bool ok;
             const int64_t gb = b_row(row, ok);
-            const int64_t k = k0 + kc * 8;
-            if (VEC) {
-                if (ok && k < k_end)
-                    rb[i] = *reinterpret_cast<const u32x4*>(B + gb * p.K + k);
-                else
-                    rb[i] = u32x4{0u, 0u, 0u, 0u};
-            } else {
-                uint32_t w[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t lo = 0, hi = 0;
-                    if (ok && k + 2 * q < k_end) lo = B[gb * p.K + k + 2 * q];
-                    if (ok && k + 2 * q + 1 < k_end) hi = B[gb * p.K + k + 2 * q + 1];
-                    w[q] = lo | (hi << 16);
-                }
-                rb[i] = u32x4{w[0], w[1], w[2], w[3]};
-            }
+            rb[i] = load_chunk(B, gb, ok, k0 + kc * 8);
         }
     };
 
@@ -180,110 +216,211 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
         }
     };
 
-    // wave's B-tile row base for MFMA N-tile tn
-    auto b_tile_row = [&](int tn) -> int {
+    // B-tile row base of the wave's MFMA tile i (output-column side)
+    auto b_tile_row = [&](int i) -> int {
         if (GATED) {
             constexpr int HALF_W = WTN / 2;     // gate (or up) rows per wave
-            return tn < TN / 2 ? wn * HALF_W + tn * 32 : BN / 2 + wn * HALF_W + (tn - TN / 2) * 32;
+            return i < TN / 2 ? wn * HALF_W + i * 32 : BN / 2 + wn * HALF_W + (i - TN / 2) * 32;
         }
-        return wn * WTN + tn * 32;
+        return wn * WTN + i * 32;
     };
 
-    f32x16 acc[TM][TN];
+    // fragments, double-buffered in registers: sub-step kk+1 is read from LDS
+    // while the MFMAs of sub-step kk run
+    bf16x8 wf[2][TN], xf[2][TM];
+    auto read_frags = [&](int buf, int kk, int slot) {
+        const uint16_t* As = smem + buf * (A_ELEMS + B_ELEMS);
+        const uint16_t* Bs = As + A_ELEMS;
+        const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TN; ++i) {
+            const int row = b_tile_row(i) + (lane & 31);
+            wf[slot][i] = *reinterpret_cast<const bf16x8*>(Bs + row * BK + swz(row, c) * 8);
+        }
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TM; ++j) {
+            const int row = wm * WTM + j * 32 + (lane & 31);
+            xf[slot][j] = *reinterpret_cast<const bf16x8*>(As + row * BK + swz(row, c) * 8);
+        }
+    };
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // ---- main loop -------------------------------------------------------
+    // LDS buffer (kt & 1) holds K tile kt.  One K step = 4 sub-steps of 16;
+    // while the MFMAs of sub-step kk run, the fragments of kk+1 are read
+    // (register double buffer).  Tile kt+1 (staged in registers) is written
+    // to the other LDS buffer during sub-step 0, tile kt+2 is fetched into
+    // the registers during sub-step 1, and the barrier sits before sub-step
+    // 3, whose MFMAs cover the reads of the next tile's first fragments.
+    // The last two K steps are peeled so the steady-state body has no
+    // branches and the interleave hints apply to one scheduling region.
+    constexpr int MF = TN * TM;          // MFMAs per sub-step
+    constexpr int NR = TN + TM;          // fragment reads per sub-step
+    constexpr int NW = A_LD + B_LD;      // 16-byte LDS writes (and global loads) per K step
+
+    auto mfma_step = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][i], xf[slot][j], acc[i][j], 0, 0, 0);
+    };
+
+    auto k_step = [&](int kt, auto store_c, auto load_c, auto next_c) {
+        constexpr bool STORE = decltype(store_c)::value;   // tile kt+1 -> other LDS buffer
+        constexpr bool LOAD = decltype(load_c)::value;     // fetch tile kt+2
+        constexpr bool NEXT = decltype(next_c)::value;     // read tile kt+1's first fragments
+        const int cur = kt & 1;
+        // sub-step 0
+        read_frags(cur, 1, 1);
+        if (STORE) store_tile(cur ^ 1);
+        mfma_step(0);
+#pragma unroll
+        for (int q = 0; q < MF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (STORE && q < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+        // sub-step 1
+        read_frags(cur, 2, 0);
+        if (LOAD) load_tile(k_begin + (int64_t)(kt + 2) * BK);
+        mfma_step(1);
+#pragma unroll
+        for (int q = 0; q < MF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (LOAD && q < NW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        // sub-step 2
+        read_frags(cur, 3, 1);
+        mfma_step(0);
+#pragma unroll
+        for (int q = 0; q < MF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __syncthreads();
+        // sub-step 3
+        if (NEXT) read_frags(cur ^ 1, 0, 0);
+        mfma_step(1);
+#pragma unroll
+        for (int q = 0; q < MF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (NEXT && q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
     const int nk = (int)ceil_div(k_end - k_begin, BK);
     if (nk > 0) {
         load_tile(k_begin);
         store_tile(0);
+        if (nk > 1) load_tile(k_begin + BK);
         __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_tile(k_begin + (int64_t)(kt + 1) * BK);
-        const uint16_t* As = smem + cur * (A_ELEMS + B_ELEMS);
-        const uint16_t* Bs = As + A_ELEMS;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = kk * 2 + (lane >> 5);
-            bf16x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const bf16x8*>(As + row * BK + swz(row, c) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int row = b_tile_row(j) + (lane & 31);
-                bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + row * BK + swz(row, c) * 8);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        read_frags(0, 0, 0);
+        int kt = 0;
+        for (; kt + 2 < nk; ++kt) k_step(kt, T_{}, T_{}, T_{});
+        if (kt + 1 < nk) {
+            k_step(kt, T_{}, F_{}, T_{});
+            ++kt;
         }
-        if (kt + 1 < nk) store_tile(cur ^ 1);
-        __syncthreads();
+        k_step(kt, F_{}, F_{}, F_{});
     }
 
     // ---- epilogue --------------------------------------------------------
-    // 32x32 MFMA result layout: lane l holds column (l & 31) of the tile and,
-    // in accumulator r, row 8*(r/4) + 4*(l/32) + (r%4).
-    const int col_l = lane & 31;
-    const int row_l = 4 * (lane >> 5);
+    const int mrow = lane & 31;
+    const int ncol = 4 * (lane >> 5);
     if (EPI == EPI_SPLIT) {
         float* ws = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.M * p.Nb;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TM; ++j) {
+            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
+            if (gm >= p.M) continue;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t gc = n0 + b_tile_row(j) + col_l;
-                if (gc >= p.Nb) continue;
+            for (int i = 0; i < TN; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t gr = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                    if (gr < p.M) ws[gr * p.Nb + gc] = acc[i][j][r];
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gn = n0 + b_tile_row(i) + 8 * g + ncol;
+                    float* dst = ws + gm * p.Nb + gn;
+                    if (p.vec_out && gn + 3 < p.Nb) {
+                        *reinterpret_cast<float4*>(dst) =
+                            make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (gn + q < p.Nb) dst[q] = acc[i][j][4 * g + q];
+                    }
                 }
-            }
+        }
     } else if (GATED) {
         uint16_t* C = static_cast<uint16_t*>(p.C);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TM; ++j) {
+            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
+            if (gm >= p.M) continue;
 #pragma unroll
-            for (int j = 0; j < TN / 2; ++j) {
-                const int64_t gc = n0 + wn * (WTN / 2) + j * 32 + col_l;
-                if (gc >= p.N) continue;
+            for (int i = 0; i < TN / 2; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t gr = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                    if (gr < p.M) C[gr * p.N + gc] = f32_to_bf16(silu_mul(acc[i][j][r], acc[i][j + TN / 2][r]));
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gn = n0 + wn * (WTN / 2) + i * 32 + 8 * g + ncol;
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = silu_mul(acc[i][j][4 * g + q], acc[i + TN / 2][j][4 * g + q]);
+                    uint16_t* dst = C + gm * p.N + gn;
+                    if (p.vec_out && gn + 3 < p.N) {
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (gn + q < p.N) dst[q] = f32_to_bf16(v[q]);
+                    }
                 }
-            }
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TM; ++j) {
+            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
+            if (gm >= p.M) continue;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t gc = n0 + b_tile_row(j) + col_l;
-                if (gc >= p.N) continue;
-                const float bv = p.bias ? bf16_to_f32(p.bias[gc]) : 0.0f;
+            for (int i = 0; i < TN; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t gr = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                    if (gr >= p.M) continue;
-                    const float v = acc[i][j][r] + bv;
-                    if (EPI == EPI_STORE_F32)
-                        static_cast<float*>(p.C)[gr * p.N + gc] = v;
-                    else
-                        static_cast<uint16_t*>(p.C)[gr * p.N + gc] = f32_to_bf16(v);
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gn = n0 + b_tile_row(i) + 8 * g + ncol;
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v[q] = acc[i][j][4 * g + q];
+                        if (p.bias && gn + q < p.N) v[q] = v[q] + bf16_to_f32(p.bias[gn + q]);
+                    }
+                    if (EPI == EPI_STORE_F32) {
+                        float* dst = static_cast<float*>(p.C) + gm * p.N + gn;
+                        if (p.vec_out && gn + 3 < p.N) {
+                            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (gn + q < p.N) dst[q] = v[q];
+                        }
+                    } else {
+                        uint16_t* dst = static_cast<uint16_t*>(p.C) + gm * p.N + gn;
+                        if (p.vec_out && gn + 3 < p.N) {
+                            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (gn + q < p.N) dst[q] = f32_to_bf16(v[q]);
+                        }
+                    }
                 }
-            }
+        }
     }
 }
 
@@ -397,12 +534,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args p) {
 
 // ---- planning -------------------------------------------------------------
 
-enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2 };
+enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE = 3, K_BF16_HUGE8 = 4 };
 
-// Tile configurations: LARGE 128x128x64 with 2x2 waves; SMALL (M <= 64)
-// 64x128x64 with 1x2 waves.
-struct TileCfg { int bm, bn; };
-static TileCfg tile_cfg(int k) { return k == K_BF16_SMALL ? TileCfg{64, 128} : TileCfg{128, 128}; }
+// Tile configurations (BM tokens x BN weight rows, BK = 64):
+//   HUGE  256x256, 2x2 waves of 128x128 (prefill-sized problems)
+//   LARGE 128x128, 2x2 waves of 64x64
+//   SMALL  64x128, 1x2 waves of 64x64 (decode, M <= 64)
+struct TileCfg { int bm, bn, wm, wn; };
+static TileCfg tile_cfg(int k) {
+    switch (k) {
+        case K_BF16_HUGE: return TileCfg{256, 256, 2, 2};
+        case K_BF16_HUGE8: return TileCfg{256, 256, 2, 4};
+        case K_BF16_SMALL: return TileCfg{64, 128, 1, 2};
+        default: return TileCfg{128, 128, 2, 2};
+    }
+}
+
+static size_t lds_bytes(int k) {
+    TileCfg c = tile_cfg(k);
+    return (size_t)2 * (c.bm + c.bn) * 64 * sizeof(uint16_t);
+}
 
 static void tiles_for(int kern, int64_t M, int64_t N, bool gated, int& tm, int& tn) {
     if (kern == K_F32) {
@@ -415,6 +566,18 @@ static void tiles_for(int kern, int64_t M, int64_t N, bool gated, int& tm, int& 
     tn = (int)(gated ? ceil_div(N, c.bn / 2) : ceil_div(N, c.bn));
 }
 
+// 256x256 tiles: 8 waves of 128x64 (default: two waves per SIMD hide each
+// other's LDS and barrier waits) or 4 waves of 128x128; the environment
+// variable TPSHARD_GEMM_WAVES=4 selects the latter (tuning knob).
+static int huge_kernel() {
+    static int k = -1;
+    if (k < 0) {
+        const char* e = getenv("TPSHARD_GEMM_WAVES");
+        k = (e && atoi(e) == 4) ? K_BF16_HUGE : K_BF16_HUGE8;
+    }
+    return k;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     GemmPlan pl{};
     pl.splits = 1;
@@ -424,8 +587,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
         pl.kernel = K_F32;
         return pl;
     }
-    pl.kernel = M <= 64 ? K_BF16_SMALL : K_BF16_LARGE;
     int tm, tn;
+    if (M > 64) {
+        tiles_for(K_BF16_HUGE, M, N, gated, tm, tn);
+        pl.kernel = (int64_t)tm * tn >= 512 ? huge_kernel() : K_BF16_LARGE;
+    } else {
+        pl.kernel = K_BF16_SMALL;
+    }
     tiles_for(pl.kernel, M, N, gated, tm, tn);
     const int64_t tiles = (int64_t)tm * tn;
     const int64_t Nb = gated ? 2 * N : N;
@@ -447,23 +615,47 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     return pl;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-static void launch_bf16_cfg(const GemmArgs& a, int splits, bool vec, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int EPI, bool VEC>
+static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream_t s) {
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, VEC>;
+    if (lds > 65536) {
+        // opt in to more than 64 KiB of LDS once per instantiation
+        static bool done = false;
+        if (!done) {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            done = true;
+        }
+    }
     dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
-    dim3 block(WM * WN * 64);
+    hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), lds, s, a);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+static void launch_bf16_cfg(const GemmArgs& a, int splits, bool vec, size_t lds, hipStream_t s) {
     if (vec)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, WM, WN, EPI, true>), grid, block, 0, s, a);
+        launch_bf16_one<BM, BN, WM, WN, EPI, true>(a, splits, lds, s);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, WM, WN, EPI, false>), grid, block, 0, s, a);
+        launch_bf16_one<BM, BN, WM, WN, EPI, false>(a, splits, lds, s);
 }
 
 template <int BM, int BN, int WM, int WN>
-static void launch_bf16_epi(int epi, const GemmArgs& a, int splits, bool vec, hipStream_t s) {
+static void launch_bf16_epi(int epi, const GemmArgs& a, int splits, bool vec, size_t lds, hipStream_t s) {
     switch (epi) {
-        case EPI_STORE_BF16: launch_bf16_cfg<BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, vec, s); break;
-        case EPI_STORE_F32: launch_bf16_cfg<BM, BN, WM, WN, EPI_STORE_F32>(a, splits, vec, s); break;
-        case EPI_GATED_BF16: launch_bf16_cfg<BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, vec, s); break;
-        default: launch_bf16_cfg<BM, BN, WM, WN, EPI_SPLIT>(a, splits, vec, s); break;
+        case EPI_STORE_BF16: launch_bf16_cfg<BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, vec, lds, s); break;
+        case EPI_STORE_F32: launch_bf16_cfg<BM, BN, WM, WN, EPI_STORE_F32>(a, splits, vec, lds, s); break;
+        case EPI_GATED_BF16: launch_bf16_cfg<BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, vec, lds, s); break;
+        default: launch_bf16_cfg<BM, BN, WM, WN, EPI_SPLIT>(a, splits, vec, lds, s); break;
+    }
+}
+
+static void launch_bf16_kern(int kern, int epi, const GemmArgs& a, int splits, bool vec, hipStream_t s) {
+    const size_t lds = lds_bytes(kern);
+    switch (kern) {
+        case K_BF16_HUGE: launch_bf16_epi<256, 256, 2, 2>(epi, a, splits, vec, lds, s); break;
+        case K_BF16_HUGE8: launch_bf16_epi<256, 256, 2, 4>(epi, a, splits, vec, lds, s); break;
+        case K_BF16_SMALL: launch_bf16_epi<64, 128, 1, 2>(epi, a, splits, vec, lds, s); break;
+        default: launch_bf16_epi<128, 128, 2, 2>(epi, a, splits, vec, lds, s); break;
     }
 }
 
@@ -472,9 +664,9 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
                        void* ws, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int64_t Nb = gated ? 2 * N : N;
-    int tm, tn;
-    tiles_for(pl.kernel, M, N, gated && pl.splits == 1, tm, tn);
     if (pl.kernel == K_F32) {
+        int tm, tn;
+        tiles_for(K_F32, M, N, gated, tm, tn);
         F32Args a{static_cast<const float*>(A), static_cast<const float*>(B),
                   static_cast<const float*>(bias), static_cast<float*>(C), M, N, K, Nb, tm, tn};
         dim3 grid((unsigned)(tm * tn));
@@ -501,10 +693,8 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         a.tiles_n = (int)ceil_div(Nb, c.bn);
         a.N = Nb;
         a.C = ws;
-        if (pl.kernel == K_BF16_SMALL)
-            launch_bf16_epi<64, 128, 1, 2>(EPI_SPLIT, a, pl.splits, vec, s);
-        else
-            launch_bf16_epi<128, 128, 2, 2>(EPI_SPLIT, a, pl.splits, vec, s);
+        a.vec_out = (Nb % 4) == 0 && (((uintptr_t)ws) & 15u) == 0;
+        launch_bf16_kern(pl.kernel, EPI_SPLIT, a, pl.splits, vec, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         int64_t blocks = ceil_div(M * N, 256);
@@ -523,14 +713,14 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
                                wsf, pl.splits, M, N, Nb, bb, C);
         return hipGetLastError();
     }
+    int tm, tn;
+    tiles_for(pl.kernel, M, N, gated, tm, tn);
     a.tiles_m = tm;
     a.tiles_n = tn;
     a.C = C;
+    a.vec_out = (N % 4) == 0 && (((uintptr_t)C) & 15u) == 0;
     const int epi = gated ? EPI_GATED_BF16 : (out_dt == TP_F32 ? EPI_STORE_F32 : EPI_STORE_BF16);
-    if (pl.kernel == K_BF16_SMALL)
-        launch_bf16_epi<64, 128, 1, 2>(epi, a, 1, vec, s);
-    else
-        launch_bf16_epi<128, 128, 2, 2>(epi, a, 1, vec, s);
+    launch_bf16_kern(pl.kernel, epi, a, 1, vec, s);
     return hipGetLastError();
 }
 
