@@ -71,6 +71,116 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
+// B-tile row base of MFMA tile i of wave column wn (output-column side).
+// Gated tiles: the first TN/2 tiles are gate rows, the rest the same up rows.
+template <int BN, int WN, bool GATED>
+__device__ __forceinline__ int b_tile_row_of(int i, int wn) {
+    constexpr int WTN = BN / WN, TN = WTN / 32;
+    if (GATED) {
+        constexpr int HALF_W = WTN / 2;
+        return i < TN / 2 ? wn * HALF_W + i * 32 : BN / 2 + wn * HALF_W + (i - TN / 2) * 32;
+    }
+    return wn * WTN + i * 32;
+}
+
+// Writes one workgroup's accumulators: split-K partials (fp32), the gated
+// SiLU(g)*u activation (bf16), or C (+bias) in bf16/fp32.  Lane l holds
+// output row (l & 31) and columns 8g + 4(l >> 5) + q of each 32x32 tile.
+template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[BN / WN / 32][BM / WM / 32],
+                                              int64_t m0, int64_t n0, int wm, int wn, int lane) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    auto b_tile_row = [&](int i) { return b_tile_row_of<BN, WN, GATED>(i, wn); };
+    const int mrow = lane & 31;
+    const int ncol = 4 * (lane >> 5);
+    if (EPI == EPI_SPLIT) {
+        float* ws = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.M * p.Nb;
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
+            if (gm >= p.M) continue;
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gn = n0 + b_tile_row(i) + 8 * g + ncol;
+                    float* dst = ws + gm * p.Nb + gn;
+                    if (p.vec_out && gn + 3 < p.Nb) {
+                        *reinterpret_cast<float4*>(dst) =
+                            make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (gn + q < p.Nb) dst[q] = acc[i][j][4 * g + q];
+                    }
+                }
+        }
+    } else if (GATED) {
+        uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
+            if (gm >= p.M) continue;
+#pragma unroll
+            for (int i = 0; i < TN / 2; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gn = n0 + wn * (WTN / 2) + i * 32 + 8 * g + ncol;
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = silu_mul(acc[i][j][4 * g + q], acc[i + TN / 2][j][4 * g + q]);
+                    uint16_t* dst = C + gm * p.N + gn;
+                    if (p.vec_out && gn + 3 < p.N) {
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (gn + q < p.N) dst[q] = f32_to_bf16(v[q]);
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
+            if (gm >= p.M) continue;
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gn = n0 + b_tile_row(i) + 8 * g + ncol;
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v[q] = acc[i][j][4 * g + q];
+                        if (p.bias && gn + q < p.N) v[q] = v[q] + bf16_to_f32(p.bias[gn + q]);
+                    }
+                    if (EPI == EPI_STORE_F32) {
+                        float* dst = static_cast<float*>(p.C) + gm * p.N + gn;
+                        if (p.vec_out && gn + 3 < p.N) {
+                            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (gn + q < p.N) dst[q] = v[q];
+                        }
+                    } else {
+                        uint16_t* dst = static_cast<uint16_t*>(p.C) + gm * p.N + gn;
+                        if (p.vec_out && gn + 3 < p.N) {
+                            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (gn + q < p.N) dst[q] = f32_to_bf16(v[q]);
+                        }
+                    }
+                }
+        }
+    }
+}
+
 // Output tile of one workgroup: BM rows of A (tokens) x BN rows of B
 // (weight rows = output columns; gated: BN/2 gate rows + the same BN/2 up
 // rows).  The weight fragment is the MFMA's A operand and the token fragment
@@ -335,93 +445,201 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
         k_step(kt, F_{}, F_{}, F_{});
     }
 
-    // ---- epilogue --------------------------------------------------------
-    const int mrow = lane & 31;
-    const int ncol = 4 * (lane >> 5);
-    if (EPI == EPI_SPLIT) {
-        float* ws = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.M * p.Nb;
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
-            if (gm >= p.M) continue;
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t gn = n0 + b_tile_row(i) + 8 * g + ncol;
-                    float* dst = ws + gm * p.Nb + gn;
-                    if (p.vec_out && gn + 3 < p.Nb) {
-                        *reinterpret_cast<float4*>(dst) =
-                            make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (gn + q < p.Nb) dst[q] = acc[i][j][4 * g + q];
-                    }
-                }
+    gemm_epilogue<BM, BN, WM, WN, EPI>(p, acc, m0, n0, wm, wn, lane);
+}
+
+// Direct-to-LDS variant (16-byte-aligned operands, K a multiple of 8).
+// Tiles move from global memory straight into LDS with buffer_load ... lds:
+// one wave instruction fills 64 consecutive 16-byte LDS slots, lane l writing
+// slot l.  LDS layout: each tile row is its BK = 64 bf16 (8 slots) followed by
+// one pad slot, a row stride of 144 bytes.  Fragment reads (32 rows, one
+// 16-byte chunk) then hit 32 distinct banks groups for 32- and 64-bank LDS,
+// and the chunk of sub-step kk is at a constant offset (32 kk bytes) from a
+// per-fragment base, so reads use immediate offsets.  Lanes that land on a
+// pad slot fetch with an out-of-range offset and write zeros.  No VGPR
+// staging and no LDS stores: tile kt+1 streams into the other LDS buffer
+// while tile kt is multiplied; one wait + barrier per K step.  The two LDS
+// buffers are distinct objects so that the compiler's wait insertion can
+// tell the in-flight next tile from the one being read.
+template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) {
+    constexpr int BK = 64;
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    constexpr int RS = 9;                        // 16-byte slots per LDS row (8 data + 1 pad)
+    constexpr int ROWB = RS * 16;                // row stride in bytes
+    constexpr int A_SLOTS = BM * RS, B_SLOTS = BN * RS;
+    static_assert(A_SLOTS % 64 == 0 && B_SLOTS % 64 == 0, "tiles must fill whole 64-slot blocks");
+    constexpr int A_INSTR = A_SLOTS / 64, N_INSTR = (A_SLOTS + B_SLOTS) / 64;
+    constexpr int PER_WAVE = (N_INSTR + NW - 1) / NW;
+    static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up MFMA tiles");
+    constexpr int BUF_BYTES = (A_SLOTS + B_SLOTS) * 16;
+    constexpr uint32_t SENT = 0x80000000u;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[BUF_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid / WN, wn = wid % WN;
+
+    int tile_m, tile_n;
+    tile_coords(p.tiles_m, p.tiles_n, tile_m, tile_n);
+    const int64_t m0 = (int64_t)tile_m * BM;
+    const int64_t n0 = GATED ? (int64_t)tile_n * (BN / 2) : (int64_t)tile_n * BN;
+    const int64_t k_begin = (int64_t)blockIdx.y * p.k_split;
+    int64_t k_end = k_begin + p.k_split;
+    if (k_end > p.K) k_end = p.K;
+
+    auto b_row = [&](int lr, bool& ok) -> int64_t {
+        if (GATED) {
+            const int half = BN / 2;
+            const int64_t c = n0 + (lr < half ? lr : lr - half);
+            ok = c < p.N;
+            return lr < half ? c : p.N + c;
         }
-    } else if (GATED) {
-        uint16_t* C = static_cast<uint16_t*>(p.C);
+        const int64_t r = n0 + lr;
+        ok = r < p.Nb;
+        return r;
+    };
+
+    // per (instruction, lane): byte offset of the chunk within the tile's
+    // K window (SENT for pads and rows outside the matrix), and its chunk
+    // index (for the partial last K tile)
+    uint32_t off[PER_WAVE];
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
-            if (gm >= p.M) continue;
-#pragma unroll
-            for (int i = 0; i < TN / 2; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t gn = n0 + wn * (WTN / 2) + i * 32 + 8 * g + ncol;
-                    float v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = silu_mul(acc[i][j][4 * g + q], acc[i + TN / 2][j][4 * g + q]);
-                    uint16_t* dst = C + gm * p.N + gn;
-                    if (p.vec_out && gn + 3 < p.N) {
-                        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (gn + q < p.N) dst[q] = f32_to_bf16(v[q]);
-                    }
-                }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int64_t gm = m0 + wm * WTM + j * 32 + mrow;
-            if (gm >= p.M) continue;
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t gn = n0 + b_tile_row(i) + 8 * g + ncol;
-                    float v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        v[q] = acc[i][j][4 * g + q];
-                        if (p.bias && gn + q < p.N) v[q] = v[q] + bf16_to_f32(p.bias[gn + q]);
-                    }
-                    if (EPI == EPI_STORE_F32) {
-                        float* dst = static_cast<float*>(p.C) + gm * p.N + gn;
-                        if (p.vec_out && gn + 3 < p.N) {
-                            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                if (gn + q < p.N) dst[q] = v[q];
-                        }
-                    } else {
-                        uint16_t* dst = static_cast<uint16_t*>(p.C) + gm * p.N + gn;
-                        if (p.vec_out && gn + 3 < p.N) {
-                            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                if (gn + q < p.N) dst[q] = f32_to_bf16(v[q]);
-                        }
-                    }
-                }
+    for (int q = 0; q < PER_WAVE; ++q) {
+        const int j = wid * PER_WAVE + q;
+        const int slot = j * 64 + lane;
+        off[q] = SENT;
+        if (j < N_INSTR) {
+            if (slot < A_SLOTS) {
+                const int r = slot / RS, c = slot % RS;
+                if (c < 8 && m0 + r < p.M) off[q] = (uint32_t)(((int64_t)r * p.K + c * 8) * 2);
+            } else {
+                const int sb = slot - A_SLOTS;
+                const int r = sb / RS, c = sb % RS;
+                bool ok;
+                const int64_t gb = b_row(r, ok);
+                if (c < 8 && ok) off[q] = (uint32_t)(((gb - n0) * p.K + c * 8) * 2);
+            }
         }
     }
+    const uint16_t* a_tile = p.A + m0 * p.K;
+    const uint16_t* b_tile = p.B + n0 * p.K;
+
+    // KTAIL: the K range may end inside a tile (K or the split length not a
+    // multiple of BK); chunks at or past k_end are then fetched as zeros.
+    auto issue_tile = [&](int64_t k0, uint8_t* buf) {
+        __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+        __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+        const bool tail = KTAIL && k0 + BK > k_end;
+#pragma unroll
+        for (int q = 0; q < PER_WAVE; ++q) {
+            const int j = wid * PER_WAVE + q;
+            if (PER_WAVE * NW != N_INSTR && j >= N_INSTR) break;
+            uint32_t o = off[q];
+            if (KTAIL && tail) {
+                // chunk index of this lane's slot (pads count as chunk 8)
+                const int slot = j * 64 + lane;
+                const int c = (slot < A_SLOTS ? slot : slot - A_SLOTS) % RS;
+                if (k0 + c * 8 >= k_end) o = SENT;
+            }
+            auto* dst = (__attribute__((address_space(3))) void*)(buf + j * 1024);
+            if (j < A_INSTR)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, o, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, o, 0, 0, 0);
+        }
+    };
+
+    // fragment bases (bytes within a buffer); sub-step kk adds 32 kk
+    int fb_w[TN], fb_x[TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+        fb_w[i] = A_SLOTS * 16 + (b_tile_row_of<BN, WN, GATED>(i, wn) + (lane & 31)) * ROWB + (lane >> 5) * 16;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) fb_x[j] = (wm * WTM + j * 32 + (lane & 31)) * ROWB + (lane >> 5) * 16;
+
+    bf16x8 wf[2][TN], xf[2][TM];
+    auto read_frags = [&](const uint8_t* buf, int kk, int slot) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i) wf[slot][i] = *reinterpret_cast<const bf16x8*>(buf + fb_w[i] + kk * 32);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) xf[slot][j] = *reinterpret_cast<const bf16x8*>(buf + fb_x[j] + kk * 32);
+    };
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    constexpr int MF = TN * TM;          // MFMAs per 16-wide sub-step
+    constexpr int NR = TN + TM;          // fragment reads per sub-step
+    auto mfma_step = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][i], xf[slot][j], acc[i][j], 0, 0, 0);
+    };
+    // one MFMA, one fragment read, ... so reads overlap the matrix pipe
+    auto interleave = [&](bool reads) {
+#pragma unroll
+        for (int q = 0; q < MF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (reads && q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // One K step on tile `cur`: issue tile kt+1 into `nxt` first (ISSUE),
+    // sub-steps 0..2 read the next sub-step's fragments under the current
+    // MFMAs, then wait for the DMA + barrier, and sub-step 3 reads the next
+    // tile's first fragments under its MFMAs.
+    auto k_step = [&](auto issue_c, int64_t k_next, const uint8_t* cur, uint8_t* nxt) {
+        constexpr bool ISSUE = decltype(issue_c)::value;
+        if (ISSUE) issue_tile(k_next, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk) {
+            read_frags(cur, kk + 1, (kk + 1) & 1);
+            mfma_step(kk & 1);
+            interleave(true);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ISSUE) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of tile kt+1 landed
+            __syncthreads();                          // ... and every other wave's; tile kt fully read
+            read_frags(nxt, 0, 0);
+        }
+        mfma_step(1);
+        interleave(ISSUE);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int nk = (int)ceil_div(k_end - k_begin, BK);
+    if (nk > 0) {
+        issue_tile(k_begin, lds0);
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+        read_frags(lds0, 0, 0);
+        uint8_t* cur = lds0;
+        uint8_t* nxt = lds1;
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            k_step(std::true_type{}, k_begin + (int64_t)(kt + 1) * BK, cur, nxt);
+            uint8_t* t = cur;
+            cur = nxt;
+            nxt = t;
+        }
+        k_step(std::false_type{}, 0, cur, nxt);
+    }
+    gemm_epilogue<BM, BN, WM, WN, EPI>(p, acc, m0, n0, wm, wn, lane);
 }
 
 // Adds the split-K partial sums in split order and applies the epilogue.
@@ -617,6 +835,21 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
 
 template <int BM, int BN, int WM, int WN, int EPI, bool VEC>
 static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream_t s) {
+    static int use_dl = -1;
+    if (use_dl < 0) {
+        const char* e = getenv("TPSHARD_GEMM_DL");
+        use_dl = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    if (VEC && use_dl) {
+        // direct-to-LDS kernel: its two LDS buffers are static allocations
+        dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
+        const bool ktail = (a.K % 64) != 0 || (a.k_split % 64) != 0;
+        if (ktail)
+            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, a);
+        return;
+    }
     auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, VEC>;
     if (lds > 65536) {
         // opt in to more than 64 KiB of LDS once per instantiation
