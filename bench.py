@@ -116,6 +116,23 @@ def mlp_flops(n, h, fl):
     return 2.0 * n * h * (2 * fl) + 2.0 * n * fl * h
 
 
+def measured_traffic():
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy), or None if
+    the GEMM source changed since those counters were taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "traffic_gate_up_llama70b_prefill_tp8.json")
+    src_path = os.path.join(ROOT, "rank_sharded_layer_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(rec_path))
+        sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("gemm_source_sha256") != sha:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 # ---------------------------------------------------------------------------
 # legs
 # ---------------------------------------------------------------------------
@@ -396,12 +413,14 @@ def main():
         torch.cuda.empty_cache()
 
     if a.copy_calib:
-        src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device=DEV)
-        dst = torch.empty_like(src).view(1, -1)
+        # a [4096, 65536] bf16 copy (dim-1 shard with t=1): 512 MiB read and
+        # 512 MiB written by one copy2d_kernel launch of grid 32 x 4096
+        src = torch.empty((4096, 65536), dtype=torch.bfloat16, device=DEV)
+        dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        T.tp_shard_weights(src.view(1, -1), 0, 0, 1, out=dst)
+        T.tp_shard_weights(src, 1, 0, 1, out=dst)
         torch.cuda.synchronize()
-        log("bench: copy calibration: 512 MiB read + 512 MiB written by copy2d_kernel")
+        log("bench: copy calibration: 512 MiB read + 512 MiB written by copy2d_kernel (grid 32x4096)")
         del src, dst
 
     cpu = None
@@ -423,7 +442,7 @@ def main():
         "roofline": {"kernel": "gate_up GEMM + SiLU*up epilogue", "bound": "mfma",
                      "achieved": round(gu_flops / gu_ms / 1e9, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gu_flops / gu_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "legs": legs,
     }

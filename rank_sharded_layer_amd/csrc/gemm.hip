@@ -35,6 +35,7 @@ namespace tpk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GATED_BF16 = 2, EPI_SPLIT = 3,
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
 // while tile kt is multiplied; one wait + barrier per K step.  The two LDS
 // buffers are distinct objects so that the compiler's wait insertion can
 // tell the in-flight next tile from the one being read.
-template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
+template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL, int NST>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) {
     constexpr int BK = 64;
     constexpr int NW = WM * WN;
@@ -478,8 +479,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) 
     constexpr int BUF_BYTES = (A_SLOTS + B_SLOTS) * 16;
     constexpr uint32_t SENT = 0x80000000u;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[BUF_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[BUF_BYTES];
+    static_assert(NST >= 2, "at least double buffering");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * BUF_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -598,48 +599,210 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) 
         }
     };
 
-    // One K step on tile `cur`: issue tile kt+1 into `nxt` first (ISSUE),
-    // sub-steps 0..2 read the next sub-step's fragments under the current
-    // MFMAs, then wait for the DMA + barrier, and sub-step 3 reads the next
-    // tile's first fragments under its MFMAs.
-    auto k_step = [&](auto issue_c, int64_t k_next, const uint8_t* cur, uint8_t* nxt) {
-        constexpr bool ISSUE = decltype(issue_c)::value;
-        if (ISSUE) issue_tile(k_next, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < 3; ++kk) {
-            read_frags(cur, kk + 1, (kk + 1) & 1);
-            mfma_step(kk & 1);
-            interleave(true);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (ISSUE) {
-            __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of tile kt+1 landed
-            __syncthreads();                          // ... and every other wave's; tile kt fully read
-            read_frags(nxt, 0, 0);
-        }
-        mfma_step(1);
-        interleave(ISSUE);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
+    // LDS ring of NST stages: stage (kt mod NST) holds K tile kt; tiles
+    // kt+1 .. kt+NST-1 are in flight while tile kt is multiplied.
+    // One K step: issue tile kt+NST-1 (into the stage tile kt-1 used, free
+    // since the previous barrier), sub-steps 0..2 read the next sub-step's
+    // fragments under the current MFMAs, then wait until tile kt+1 has
+    // landed (this wave's DMA, then the barrier for everyone's), and
+    // sub-step 3 reads tile kt+1's first fragments under its MFMAs.
+    constexpr int PW_MIN = N_INSTR / NW;             // DMA instructions per tile, any wave
+    constexpr int VM_AHEAD = (NST - 2) * PW_MIN < 63 ? (NST - 2) * PW_MIN : 63;
+    auto stage = [&](int s) { return lds + s * BUF_BYTES; };
     const int nk = (int)ceil_div(k_end - k_begin, BK);
+    auto kof = [&](int t) { return k_begin + (int64_t)t * BK; };
     if (nk > 0) {
-        issue_tile(k_begin, lds0);
-        __builtin_amdgcn_s_waitcnt(0x0f70);
+#pragma unroll
+        for (int t = 0; t < NST - 1; ++t)
+            if (t < nk) issue_tile(kof(t), stage(t));
+        if (nk >= NST - 1)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (VM_AHEAD & 15) | ((VM_AHEAD >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
-        read_frags(lds0, 0, 0);
-        uint8_t* cur = lds0;
-        uint8_t* nxt = lds1;
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-            k_step(std::true_type{}, k_begin + (int64_t)(kt + 1) * BK, cur, nxt);
-            uint8_t* t = cur;
-            cur = nxt;
-            nxt = t;
-        }
-        k_step(std::false_type{}, 0, cur, nxt);
+        read_frags(stage(0), 0, 0);
+        int rs = 0;                                  // stage of tile kt
+        auto k_step = [&](int kt, auto more_c) {
+            constexpr bool MORE = decltype(more_c)::value;   // a tile kt+1 follows
+            const uint8_t* cur = stage(rs);
+            const int rn = rs + 1 == NST ? 0 : rs + 1;
+            const bool issue = MORE && kt + NST - 1 < nk;
+            if (issue) issue_tile(kof(kt + NST - 1), stage(rs == 0 ? NST - 1 : rs - 1));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < 3; ++kk) {
+                read_frags(cur, kk + 1, (kk + 1) & 1);
+                mfma_step(kk & 1);
+                interleave(true);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (MORE) {
+                if (issue)
+                    __builtin_amdgcn_s_waitcnt(0x0f70 | (VM_AHEAD & 15) | ((VM_AHEAD >> 4) << 14));
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0f70);
+                __syncthreads();
+                read_frags(stage(rn), 0, 0);
+            }
+            mfma_step(1);
+            interleave(MORE);
+            __builtin_amdgcn_sched_barrier(0);
+            rs = rn;
+        };
+        for (int kt = 0; kt + 1 < nk; ++kt) k_step(kt, std::true_type{});
+        k_step(nk - 1, std::false_type{});
     }
     gemm_epilogue<BM, BN, WM, WN, EPI>(p, acc, m0, n0, wm, wn, lane);
+}
+
+// Decode-sized GEMM (M <= 64 tokens): weight streaming.  HBM-bound on the
+// weights, so the design keeps many weight bytes in flight per CU and reads
+// every weight byte once:
+//   * a workgroup owns 16 output columns over the FULL K (gated: 16 gate rows
+//     and the same 16 up rows; plain: 16 weight rows) -- f_local/16 or N/16
+//     workgroups, two per CU;
+//   * its KW waves split K; each wave streams its weight slice and the
+//     matching token slice straight from global memory into MFMA operand
+//     registers (v_mfma_f32_16x16x32_bf16: lane l holds row l & 15 and k
+//     offset 8 (l >> 4), so the four lanes of a row read 64 contiguous bytes
+//     per load), two 64-wide K blocks ahead of the MFMAs;
+//   * the waves' partial sums meet in LDS and are added in wave order
+//     0..KW-1 (deterministic), then the gated SiLU(g)*u or plain epilogue.
+template <int EPI, int KW, bool KTAIL>
+__global__ __launch_bounds__(KW * 64) void gemm_bf16_decode_kernel(GemmArgs p) {
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    constexpr int WT = GATED ? 2 : 1;     // 16-row weight tiles per wave
+    constexpr int XT = 4;                 // 16-token tiles (64 tokens)
+    constexpr int NS = 3;                 // register stages (blocks in flight + 1)
+    constexpr uint32_t SENT = 0x80000000u;
+    constexpr int PER_WAVE = WT * XT * 4 * 64;
+    __shared__ __attribute__((aligned(16))) float red[KW * PER_WAVE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t n0 = (int64_t)blockIdx.x * 16;   // first output column of the workgroup
+
+    // K range of this wave (multiples of 64 except at the end)
+    const int64_t chunk = ceil_div(ceil_div(p.K, KW), 64) * 64;
+    const int64_t kw0 = (int64_t)wid * chunk;
+    int64_t kw1 = kw0 + chunk;
+    if (kw1 > p.K) kw1 = p.K;
+
+    const int q = lane >> 4;              // k offset 8q within a 32-wide sub-step
+    uint32_t wrow[WT], xrow[XT];
+#pragma unroll
+    for (int t = 0; t < WT; ++t) {
+        const int64_t c = n0 + (lane & 15);
+        int64_t row;
+        bool ok;
+        if (GATED) {
+            ok = c < p.N;
+            row = t == 0 ? c : p.N + c;
+        } else {
+            ok = c < p.Nb;
+            row = c;
+        }
+        wrow[t] = ok ? (uint32_t)((row * p.K + 8 * q) * 2) : SENT;
+    }
+#pragma unroll
+    for (int j = 0; j < XT; ++j) {
+        const int64_t m = 16 * j + (lane & 15);
+        xrow[j] = m < p.M ? (uint32_t)((m * p.K + 8 * q) * 2) : SENT;
+    }
+
+    f32x4 acc[WT][XT];
+#pragma unroll
+    for (int t = 0; t < WT; ++t)
+#pragma unroll
+        for (int j = 0; j < XT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[t][j][r] = 0.0f;
+
+    // a 64-wide K block = two 32-wide sub-steps
+    bf16x8 wv[NS][WT][2], xv[NS][XT][2];
+    // Offsets past num_records (the sentinel plus up to 64) load zeros.  With
+    // KTAIL (K not a multiple of 64), chunks at or past the wave's k end are
+    // fetched as zeros too.
+    auto load_block = [&](int64_t kb, int slot) {
+        __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + kb), (short)0, 0x7fffffff, 0x00020000);
+        __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + kb), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint32_t kill = 0;
+            if (KTAIL) kill = kb + 32 * s2 + 8 * q >= kw1 ? SENT : 0u;
+#pragma unroll
+            for (int t = 0; t < WT; ++t)
+                wv[slot][t][s2] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, (wrow[t] | kill) + 64 * s2, 0, 0));
+#pragma unroll
+            for (int j = 0; j < XT; ++j)
+                xv[slot][j][s2] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, (xrow[j] | kill) + 64 * s2, 0, 0));
+        }
+    };
+    auto mma_block = [&](int slot) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int t = 0; t < WT; ++t)
+#pragma unroll
+                for (int j = 0; j < XT; ++j)
+                    acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[slot][t][s2], xv[slot][j][s2], acc[t][j], 0, 0, 0);
+    };
+
+    // NS-1 blocks are in flight while a block is multiplied; fences keep the
+    // loads of block b+NS-1 ahead of the MFMAs of block b
+    const int nb = kw1 > kw0 ? (int)ceil_div(kw1 - kw0, 64) : 0;
+    auto kof = [&](int b) { return kw0 + (int64_t)b * 64; };
+#pragma unroll
+    for (int b = 0; b < NS - 1; ++b)
+        if (b < nb) load_block(kof(b), b);
+    int b = 0;
+    for (; b + NS - 1 < nb; b += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            if (b + u + NS - 1 < nb) load_block(kof(b + u + NS - 1), (u + NS - 1) % NS);
+            __builtin_amdgcn_sched_barrier(0);
+            if (b + u < nb) mma_block(u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+        if (b + u < nb) mma_block(u);
+
+    // ---- cross-wave reduction in LDS, in wave order --------------------
+#pragma unroll
+    for (int t = 0; t < WT; ++t)
+#pragma unroll
+        for (int j = 0; j < XT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wid * PER_WAVE + ((t * XT + j) * 4 + r) * 64 + lane] = acc[t][j][r];
+    __syncthreads();
+    // element e = (j, r, l): token 16 j + (l & 15), column n0 + 4 (l >> 4) + r
+    for (int e = tid; e < XT * 4 * 64; e += KW * 64) {
+        const int l = e & 63;
+        const int r = (e >> 6) & 3;
+        const int j = e >> 8;
+        const int64_t m = 16 * j + (l & 15);
+        const int64_t n = n0 + 4 * (l >> 4) + r;
+        float v0 = 0.0f, v1 = 0.0f;
+        for (int w = 0; w < KW; ++w) {
+            v0 = v0 + red[w * PER_WAVE + ((0 * XT + j) * 4 + r) * 64 + l];
+            if (GATED) v1 = v1 + red[w * PER_WAVE + ((1 * XT + j) * 4 + r) * 64 + l];
+        }
+        if (m >= p.M || n >= p.N) continue;
+        if (GATED) {
+            static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(silu_mul(v0, v1));
+        } else {
+            if (p.bias) v0 = v0 + bf16_to_f32(p.bias[n]);
+            if (EPI == EPI_STORE_F32)
+                static_cast<float*>(p.C)[m * p.N + n] = v0;
+            else
+                static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(v0);
+        }
+    }
 }
 
 // Adds the split-K partial sums in split order and applies the epilogue.
@@ -750,9 +913,77 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args p) {
     }
 }
 
+// fp32, few tokens (M <= 32): each wave owns RW weight rows (gated: RW/2
+// gate rows and the same up rows) for all M tokens; lane l takes k = l,
+// l+64, ... and keeps M x RW fp32 partial dot products (sequential FMAs);
+// the 64 lanes' partials are then added in lane order through LDS
+// (deterministic).  Launch-latency-sized problems get ~N/RW waves.
+template <bool GATED, int MT>
+__global__ __launch_bounds__(256) void gemm_f32_small_kernel(F32Args p) {
+    constexpr int RW = 4;                       // B rows per wave
+    constexpr int NW = 4;                       // waves per workgroup
+    __shared__ float red[NW][MT * RW][65];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // this wave's B rows
+    const int64_t unit = (int64_t)blockIdx.x * NW + w;     // RW/2 act columns (gated) or RW rows
+    int64_t brow[RW];
+    bool bok[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        if (GATED) {
+            const int64_t c = unit * (RW / 2) + (r % (RW / 2));
+            bok[r] = c < p.N;
+            brow[r] = r < RW / 2 ? c : p.N + c;
+        } else {
+            brow[r] = unit * RW + r;
+            bok[r] = brow[r] < p.Nb;
+        }
+    }
+    float acc[MT][RW];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[m][r] = 0.0f;
+    for (int64_t k = lane; k < p.K; k += 64) {
+        float wv[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) wv[r] = bok[r] ? p.B[brow[r] * p.K + k] : 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float xv = m < p.M ? p.A[(int64_t)m * p.K + k] : 0.0f;
+#pragma unroll
+            for (int r = 0; r < RW; ++r) acc[m][r] = fmaf(xv, wv[r], acc[m][r]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) red[w][m * RW + r][lane] = acc[m][r];
+    __syncthreads();
+    // lane e of wave w finishes value e (m = e / RW, r = e % RW) of this wave
+    for (int e = lane; e < MT * RW; e += 64) {
+        float v = 0.0f;
+        for (int l = 0; l < 64; ++l) v = v + red[w][e][l];
+        red[w][e][64] = v;
+    }
+    __syncthreads();
+    for (int e = lane; e < MT * RW; e += 64) {
+        const int m = e / RW, r = e % RW;
+        if (m >= p.M) continue;
+        if (GATED) {
+            if (r >= RW / 2) continue;
+            const int64_t c = unit * (RW / 2) + r;
+            if (c < p.N) p.C[(int64_t)m * p.N + c] = silu_mul(red[w][e][64], red[w][m * RW + r + RW / 2][64]);
+        } else {
+            const int64_t c = unit * RW + r;
+            if (c < p.N) p.C[(int64_t)m * p.N + c] = red[w][e][64] + (p.bias ? p.bias[c] : 0.0f);
+        }
+    }
+}
+
 // ---- planning -------------------------------------------------------------
 
-enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE = 3, K_BF16_HUGE8 = 4 };
+enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE = 3, K_BF16_HUGE8 = 4, K_BF16_DECODE = 5 };
 
 // Tile configurations (BM tokens x BN weight rows, BK = 64):
 //   HUGE  256x256, 2x2 waves of 128x128 (prefill-sized problems)
@@ -796,6 +1027,30 @@ static int huge_kernel() {
     return k;
 }
 
+// Weight-streaming decode kernel: off by default (the split-K tiled path
+// measures faster: this kernel re-reads the token block once per 16 output
+// columns); TPSHARD_GEMM_DECODE=1 selects it.
+static bool decode_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TPSHARD_GEMM_DECODE");
+        on = (e && atoi(e) == 1) ? 1 : 0;
+    }
+    return on == 1;
+}
+
+// Split-K target: about this many workgroups for shapes with fewer output
+// tiles than CUs (TPSHARD_SPLIT_TARGET overrides; tuning knob).
+static int64_t split_target() {
+    static int64_t t = -1;
+    if (t < 0) {
+        const char* e = getenv("TPSHARD_SPLIT_TARGET");
+        t = e ? atoll(e) : 1024;
+        if (t < 1) t = 1024;
+    }
+    return t;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     GemmPlan pl{};
     pl.splits = 1;
@@ -806,6 +1061,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
         return pl;
     }
     int tm, tn;
+    const int64_t Nb0 = gated ? 2 * N : N;
+    if (M <= 64 && K % 8 == 0 && Nb0 * K * 2 < ((int64_t)1 << 31) && M * K * 2 < ((int64_t)1 << 31) &&
+        decode_enabled()) {
+        pl.kernel = K_BF16_DECODE;     // weight streaming, full K per workgroup, no workspace
+        return pl;
+    }
     if (M > 64) {
         tiles_for(K_BF16_HUGE, M, N, gated, tm, tn);
         pl.kernel = (int64_t)tm * tn >= 512 ? huge_kernel() : K_BF16_LARGE;
@@ -817,7 +1078,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     const int64_t Nb = gated ? 2 * N : N;
     // fewer tiles than CUs: split K so that the launch fills the machine
     if (tiles < 256 && K >= 1024) {
-        int64_t want = ceil_div(1024, tiles);
+        int64_t want = ceil_div(split_target(), tiles);
         int64_t maxs = K / 512;
         int64_t s = want < maxs ? want : maxs;
         if (s > 1) {
@@ -844,10 +1105,13 @@ static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream
         // direct-to-LDS kernel: its two LDS buffers are static allocations
         dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
         const bool ktail = (a.K % 64) != 0 || (a.k_split % 64) != 0;
+        // LDS ring depth 2: deeper rings measured slower here because they
+        // cost a second resident workgroup per CU (occupancy beats depth)
+        constexpr int NST = 2;
         if (ktail)
-            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, a);
+            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, true, NST>), grid, dim3(WM * WN * 64), 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, a);
+            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, false, NST>), grid, dim3(WM * WN * 64), 0, s, a);
         return;
     }
     auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, VEC>;
@@ -902,6 +1166,19 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         tiles_for(K_F32, M, N, gated, tm, tn);
         F32Args a{static_cast<const float*>(A), static_cast<const float*>(B),
                   static_cast<const float*>(bias), static_cast<float*>(C), M, N, K, Nb, tm, tn};
+        if (M <= 32) {
+            // 4 waves per workgroup, 4 B rows (gated: 2 act columns) per wave
+            const int64_t units = gated ? ceil_div(N, 2) : ceil_div(N, 4);
+            dim3 g((unsigned)ceil_div(units, 4));
+            if (gated) {
+                if (M <= 16) hipLaunchKernelGGL((gemm_f32_small_kernel<true, 16>), g, dim3(256), 0, s, a);
+                else hipLaunchKernelGGL((gemm_f32_small_kernel<true, 32>), g, dim3(256), 0, s, a);
+            } else {
+                if (M <= 16) hipLaunchKernelGGL((gemm_f32_small_kernel<false, 16>), g, dim3(256), 0, s, a);
+                else hipLaunchKernelGGL((gemm_f32_small_kernel<false, 32>), g, dim3(256), 0, s, a);
+            }
+            return hipGetLastError();
+        }
         dim3 grid((unsigned)(tm * tn));
         if (gated)
             hipLaunchKernelGGL(gemm_f32_kernel<EPI_GATED_F32>, grid, dim3(256), 0, s, a);
@@ -910,6 +1187,15 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         return hipGetLastError();
     }
     const bool vec = (K % 8) == 0 && (((uintptr_t)A | (uintptr_t)B) & 15u) == 0;
+    if (pl.kernel == K_BF16_DECODE && !vec) {
+        // unaligned operands: the element-wise tiled kernel, without split-K
+        GemmPlan alt = pl;
+        alt.kernel = K_BF16_SMALL;
+        alt.splits = 1;
+        alt.k_split = K;
+        alt.ws_bytes = 0;
+        return launch_gemm(alt, A, B, bias, C, M, N, K, gated, dt, out_dt, ws, s);
+    }
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(A);
     a.B = static_cast<const uint16_t*>(B);
@@ -944,6 +1230,26 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         else
             hipLaunchKernelGGL(splitk_finalize_kernel<EPI_STORE_BF16>, dim3((unsigned)blocks), dim3(256), 0, s,
                                wsf, pl.splits, M, N, Nb, bb, C);
+        return hipGetLastError();
+    }
+    if (pl.kernel == K_BF16_DECODE) {
+        a.C = C;
+        const unsigned wgs = (unsigned)ceil_div(N, 16);
+        if (K % 64 == 0) {
+            if (gated)
+                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_GATED_BF16, 8, false>), dim3(wgs), dim3(512), 0, s, a);
+            else if (out_dt == TP_F32)
+                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_F32, 8, false>), dim3(wgs), dim3(512), 0, s, a);
+            else
+                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_BF16, 8, false>), dim3(wgs), dim3(512), 0, s, a);
+        } else {
+            if (gated)
+                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_GATED_BF16, 8, true>), dim3(wgs), dim3(512), 0, s, a);
+            else if (out_dt == TP_F32)
+                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_F32, 8, true>), dim3(wgs), dim3(512), 0, s, a);
+            else
+                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_BF16, 8, true>), dim3(wgs), dim3(512), 0, s, a);
+        }
         return hipGetLastError();
     }
     int tm, tn;

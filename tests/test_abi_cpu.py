@@ -63,14 +63,19 @@ def test_ring_schedule_matches_oracle(t, K):
 
 
 def test_workspace_queries():
-    # large-M shapes need no split-K workspace, decode shapes do
+    # large-M shapes need no split-K workspace
     assert T.tp_linear_workspace_bytes(8192, 3584, 8192, torch.bfloat16) == 0
     assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 0
+    # decode shapes have few output tiles: split-K partial sums need a workspace
     assert T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16) > 0
-    mlp = T.tp_mlp_workspace_bytes(64, 8192, 7168, torch.bfloat16)
-    act = 64 * 7168 * 2
-    assert mlp >= act + T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16)
-    assert mlp >= act + T.tp_linear_workspace_bytes(64, 7168, 8192, torch.bfloat16)
+    assert T.tp_linear_workspace_bytes(64, 7168, 8192, torch.bfloat16) > 0
+    # few output tiles and a long K: split-K partial sums need a workspace
+    assert T.tp_gate_up_workspace_bytes(80, 2048, 128, torch.bfloat16) > 0
+    assert T.tp_linear_workspace_bytes(64, 7167, 8192, torch.bfloat16) > 0
+    mlp = T.tp_mlp_workspace_bytes(80, 2048, 128, torch.bfloat16)
+    act = 80 * 128 * 2
+    assert mlp >= act + T.tp_gate_up_workspace_bytes(80, 2048, 128, torch.bfloat16)
+    assert mlp >= act + T.tp_linear_workspace_bytes(80, 128, 2048, torch.bfloat16)
     assert T.tp_mlp_workspace_bytes(16, 1024, 1536, torch.float32) >= 16 * 1536 * 4
 
 
@@ -120,9 +125,9 @@ def test_gemm_errors():
     assert st == 1                    # n = 0
     st, _ = _status(L.tp_linear_rank_forward, DUMMY, 4, 4, DUMMY, 4, NULL, 0, DUMMY, 1, NULL, 0, NULL)
     assert st == 3                    # f32 -> bf16 unsupported
-    st, msg = _status(L.tp_linear_rank_forward, DUMMY, 64, 7168, DUMMY, 8192, NULL, 1, DUMMY, 1, NULL, 0, NULL)
+    st, msg = _status(L.tp_linear_rank_forward, DUMMY, 64, 7167, DUMMY, 8192, NULL, 1, DUMMY, 1, NULL, 0, NULL)
     assert st == 6 and "workspace" in msg   # split-K shape without workspace
-    st, _ = _status(L.tp_gate_up_act_rank, DUMMY, 64, 8192, DUMMY, 7168, 1, DUMMY, NULL, 0, NULL)
+    st, _ = _status(L.tp_gate_up_act_rank, DUMMY, 80, 2048, DUMMY, 128, 1, DUMMY, NULL, 0, NULL)
     assert st == 6
     st, _ = _status(L.tp_mlp_rank_forward, DUMMY, 4, 8, DUMMY, DUMMY, 6, 1, DUMMY, 1, NULL, 0, NULL)
     assert st == 6

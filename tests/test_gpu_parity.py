@@ -303,9 +303,9 @@ def test_lm_head_concat_matches_oracle(t):
 
 
 def test_split_k_path_matches_oracle():
-    """Decode-sized shapes take the split-K path (fp32 partials in the
-    workspace, reduced in split order); same bar as the direct path."""
-    n, h, fl = 64, 2048, 256
+    """Few output tiles with a long K take the split-K path (fp32 partials in
+    the workspace, reduced in split order); same bar as the direct path."""
+    n, h, fl = 80, 2048, 256
     assert T.tp_gate_up_workspace_bytes(n, h, fl, torch.bfloat16) > 0
     x = rnd((n, h), 1.0, 130, torch.bfloat16)
     wgu = rnd((2 * fl, h), 0.02, 131, torch.bfloat16)
@@ -319,3 +319,37 @@ def test_split_k_path_matches_oracle():
     Wg, Wu = W[:fl], W[fl:]
     ref_p = oracle.linear(oracle.silu_mul(oracle.linear(xg, Wg), oracle.linear(xg, Wu)), to_f64(wd))
     assert relf(to_f64(p), ref_p) <= 1e-2
+
+
+@pytest.mark.parametrize("n", [1, 7, 33, 64])
+@pytest.mark.parametrize("k,m", [(64, 32), (200, 100), (1024, 96), (1000, 64), (4096, 160)])
+@pytest.mark.parametrize("out_dt", [torch.bfloat16, torch.float32])
+def test_decode_linear_matches_oracle(n, k, m, out_dt):
+    """Token counts <= 64 (the decode path; split-K where the shape has few
+    output tiles)."""
+    x = rnd((n, k), 1.0, 140 + n, torch.bfloat16)
+    w = rnd((m, k), 0.05, 141 + m, torch.bfloat16)
+    b = rnd((m,), 0.05, 142, torch.bfloat16)
+    for bias in (None, b):
+        y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+        ref = oracle.linear(to_f64(x), to_f64(w), to_f64(bias) if bias is not None else None)
+        assert relf(to_f64(y), ref) <= 1e-2
+
+
+@pytest.mark.parametrize("n", [1, 5, 64])
+@pytest.mark.parametrize("h,fl", [(64, 32), (1000, 48), (2048, 96), (8192, 64)])
+def test_decode_gate_up_matches_oracle(n, h, fl):
+    x = rnd((n, h), 1.0, 150 + n, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.05, 151 + fl, torch.bfloat16)
+    act = T.tp_gate_up_act_rank(x, wgu)
+    xg, W = to_f64(x), to_f64(wgu)
+    ref = oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:]))
+    assert relf(to_f64(act), ref) <= 1e-2
+
+
+def test_decode_is_deterministic():
+    x = rnd((64, 4096), 1.0, 160, torch.bfloat16)
+    w = rnd((256, 4096), 0.05, 161, torch.bfloat16)
+    a = bits(T.tp_linear_rank_forward(x, w))
+    b = bits(T.tp_linear_rank_forward(x, w))
+    assert np.array_equal(a, b)
