@@ -71,7 +71,12 @@ struct GemmPlan {
     int kernel;       // which tile configuration
     int splits;       // split-K factor (1 = none)
     int64_t k_split;  // K elements per split (multiple of the tile K) when splits > 1
-    size_t ws_bytes;  // fp32 workspace for split-K partial sums
+    size_t ws_bytes;  // fp32 workspace for split-K partial sums (or the tail pieces)
+    // balanced last round: the first full_tiles tiles run whole; each of the
+    // remaining tiles is cut into tail_split K pieces of tail_k elements
+    int full_tiles;
+    int tail_split;   // 0 = no tail split
+    int64_t tail_k;
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt);

@@ -50,9 +50,27 @@ struct GemmArgs {
     int64_t k_split;        // K elements per split
     int tiles_m, tiles_n;
     int vec_out;            // 1: output row length and base allow 8/16-byte stores
+    // balanced last round (direct-to-LDS kernel): blocks >= full_tiles are
+    // K pieces of the remaining tiles, tail_split pieces of tail_k each,
+    // written as fp32 [BM][BN] partial tiles to tail_ws
+    int full_tiles, tail_split;
+    int64_t tail_k;
+    float* tail_ws;
 };
 
 constexpr int GROUP_M = 8;
+
+// logical tile id -> (tile row, tile column), grouped GROUP_M tile rows tall
+__host__ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int per_group = GROUP_M * tiles_n;
+    const int group = b / per_group;
+    const int first_m = group * GROUP_M;
+    int gsize = tiles_m - first_m;
+    if (gsize > GROUP_M) gsize = GROUP_M;
+    const int in_group = b - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
 
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
     const int nb = tiles_m * tiles_n;
@@ -488,12 +506,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) 
     const int wm = wid / WN, wn = wid % WN;
 
     int tile_m, tile_n;
-    tile_coords(p.tiles_m, p.tiles_n, tile_m, tile_n);
+    int64_t k_begin, k_end;
+    const int bid = blockIdx.x;
+    const bool tail_unit = p.tail_split > 1 && bid >= p.full_tiles;
+    if (!tail_unit) {
+        int b = bid;
+        const int nb = p.tail_split > 1 ? p.full_tiles : p.tiles_m * p.tiles_n;
+        // XCD-aware remap: block b executes on XCD (b mod 8); give each XCD
+        // a contiguous range of logical tile ids
+        if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+        tile_of(b, p.tiles_m, p.tiles_n, tile_m, tile_n);
+        k_begin = (int64_t)blockIdx.y * p.k_split;
+        k_end = k_begin + p.k_split;
+    } else {
+        const int u = bid - p.full_tiles;
+        tile_of(p.full_tiles + u / p.tail_split, p.tiles_m, p.tiles_n, tile_m, tile_n);
+        k_begin = (int64_t)(u % p.tail_split) * p.tail_k;
+        k_end = k_begin + p.tail_k;
+    }
+    if (k_end > p.K) k_end = p.K;
     const int64_t m0 = (int64_t)tile_m * BM;
     const int64_t n0 = GATED ? (int64_t)tile_n * (BN / 2) : (int64_t)tile_n * BN;
-    const int64_t k_begin = (int64_t)blockIdx.y * p.k_split;
-    int64_t k_end = k_begin + p.k_split;
-    if (k_end > p.K) k_end = p.K;
 
     auto b_row = [&](int lr, bool& ok) -> int64_t {
         if (GATED) {
@@ -651,6 +684,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) 
         };
         for (int kt = 0; kt + 1 < nk; ++kt) k_step(kt, std::true_type{});
         k_step(nk - 1, std::false_type{});
+    }
+    if (tail_unit) {
+        // fp32 partial tile [BM][BN] in B-row order (gated: gate then up columns)
+        float* t = p.tail_ws + (int64_t)(bid - p.full_tiles) * BM * BN;
+        const int mrow = lane & 31, ncol = 4 * (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int lm = wm * WTM + j * 32 + mrow;
+                    const int ln = b_tile_row_of<BN, WN, GATED>(i, wn) + 8 * g + ncol;
+                    *reinterpret_cast<float4*>(t + lm * BN + ln) =
+                        make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                }
+        return;
     }
     gemm_epilogue<BM, BN, WM, WN, EPI>(p, acc, m0, n0, wm, wn, lane);
 }
@@ -981,18 +1031,55 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(F32Args p) {
     }
 }
 
+// Finishes the tiles of a balanced last round: adds each tile's K pieces in
+// piece order and applies the epilogue (gated SiLU(g)*u, or store + bias).
+template <int EPI>
+__global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs p, int BM, int BN) {
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    const int ntail = p.tiles_m * p.tiles_n - p.full_tiles;
+    const int cols = GATED ? BN / 2 : BN;
+    const int64_t per_tile = (int64_t)BM * cols;
+    const int64_t total = (int64_t)ntail * per_tile;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int t = (int)(idx / per_tile);
+        const int64_t rem = idx - (int64_t)t * per_tile;
+        const int lm = (int)(rem / cols), lc = (int)(rem % cols);
+        int tm, tn;
+        tile_of(p.full_tiles + t, p.tiles_m, p.tiles_n, tm, tn);
+        const int64_t m = (int64_t)tm * BM + lm;
+        const int64_t n = (int64_t)tn * cols + lc;
+        if (m >= p.M || n >= p.N) continue;
+        const float* base = p.tail_ws + (int64_t)t * p.tail_split * BM * BN;
+        float v0 = base[(int64_t)lm * BN + lc];
+        float v1 = GATED ? base[(int64_t)lm * BN + BN / 2 + lc] : 0.0f;
+        for (int s = 1; s < p.tail_split; ++s) {
+            v0 = v0 + base[(int64_t)s * BM * BN + (int64_t)lm * BN + lc];
+            if (GATED) v1 = v1 + base[(int64_t)s * BM * BN + (int64_t)lm * BN + BN / 2 + lc];
+        }
+        if (GATED) {
+            static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(silu_mul(v0, v1));
+        } else {
+            if (p.bias) v0 = v0 + bf16_to_f32(p.bias[n]);
+            if (EPI == EPI_STORE_F32)
+                static_cast<float*>(p.C)[m * p.N + n] = v0;
+            else
+                static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(v0);
+        }
+    }
+}
+
 // ---- planning -------------------------------------------------------------
 
-enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE = 3, K_BF16_HUGE8 = 4, K_BF16_DECODE = 5 };
+enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DECODE = 5 };
 
 // Tile configurations (BM tokens x BN weight rows, BK = 64):
-//   HUGE  256x256, 2x2 waves of 128x128 (prefill-sized problems)
+//   HUGE8 256x256, 2x4 waves of 128x64 (prefill-sized problems)
 //   LARGE 128x128, 2x2 waves of 64x64
 //   SMALL  64x128, 1x2 waves of 64x64 (decode, M <= 64)
 struct TileCfg { int bm, bn, wm, wn; };
 static TileCfg tile_cfg(int k) {
     switch (k) {
-        case K_BF16_HUGE: return TileCfg{256, 256, 2, 2};
         case K_BF16_HUGE8: return TileCfg{256, 256, 2, 4};
         case K_BF16_SMALL: return TileCfg{64, 128, 1, 2};
         default: return TileCfg{128, 128, 2, 2};
@@ -1002,6 +1089,15 @@ static TileCfg tile_cfg(int k) {
 static size_t lds_bytes(int k) {
     TileCfg c = tile_cfg(k);
     return (size_t)2 * (c.bm + c.bn) * 64 * sizeof(uint16_t);
+}
+
+// Workgroups of the direct-to-LDS kernel resident on one CU: its LDS ring
+// (2 buffers of BM + BN rows of 144 bytes) against the CU's 160 KiB.
+static int64_t wgs_per_cu(int k) {
+    TileCfg c = tile_cfg(k);
+    const int64_t ring = (int64_t)2 * (c.bm + c.bn) * 144;
+    const int64_t w = (int64_t)160 * 1024 / ring;
+    return w < 1 ? 1 : w;
 }
 
 static void tiles_for(int kern, int64_t M, int64_t N, bool gated, int& tm, int& tn) {
@@ -1015,17 +1111,10 @@ static void tiles_for(int kern, int64_t M, int64_t N, bool gated, int& tm, int& 
     tn = (int)(gated ? ceil_div(N, c.bn / 2) : ceil_div(N, c.bn));
 }
 
-// 256x256 tiles: 8 waves of 128x64 (default: two waves per SIMD hide each
-// other's LDS and barrier waits) or 4 waves of 128x128; the environment
-// variable TPSHARD_GEMM_WAVES=4 selects the latter (tuning knob).
-static int huge_kernel() {
-    static int k = -1;
-    if (k < 0) {
-        const char* e = getenv("TPSHARD_GEMM_WAVES");
-        k = (e && atoi(e) == 4) ? K_BF16_HUGE : K_BF16_HUGE8;
-    }
-    return k;
-}
+// 256x256 tiles run as 8 waves of 128x64 (two waves per SIMD hide each
+// other's LDS and barrier waits; 4 waves of 128x128 would need more than
+// the 256 architectural VGPRs for the accumulators and spill).
+static int huge_kernel() { return K_BF16_HUGE8; }
 
 // Weight-streaming decode kernel: off by default (the split-K tiled path
 // measures faster: this kernel re-reads the token block once per 16 output
@@ -1035,6 +1124,16 @@ static bool decode_enabled() {
     if (on < 0) {
         const char* e = getenv("TPSHARD_GEMM_DECODE");
         on = (e && atoi(e) == 1) ? 1 : 0;
+    }
+    return on == 1;
+}
+
+// balanced-last-round switch (TPSHARD_GEMM_TAIL=0 turns it off)
+static bool tail_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TPSHARD_GEMM_TAIL");
+        on = (e && atoi(e) == 0) ? 0 : 1;
     }
     return on == 1;
 }
@@ -1056,6 +1155,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     pl.splits = 1;
     pl.k_split = K;
     pl.ws_bytes = 0;
+    pl.full_tiles = 0;
+    pl.tail_split = 0;
+    pl.tail_k = K;
     if (dt == TP_F32) {
         pl.kernel = K_F32;
         return pl;
@@ -1068,7 +1170,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
         return pl;
     }
     if (M > 64) {
-        tiles_for(K_BF16_HUGE, M, N, gated, tm, tn);
+        tiles_for(K_BF16_HUGE8, M, N, gated, tm, tn);
         pl.kernel = (int64_t)tm * tn >= 512 ? huge_kernel() : K_BF16_LARGE;
     } else {
         pl.kernel = K_BF16_SMALL;
@@ -1091,6 +1193,29 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
             }
         }
     }
+    // Balanced last round: with tiles = q * slots + rem (0 < rem <= slots/2,
+    // slots = CUs x resident workgroups per CU), the last round would run
+    // half empty or worse; instead cut each of the last rem tiles into
+    // s = slots / rem K pieces so that round holds about one piece per slot,
+    // and add the pieces afterwards (tail_fixup_kernel, fixed order).  Only
+    // for long K: each piece costs a 4-byte-per-element partial tile written
+    // and read back, which pieces shorter than 1024 do not pay for.
+    const int64_t slots = 256 * wgs_per_cu(pl.kernel);
+    if (pl.splits == 1 && K % 8 == 0 && tiles > slots && tiles % slots != 0 && tail_enabled()) {
+        const int64_t rem = tiles % slots;
+        int64_t sp = slots / rem;
+        if (sp >= 2) {
+            const int64_t tk = ceil_div(ceil_div(K, sp), 64) * 64;
+            sp = ceil_div(K, tk);
+            if (sp >= 2 && tk >= 1024) {
+                TileCfg c = tile_cfg(pl.kernel);
+                pl.full_tiles = (int)(tiles - rem);
+                pl.tail_split = (int)sp;
+                pl.tail_k = tk;
+                pl.ws_bytes = (size_t)rem * (size_t)sp * (size_t)c.bm * (size_t)c.bn * sizeof(float);
+            }
+        }
+    }
     return pl;
 }
 
@@ -1102,8 +1227,10 @@ static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream
         use_dl = (e && atoi(e) == 0) ? 0 : 1;
     }
     if (VEC && use_dl) {
-        // direct-to-LDS kernel: its two LDS buffers are static allocations
-        dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
+        // direct-to-LDS kernel: its LDS ring is a static allocation
+        const int ntiles = a.tiles_m * a.tiles_n;
+        const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
+        dim3 grid((unsigned)units, (unsigned)splits);
         const bool ktail = (a.K % 64) != 0 || (a.k_split % 64) != 0;
         // LDS ring depth 2: deeper rings measured slower here because they
         // cost a second resident workgroup per CU (occupancy beats depth)
@@ -1112,9 +1239,15 @@ static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream
             hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, true, NST>), grid, dim3(WM * WN * 64), 0, s, a);
         else
             hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, false, NST>), grid, dim3(WM * WN * 64), 0, s, a);
+        if (a.tail_split > 1 && EPI != EPI_SPLIT) {
+            const int cols = EPI == EPI_GATED_BF16 ? BN / 2 : BN;
+            int64_t blocks = ceil_div((int64_t)(ntiles - a.full_tiles) * BM * cols, 256);
+            if (blocks > 8192) blocks = 8192;
+            hipLaunchKernelGGL((tail_fixup_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, a, BM, BN);
+        }
         return;
     }
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, VEC>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, VEC>;   // whole tiles only (no tail pieces)
     if (lds > 65536) {
         // opt in to more than 64 KiB of LDS once per instantiation
         static bool done = false;
@@ -1149,7 +1282,6 @@ static void launch_bf16_epi(int epi, const GemmArgs& a, int splits, bool vec, si
 static void launch_bf16_kern(int kern, int epi, const GemmArgs& a, int splits, bool vec, hipStream_t s) {
     const size_t lds = lds_bytes(kern);
     switch (kern) {
-        case K_BF16_HUGE: launch_bf16_epi<256, 256, 2, 2>(epi, a, splits, vec, lds, s); break;
         case K_BF16_HUGE8: launch_bf16_epi<256, 256, 2, 4>(epi, a, splits, vec, lds, s); break;
         case K_BF16_SMALL: launch_bf16_epi<64, 128, 1, 2>(epi, a, splits, vec, lds, s); break;
         default: launch_bf16_epi<128, 128, 2, 2>(epi, a, splits, vec, lds, s); break;
@@ -1257,6 +1389,12 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
     a.tiles_m = tm;
     a.tiles_n = tn;
     a.C = C;
+    if (pl.tail_split > 1 && vec && ws && (((uintptr_t)ws) & 15u) == 0) {
+        a.full_tiles = pl.full_tiles;
+        a.tail_split = pl.tail_split;
+        a.tail_k = pl.tail_k;
+        a.tail_ws = static_cast<float*>(ws);
+    }
     a.vec_out = (N % 4) == 0 && (((uintptr_t)C) & 15u) == 0;
     const int epi = gated ? EPI_GATED_BF16 : (out_dt == TP_F32 ? EPI_STORE_F32 : EPI_STORE_BF16);
     launch_bf16_kern(pl.kernel, epi, a, 1, vec, s);

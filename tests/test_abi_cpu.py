@@ -63,9 +63,15 @@ def test_ring_schedule_matches_oracle(t, K):
 
 
 def test_workspace_queries():
-    # large-M shapes need no split-K workspace
+    # large-M shapes whose tiles fill whole rounds need no workspace
+    # (8192 x 8192 in 256 x 256 tiles at one workgroup per CU: 1024 = 4 x 256)
     assert T.tp_linear_workspace_bytes(8192, 3584, 8192, torch.bfloat16) == 0
-    assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 0
+    # 8192 x 3584 in 128 x 128 tiles at two per CU: 1792 = 3 x 512 + 256, the
+    # last 256 tiles cut into two K pieces of 4096 (fp32 128 x 128 partials)
+    assert T.tp_linear_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 256 * 2 * 128 * 128 * 4
+    # 896 gated tiles = 3 rounds + 128: the last 128 tiles are cut into two
+    # K pieces each, whose fp32 256 x 256 partial tiles need a workspace
+    assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 128 * 2 * 256 * 256 * 4
     # decode shapes have few output tiles: split-K partial sums need a workspace
     assert T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16) > 0
     assert T.tp_linear_workspace_bytes(64, 7168, 8192, torch.bfloat16) > 0

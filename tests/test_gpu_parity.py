@@ -353,3 +353,55 @@ def test_decode_is_deterministic():
     a = bits(T.tp_linear_rank_forward(x, w))
     b = bits(T.tp_linear_rank_forward(x, w))
     assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# balanced last round: the tiles of a partial last round are cut along K,
+# their fp32 pieces added in piece order by a fix-up pass
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k,m", [(1024, 2600, 11342), (4900, 2600, 8100)])
+def test_tail_split_linear_matches_oracle(n, k, m):
+    """Tile counts one full round of resident workgroups plus a part round
+    (8 x 89 tiles of 128 at 2 per CU: 512 + 200; 20 x 32 tiles of 256 at
+    one per CU: 512 + 128); the part round's tiles are cut in two K pieces,
+    the last of them ending inside a 64-wide K tile."""
+    assert T.tp_linear_workspace_bytes(n, k, m, torch.bfloat16) > 0
+    x = rnd((n, k), 1.0, 170, torch.bfloat16)
+    w = rnd((m, k), 0.02, 171, torch.bfloat16)
+    b = rnd((m,), 0.02, 172, torch.bfloat16)
+    rows = sorted(set(synth.sample_rows(n, 16, 173) + list(range(n - 8, n))))
+    for bias in (None, b):
+        for out_dt in (torch.bfloat16, torch.float32):
+            y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+            ref = oracle.linear(to_f64(x[rows]), to_f64(w), to_f64(bias) if bias is not None else None)
+            got = to_f64(y[rows])
+            assert relf(got, ref) <= 1e-2, (bias is None, out_dt)
+            # the last tile columns (cut tiles), on their own
+            assert relf(got[:, -300:], ref[:, -300:]) <= 1e-2
+
+
+@pytest.mark.parametrize("n,h,fl", [(4900, 2600, 4000), (4096, 3200, 4696)])
+def test_tail_split_gate_up_matches_oracle(n, h, fl):
+    """Gated 256 x 128-act-column tiles: 20 x 32 = 512 + 128 (two K pieces
+    per cut tile) and 16 x 37 = 512 + 80 (three pieces), ragged last tile
+    row and column."""
+    assert T.tp_gate_up_workspace_bytes(n, h, fl, torch.bfloat16) > 0
+    x = rnd((n, h), 1.0, 180, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.02, 181, torch.bfloat16)
+    act = T.tp_gate_up_act_rank(x, wgu)
+    rows = sorted(set(synth.sample_rows(n, 12, 182) + list(range(n - 8, n))))
+    xg, W = to_f64(x[rows]), to_f64(wgu)
+    ref = oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:]))
+    got = to_f64(act[rows])
+    assert relf(got, ref) <= 1e-2
+    assert relf(got[:, -300:], ref[:, -300:]) <= 1e-2
+    again = T.tp_gate_up_act_rank(x, wgu)
+    assert torch.equal(act, again)          # fixed piece order: deterministic
+
+
+def test_tail_split_not_used_for_short_k_or_one_round():
+    # 594 tiles of 256 but K = 1024: pieces would be too short
+    assert T.tp_linear_workspace_bytes(512, 1024, 75968, torch.bfloat16) == 0
+    # 384 tiles of 128 at two resident workgroups per CU: a single round
+    assert T.tp_linear_workspace_bytes(8192, 8192, 768, torch.bfloat16) == 0
