@@ -92,14 +92,56 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ 
 
 // B-tile row base of MFMA tile i of wave column wn (output-column side).
 // Gated tiles: the first TN/2 tiles are gate rows, the rest the same up rows.
-template <int BN, int WN, bool GATED>
+template <int BN, int WN, bool GATED, int RB = 32>
 __device__ __forceinline__ int b_tile_row_of(int i, int wn) {
-    constexpr int WTN = BN / WN, TN = WTN / 32;
+    constexpr int WTN = BN / WN, TN = WTN / RB;
     if (GATED) {
         constexpr int HALF_W = WTN / 2;
-        return i < TN / 2 ? wn * HALF_W + i * 32 : BN / 2 + wn * HALF_W + (i - TN / 2) * 32;
+        return i < TN / 2 ? wn * HALF_W + i * RB : BN / 2 + wn * HALF_W + (i - TN / 2) * RB;
     }
-    return wn * WTN + i * 32;
+    return wn * WTN + i * RB;
+}
+
+// Stores 4 consecutive output columns gn .. gn+3 of output row gm: fp32
+// split-K partials (row length Nb), or C (+bias) in bf16/fp32, or the gated
+// activation (v already holds SiLU(g)*u).  Columns past the end are skipped.
+template <int EPI>
+__device__ __forceinline__ void store4(const GemmArgs& p, int64_t gm, int64_t gn, float (&v)[4]) {
+    if (EPI == EPI_SPLIT) {
+        float* dst = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.M * p.Nb + gm * p.Nb + gn;
+        if (p.vec_out && gn + 3 < p.Nb) {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (gn + q < p.Nb) dst[q] = v[q];
+        }
+        return;
+    }
+    if (EPI != EPI_GATED_BF16 && p.bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (gn + q < p.N) v[q] = v[q] + bf16_to_f32(p.bias[gn + q]);
+    }
+    if (EPI == EPI_STORE_F32) {
+        float* dst = static_cast<float*>(p.C) + gm * p.N + gn;
+        if (p.vec_out && gn + 3 < p.N) {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (gn + q < p.N) dst[q] = v[q];
+        }
+    } else {
+        uint16_t* dst = static_cast<uint16_t*>(p.C) + gm * p.N + gn;
+        if (p.vec_out && gn + 3 < p.N) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (gn + q < p.N) dst[q] = f32_to_bf16(v[q]);
+        }
+    }
 }
 
 // Writes one workgroup's accumulators: split-K partials (fp32), the gated
@@ -467,6 +509,57 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
     gemm_epilogue<BM, BN, WM, WN, EPI>(p, acc, m0, n0, wm, wn, lane);
 }
 
+// Which output tile and K range a workgroup of the tiled kernels owns.
+// Whole tiles come first, remapped so that each XCD (block b runs on XCD
+// b mod 8) gets a contiguous range of logical tile ids; with a balanced last
+// round the remaining tiles follow as tail_split K pieces each.
+struct Unit {
+    int tile_m, tile_n;
+    int64_t k_begin, k_end;
+    bool tail;
+};
+__device__ __forceinline__ Unit unit_of(const GemmArgs& p) {
+    Unit u;
+    const int bid = blockIdx.x;
+    u.tail = p.tail_split > 1 && bid >= p.full_tiles;
+    if (!u.tail) {
+        int b = bid;
+        const int nb = p.tail_split > 1 ? p.full_tiles : p.tiles_m * p.tiles_n;
+        if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+        tile_of(b, p.tiles_m, p.tiles_n, u.tile_m, u.tile_n);
+        u.k_begin = (int64_t)blockIdx.y * p.k_split;
+        u.k_end = u.k_begin + p.k_split;
+    } else {
+        const int v = bid - p.full_tiles;
+        tile_of(p.full_tiles + v / p.tail_split, p.tiles_m, p.tiles_n, u.tile_m, u.tile_n);
+        u.k_begin = (int64_t)(v % p.tail_split) * p.tail_k;
+        u.k_end = u.k_begin + p.tail_k;
+    }
+    if (u.k_end > p.K) u.k_end = p.K;
+    return u;
+}
+
+// A K piece of a balanced-last-round tile: the fp32 partial tile [BM][BN]
+// in B-row order (gated: gate rows, then up rows) goes to the workspace.
+template <int BM, int BN, int WM, int WN, bool GATED>
+__device__ __forceinline__ void store_tail_piece(const GemmArgs& p, f32x16 (&acc)[BN / WN / 32][BM / WM / 32],
+                                                 int wm, int wn, int lane) {
+    constexpr int WTM = BM / WM, TM = WTM / 32, TN = BN / WN / 32;
+    float* t = p.tail_ws + (int64_t)(blockIdx.x - p.full_tiles) * BM * BN;
+    const int mrow = lane & 31, ncol = 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int lm = wm * WTM + j * 32 + mrow;
+                const int ln = b_tile_row_of<BN, WN, GATED>(i, wn) + 8 * g + ncol;
+                *reinterpret_cast<float4*>(t + lm * BN + ln) =
+                    make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            }
+}
+
 // Direct-to-LDS variant (16-byte-aligned operands, K a multiple of 8).
 // Tiles move from global memory straight into LDS with buffer_load ... lds:
 // one wave instruction fills 64 consecutive 16-byte LDS slots, lane l writing
@@ -703,6 +796,238 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) 
         return;
     }
     gemm_epilogue<BM, BN, WM, WN, EPI>(p, acc, m0, n0, wm, wn, lane);
+}
+
+// Deep-pipelined direct-to-LDS kernel with 16x16x32 MFMAs (16-byte-aligned
+// operands, K a multiple of 8), for the 256 x 256 tiles.
+//   * MFMA shape: v_mfma_f32_16x16x32_bf16 moves half the accumulator data
+//     per flop of the 32x32x16 form; on this power-limited part that buys
+//     clock (measured ~15% more MFMA throughput on random operands).  Lane
+//     l holds operand row l & 15, K chunk l >> 4 (8 values), and result
+//     rows 4 (l >> 4) .. +3 (weight rows = output columns) of column l & 15
+//     (a token).
+//   * LDS ring of 4 stages of K = 32 (tile rows of 64 bytes, no padding):
+//     the stage of K step s+3 is filled by DMA while step s is multiplied;
+//     a step's data is certified (own DMA waited, then a barrier) two
+//     steps before it is multiplied.
+//   * each K step is 32 MFMAs per wave; the fragments of step s+1 are read
+//     into the other of two register slots under them.
+//   * the barrier is a bare s_barrier after a vmcnt wait: it does not wait
+//     for the fragment reads in flight.
+// Bank spreading: a ds_read_b128 serves 16 lanes (16 rows of one chunk
+// column) per LDS cycle across 64 banks = 16 groups of 16 bytes; a 64-byte
+// row covers 4 groups, so the 16-byte chunk c of tile row r sits at position
+// c ^ ((r >> 2) & 3) of its row and 16 consecutive rows hit 16 distinct
+// groups.  The DMA applies the permutation on the global side (lane l of an
+// instruction fills slot l and fetches the chunk that belongs there).
+template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p) {
+    constexpr int BK = 32;
+    constexpr int NST = 4;
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;          // 16-row MFMA blocks per wave
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    constexpr int ROWB = BK * 2;                         // 64 bytes per tile row
+    constexpr int A_BYTES = BM * ROWB;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int N_INSTR = STAGE / 1024;                // one wave instruction fills 1 KiB
+    constexpr int A_INSTR = A_BYTES / 1024;
+    static_assert(N_INSTR % NW == 0, "each wave issues the same number of DMA instructions");
+    constexpr int PW = N_INSTR / NW;
+    static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up MFMA blocks");
+    constexpr uint32_t SENT = 0x80000000u;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wid / WN, wn = wid % WN;
+
+    const Unit u = unit_of(p);
+    const int64_t m0 = (int64_t)u.tile_m * BM;
+    const int64_t n0 = GATED ? (int64_t)u.tile_n * (BN / 2) : (int64_t)u.tile_n * BN;
+    const int64_t k_begin = u.k_begin, k_end = u.k_end;
+
+    // DMA: instruction j of a stage fills slots 64 j .. 64 j + 63, i.e. tile
+    // rows 16 j + (lane >> 2), position lane & 3, which holds chunk cl
+    const int cl = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t off[PW];
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+        const int j = wid * PW + q;
+        const int r = j * 16 + (lane >> 2);
+        off[q] = SENT;
+        if (j < A_INSTR) {
+            if (m0 + r < p.M) off[q] = (uint32_t)(((int64_t)r * p.K + cl * 8) * 2);
+        } else {
+            const int lr = r - BM;
+            int64_t gb;
+            bool ok;
+            if (GATED) {
+                const int half = BN / 2;
+                const int64_t c = n0 + (lr < half ? lr : lr - half);
+                ok = c < p.N;
+                gb = lr < half ? c : p.N + c;
+            } else {
+                gb = n0 + lr;
+                ok = gb < p.Nb;
+            }
+            if (ok) off[q] = (uint32_t)(((gb - n0) * p.K + cl * 8) * 2);
+        }
+    }
+    const uint16_t* a_tile = p.A + m0 * p.K;
+    const uint16_t* b_tile = p.B + n0 * p.K;
+    auto issue_stage = [&](int64_t k0, int st) {
+        __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+        __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+        const bool tail = KTAIL && k0 + BK > k_end;
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            const int j = wid * PW + q;
+            uint32_t o = off[q];
+            if (KTAIL && tail && k0 + cl * 8 >= k_end) o = SENT;
+            auto* dst = (__attribute__((address_space(3))) void*)(lds + st * STAGE + j * 1024);
+            if (j < A_INSTR)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, o, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, o, 0, 0, 0);
+        }
+    };
+
+    // fragment reads: lane l reads row l & 15 of a 16-row block, chunk
+    // l >> 4, at its swizzled position
+    const int lo = (lane & 15) * ROWB + (((lane >> 4) ^ (((lane & 15) >> 2) & 3)) * 16);
+    const int xbase = wm * WTM * ROWB + lo;
+    const int wbase = A_BYTES + lo;
+
+    bf16x8 wf[2][TN], xf[2][TM];
+    auto read_frags = [&](int st, auto slot_c) {
+        constexpr int SL = decltype(slot_c)::value;
+        const uint8_t* b = lds + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+            wf[SL][i] = *reinterpret_cast<const bf16x8*>(b + wbase + b_tile_row_of<BN, WN, GATED, 16>(i, wn) * ROWB);
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+            xf[SL][j] = *reinterpret_cast<const bf16x8*>(b + xbase + j * 16 * ROWB);
+    };
+
+    f32x4 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int MF = TN * TM;
+    constexpr int NR = TN + TM;
+    auto mfma_slot = [&](auto slot_c) {
+        constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[SL][i], xf[SL][j], acc[i][j], 0, 0, 0);
+    };
+
+    const int nk = (int)ceil_div(k_end - k_begin, BK);
+    auto kof = [&](int s) { return k_begin + (int64_t)s * BK; };
+    auto vm_wait = [&](bool one_stage_in_flight) {
+        // this wave's DMA of older stages has landed; the newest (PW
+        // instructions) may still be in flight
+        if (one_stage_in_flight)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (PW & 15) | ((PW >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+
+    if (nk > 0) {
+        for (int s = 0; s < 3; ++s)
+            if (s < nk) issue_stage(kof(s), s);
+        vm_wait(nk > 2);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(0, S0{});
+        // K step s multiplies slot s mod 2 and reads step s + 1 into the
+        // other slot.  It first refills the stage of step s - 1 with step
+        // s + 3, and ends by certifying step s + 2.  FULL: all of this is
+        // known to apply (steady state, no branches between the MFMAs and
+        // the reads they hide); otherwise each part is checked.
+        auto step = [&](int s, auto sa, auto sb, auto full_c) {
+            constexpr bool FULL = decltype(full_c)::value;
+            const bool dma = FULL || s + 3 < nk;
+            const bool more = FULL || s + 1 < nk;
+            const bool bar = FULL || s + 2 < nk;
+            if (dma) issue_stage(kof(s + 3), (s + 3) & 3);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) read_frags((s + 1) & 3, sb);
+            mfma_slot(sa);
+#pragma unroll
+            for (int q = 0; q < MF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (FULL && (q % (MF / 4)) < NR / 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (bar) {
+                vm_wait(dma);
+                __builtin_amdgcn_s_barrier();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        int s = 0;
+        for (; s + 4 < nk; s += 2) {
+            step(s, S0{}, S1{}, T_{});
+            step(s + 1, S1{}, S0{}, T_{});
+        }
+        // at most 4 steps remain (s is even here): unrolled, so that the
+        // register slots stay compile-time
+        if (s < nk) step(s, S0{}, S1{}, F_{});
+        if (s + 1 < nk) step(s + 1, S1{}, S0{}, F_{});
+        if (s + 2 < nk) step(s + 2, S0{}, S1{}, F_{});
+        if (s + 3 < nk) step(s + 3, S1{}, S0{}, F_{});
+    }
+
+    // results: block (i, j), lane l: rows (output columns) b_row(i) + 4 (l >> 4)
+    // + q, column (token) wm WTM + 16 j + (l & 15)
+    const int mrow = lane & 15, ncol = 4 * (lane >> 4);
+    if (u.tail) {
+        float* t = p.tail_ws + (int64_t)(blockIdx.x - p.full_tiles) * BM * BN;
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const int lm = wm * WTM + j * 16 + mrow;
+                const int ln = b_tile_row_of<BN, WN, GATED, 16>(i, wn) + ncol;
+                *reinterpret_cast<float4*>(t + lm * BN + ln) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+        const int64_t gm = m0 + wm * WTM + j * 16 + mrow;
+        if (gm >= p.M) continue;
+        if (GATED) {
+#pragma unroll
+            for (int i = 0; i < TN / 2; ++i) {
+                const int64_t gn = n0 + wn * (WTN / 2) + i * 16 + ncol;
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = silu_mul(acc[i][j][q], acc[i + TN / 2][j][q]);
+                store4<EPI>(p, gm, gn, v);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const int64_t gn = n0 + b_tile_row_of<BN, WN, GATED, 16>(i, wn) + ncol;
+                float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                store4<EPI>(p, gm, gn, v);
+            }
+        }
+    }
 }
 
 // Decode-sized GEMM (M <= 64 tokens): weight streaming.  HBM-bound on the
@@ -1128,6 +1453,16 @@ static bool decode_enabled() {
     return on == 1;
 }
 
+// deep-pipelined large-tile kernel switch (TPSHARD_GEMM_PIPE=0 turns it off)
+static bool pipe_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TPSHARD_GEMM_PIPE");
+        on = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    return on == 1;
+}
+
 // balanced-last-round switch (TPSHARD_GEMM_TAIL=0 turns it off)
 static bool tail_enabled() {
     static int on = -1;
@@ -1219,6 +1554,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     return pl;
 }
 
+// adds the K pieces of a balanced last round (no-op without one)
+template <int BM, int BN, int EPI>
+static void launch_tail_fixup(const GemmArgs& a, int ntiles, hipStream_t s) {
+    if (a.tail_split > 1 && EPI != EPI_SPLIT) {
+        const int cols = EPI == EPI_GATED_BF16 ? BN / 2 : BN;
+        int64_t blocks = ceil_div((int64_t)(ntiles - a.full_tiles) * BM * cols, 256);
+        if (blocks > 8192) blocks = 8192;
+        hipLaunchKernelGGL((tail_fixup_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, a, BM, BN);
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, bool VEC>
 static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream_t s) {
     static int use_dl = -1;
@@ -1231,6 +1577,16 @@ static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream
         const int ntiles = a.tiles_m * a.tiles_n;
         const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
         dim3 grid((unsigned)units, (unsigned)splits);
+        if (pipe_enabled() && BM * BN >= 256 * 256) {
+            // deep-pipelined kernel (K steps of 32)
+            const bool kt32 = (a.K % 32) != 0 || (a.k_split % 32) != 0;
+            if (kt32)
+                hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, a);
+            else
+                hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, a);
+            launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
+            return;
+        }
         const bool ktail = (a.K % 64) != 0 || (a.k_split % 64) != 0;
         // LDS ring depth 2: deeper rings measured slower here because they
         // cost a second resident workgroup per CU (occupancy beats depth)
@@ -1239,12 +1595,7 @@ static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream
             hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, true, NST>), grid, dim3(WM * WN * 64), 0, s, a);
         else
             hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, false, NST>), grid, dim3(WM * WN * 64), 0, s, a);
-        if (a.tail_split > 1 && EPI != EPI_SPLIT) {
-            const int cols = EPI == EPI_GATED_BF16 ? BN / 2 : BN;
-            int64_t blocks = ceil_div((int64_t)(ntiles - a.full_tiles) * BM * cols, 256);
-            if (blocks > 8192) blocks = 8192;
-            hipLaunchKernelGGL((tail_fixup_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, a, BM, BN);
-        }
+        launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
         return;
     }
     auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, VEC>;   // whole tiles only (no tail pieces)
