@@ -60,6 +60,16 @@ struct GemmArgs {
 
 constexpr int GROUP_M = 8;
 
+// Workgroup barrier without a memory fence: memory operations in flight
+// (the next tiles' DMA, fragment reads) are not waited for; the kernels
+// wait for what they need with explicit counters.  The compiler-only fences
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // logical tile id -> (tile row, tile column), grouped GROUP_M tile rows tall
 __host__ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int per_group = GROUP_M * tiles_n;
@@ -946,7 +956,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
         for (int s = 0; s < 3; ++s)
             if (s < nk) issue_stage(kof(s), s);
         vm_wait(nk > 2);
-        __builtin_amdgcn_s_barrier();
+        bare_barrier();
         __builtin_amdgcn_sched_barrier(0);
         read_frags(0, S0{});
         // K step s multiplies slot s mod 2 and reads step s + 1 into the
@@ -971,7 +981,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
             __builtin_amdgcn_sched_barrier(0);
             if (bar) {
                 vm_wait(dma);
-                __builtin_amdgcn_s_barrier();
+                bare_barrier();
             }
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -1209,6 +1219,293 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float* __res
     }
 }
 
+// ---- weight-streaming decode GEMM (M <= 64) --------------------------------
+//
+// Decode multiplies a few token rows by a large weight matrix: HBM-bound on
+// the weights, which must stream in long contiguous runs (a 64-byte piece per
+// row, as a 32-wide K stage reads, runs at about two thirds of the bandwidth
+// that 256-byte and longer runs reach).  Design:
+//   * persistent grid, one workgroup per CU; the work is a list of units
+//     (output tile of 128 weight rows, K chunk of 128), tile-major, cut into
+//     gridDim.x equal contiguous ranges, so every CU streams the same number
+//     of weight bytes and its DMA never stops between tiles;
+//   * a unit stage holds the 64 token rows and the 128 weight rows over its
+//     K chunk: 256 contiguous bytes per row, fetched 4 rows x 256 B per wave
+//     instruction straight into LDS; a ring of 3 stages keeps two units of
+//     weights (64 KiB) in flight per CU;
+//   * 4 waves, each 32 weight rows x 64 tokens, 16x16x32 MFMAs;
+//   * when a workgroup leaves a tile it writes its fp32 partial tile; a
+//     finalize pass adds a tile's partials in K order (deterministic) and
+//     applies the epilogue.
+// LDS rows are 256 bytes (16 chunks); chunk c of row r sits at position
+// c ^ (r & 15), so the 16 rows of a fragment read hit 16 distinct bank groups.
+constexpr int STR_BM = 64, STR_BN = 128, STR_BK = 128, STR_NST = 3;
+constexpr int STR_ROWB = STR_BK * 2;
+constexpr int STR_A_BYTES = STR_BM * STR_ROWB;
+constexpr int STR_STAGE = (STR_BM + STR_BN) * STR_ROWB;         // 48 KiB
+constexpr int STR_LDS = STR_NST * STR_STAGE;                    // 144 KiB
+constexpr int STR_NW = 4;
+constexpr int STR_PW = STR_STAGE / 1024 / STR_NW;               // DMA instructions per wave and unit
+constexpr int STR_A_INSTR = STR_A_BYTES / 1024;
+
+__host__ __device__ __forceinline__ int64_t str_unit_begin(int w, int64_t units, int P) {
+    return ((int64_t)w * units) / P;
+}
+
+// One streamed product: C-partials of A[M, K] . B[Nb, K]^T, tiles of 128 B
+// rows (gated: 64 gate rows and the same 64 up rows), units of 128 K.
+struct StreamOp {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t M, N, K, Nb;
+    int64_t units;
+    int kc, maxseg;
+    float* part;            // [P][maxseg][BM][BN] fp32 partial tiles
+};
+
+__host__ __device__ __forceinline__ StreamOp make_stream_op(const uint16_t* A, const uint16_t* B, int64_t M,
+                                                            int64_t N, int64_t K, bool gated, float* part,
+                                                            int P) {
+    StreamOp o;
+    o.A = A;
+    o.B = B;
+    o.M = M;
+    o.N = N;
+    o.K = K;
+    o.Nb = gated ? 2 * N : N;
+    const int64_t cols = gated ? STR_BN / 2 : STR_BN;
+    const int64_t tiles = (N + cols - 1) / cols;
+    o.kc = (int)((K + STR_BK - 1) / STR_BK);
+    o.units = tiles * o.kc;
+    const int64_t per_wg = (o.units + P - 1) / P;
+    o.maxseg = (int)((per_wg + o.kc - 1) / o.kc + 1);
+    o.part = part;
+    return o;
+}
+
+// Per-lane DMA bookkeeping of a streamed product (fixed for all its units):
+// instruction q of this wave fills tile rows 4 j + (lane >> 4), j = wid PW + q,
+// position lane & 15, i.e. chunk (lane & 15) ^ (row & 15).  boff: byte offset
+// relative to the tile's first row and the unit's K start (both folded into
+// the uniform buffer base); bcol: output column of a weight row within the
+// tile (token rows: 0, or -1 past M); kchunk: the chunk's K offset.
+template <bool GATED>
+struct StreamLanes {
+    uint32_t boff[STR_PW];
+    int bcol[STR_PW];
+    int kchunk[STR_PW];
+    __device__ __forceinline__ void init(const StreamOp& o, int wid, int lane) {
+#pragma unroll
+        for (int q = 0; q < STR_PW; ++q) {
+            const int jj = wid * STR_PW + q;
+            const int r = jj * 4 + (lane >> 4);
+            const int c = (lane & 15) ^ (r & 15);
+            kchunk[q] = c * 8;
+            if (jj < STR_A_INSTR) {
+                boff[q] = (uint32_t)(((int64_t)r * o.K + c * 8) * 2);
+                bcol[q] = r < o.M ? 0 : -1;
+            } else {
+                const int lr = r - STR_BM;
+                int64_t g;
+                if (GATED) {
+                    g = lr < STR_BN / 2 ? lr : o.N + (lr - STR_BN / 2);
+                    bcol[q] = lr < STR_BN / 2 ? lr : lr - STR_BN / 2;
+                } else {
+                    g = lr;
+                    bcol[q] = lr;
+                }
+                boff[q] = (uint32_t)((g * o.K + c * 8) * 2);
+            }
+        }
+    }
+    // DMA of unit u into ring slot st: token rows (PART & 1) and / or weight
+    // rows (PART & 2)
+    template <int PART, bool KTAIL>
+    __device__ __forceinline__ void issue(const StreamOp& o, uint8_t* lds, int64_t u, int st, int wid) const {
+        constexpr int cols = GATED ? STR_BN / 2 : STR_BN;
+        constexpr uint32_t SENT = 0x80000000u;
+        const int64_t t = u / o.kc;
+        const int64_t k0 = (u - t * o.kc) * STR_BK;
+        const int64_t n0 = t * cols;
+        const int ncols = (int)((o.N - n0) < cols ? (o.N - n0) : cols);
+        const int kleft = (int)((o.K - k0) < STR_BK ? (o.K - k0) : STR_BK);
+        __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(o.A + k0), (short)0, 0x7fffffff, 0x00020000);
+        __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(o.B + n0 * o.K + k0), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < STR_PW; ++q) {
+            const int jj = wid * STR_PW + q;
+            const bool is_a = jj < STR_A_INSTR;
+            if (is_a && !(PART & 1)) continue;
+            if (!is_a && !(PART & 2)) continue;
+            bool ok = is_a ? bcol[q] >= 0 : bcol[q] < ncols;
+            if (KTAIL) ok = ok && kchunk[q] < kleft;
+            const uint32_t off = ok ? boff[q] : SENT;
+            auto* dst = (__attribute__((address_space(3))) void*)(lds + st * STR_STAGE + jj * 1024);
+            if (is_a)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, off, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, off, 0, 0, 0);
+        }
+    }
+};
+
+// Runs workgroup w's range of units of o.  With weights_ahead, the weight
+// rows of the range's first two units were already issued (into slots 0 and
+// 1) and only their token rows are fetched here.
+template <bool GATED, bool KTAIL>
+__device__ __forceinline__ void stream_units(const StreamOp& o, uint8_t* lds, int w, int P, bool weights_ahead) {
+    constexpr int BM = STR_BM, BN = STR_BN, ROWB = STR_ROWB, NST = STR_NST, PW = STR_PW;
+    constexpr int WTN = BN / STR_NW;                     // 32 weight rows per wave
+    constexpr int TM = BM / 16, TN = WTN / 16;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t u0 = str_unit_begin(w, o.units, P), u1 = str_unit_begin(w + 1, o.units, P);
+    const int n = (int)(u1 - u0);
+    StreamLanes<GATED> L;
+    L.init(o, wid, lane);
+
+    int lo[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) lo[kk] = (lane & 15) * ROWB + ((((4 * kk + (lane >> 4)) ^ (lane & 15))) * 16);
+    auto wrow = [&](int i) {
+        return GATED ? (i < TN / 2 ? wid * (WTN / 2) + i * 16 : BN / 2 + wid * (WTN / 2) + (i - TN / 2) * 16)
+                     : wid * WTN + i * 16;
+    };
+
+    f32x4 acc[TN][TM];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int j = 0; j < TM; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    zero_acc();
+    bf16x8 wf[4][TN], xf[4][TM];
+    auto read_frags = [&](int st, int kk) {
+        const uint8_t* b = lds + st * STR_STAGE + lo[kk];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) wf[kk][i] = *reinterpret_cast<const bf16x8*>(b + STR_A_BYTES + wrow(i) * ROWB);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) xf[kk][j] = *reinterpret_cast<const bf16x8*>(b + j * 16 * ROWB);
+    };
+    auto mfma = [&](int kk) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[kk][i], xf[kk][j], acc[i][j], 0, 0, 0);
+    };
+
+    if (n <= 0) return;
+    constexpr int AHEAD = NST - 1;              // units in flight beyond the one multiplied
+    for (int a = 0; a < AHEAD; ++a)
+        if (a < n) {
+            if (weights_ahead) L.template issue<1, KTAIL>(o, lds, u0 + a, a, wid);
+            else L.template issue<3, KTAIL>(o, lds, u0 + a, a, wid);
+        }
+    int seg = 0;
+    bool full_wait = weights_ahead;             // unit 1 may not be the newest DMA: wait for all once
+    for (int i = 0; i < n; ++i) {
+        const int64_t u = u0 + i;
+        const int st = i % NST;
+        // unit i has landed (this wave's DMA), then everyone's (barrier);
+        // the barrier also tells that unit i-1's slot has been read out
+        constexpr int NEWER = (AHEAD - 1) * PW;  // DMA instructions of newer units that may stay in flight
+        if (NEWER > 0 && i + AHEAD - 1 < n && !full_wait)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (NEWER & 15) | ((NEWER >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+        full_wait = false;
+        bare_barrier();
+        if (i + AHEAD < n) L.template issue<3, KTAIL>(o, lds, u + AHEAD, (i + AHEAD) % NST, wid);
+        // all four sub-steps' fragments at once: one LDS latency per unit
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) read_frags(st, kk);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) mfma(kk);
+        const int64_t t = u / o.kc;
+        if (i + 1 == n || (u + 1) / o.kc != t) {
+            // leaving tile t: fp32 partial tile [BM tokens][BN B rows]
+            float* out = o.part + ((int64_t)w * o.maxseg + seg) * BM * BN;
+#pragma unroll
+            for (int i2 = 0; i2 < TN; ++i2)
+#pragma unroll
+                for (int j = 0; j < TM; ++j) {
+                    const int lm = j * 16 + (lane & 15);
+                    const int ln = wrow(i2) + 4 * (lane >> 4);
+                    *reinterpret_cast<float4*>(out + lm * BN + ln) =
+                        make_float4(acc[i2][j][0], acc[i2][j][1], acc[i2][j][2], acc[i2][j][3]);
+                }
+            zero_acc();
+            ++seg;
+            full_wait = true;                   // stores in flight: the next wait counts them too
+        }
+    }
+}
+
+// Adds tile t's partials (from the workgroups whose unit ranges cover it, in
+// workgroup = K order) for token rows m and 4 consecutive columns from g4,
+// and stores them through the epilogue of `out`.
+template <int EPI>
+__device__ __forceinline__ void stream_finish4(const StreamOp& o, const GemmArgs& out, int P, int64_t t, int w0,
+                                               int m, int g4) {
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    constexpr int BM = STR_BM, BN = STR_BN;
+    constexpr int cols = GATED ? BN / 2 : BN;
+    const int64_t first = t * o.kc, last = first + o.kc - 1;
+    float v0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool any = false;
+    for (int w = w0; w < P; ++w) {
+        const int64_t b = str_unit_begin(w, o.units, P), e = str_unit_begin(w + 1, o.units, P);
+        if (b > last) break;
+        if (e <= first || e <= b) continue;        // before the tile, or an empty range
+        const int seg = (int)(t - b / o.kc);
+        const float* part = o.part + ((int64_t)w * o.maxseg + seg) * BM * BN + (int64_t)m * BN;
+        const float4 a = *reinterpret_cast<const float4*>(part + g4);
+        float4 c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (GATED) c = *reinterpret_cast<const float4*>(part + BN / 2 + g4);
+        if (!any) {
+            v0[0] = a.x; v0[1] = a.y; v0[2] = a.z; v0[3] = a.w;
+            v1[0] = c.x; v1[1] = c.y; v1[2] = c.z; v1[3] = c.w;
+            any = true;
+        } else {
+            v0[0] = v0[0] + a.x; v0[1] = v0[1] + a.y; v0[2] = v0[2] + a.z; v0[3] = v0[3] + a.w;
+            v1[0] = v1[0] + c.x; v1[1] = v1[1] + c.y; v1[2] = v1[2] + c.z; v1[3] = v1[3] + c.w;
+        }
+    }
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = GATED ? silu_mul(v0[q], v1[q]) : v0[q];
+    store4<EPI>(out, m, t * cols + g4, v);
+}
+
+// first workgroup whose unit range meets tile t
+__device__ __forceinline__ int stream_first_wg(const StreamOp& o, int P, int64_t t) {
+    const int64_t first = t * o.kc;
+    int w0 = (int)((first * P) / o.units);
+    while (w0 + 1 < P && str_unit_begin(w0 + 1, o.units, P) <= first) ++w0;
+    while (w0 > 0 && str_unit_begin(w0, o.units, P) > first) --w0;
+    return w0;
+}
+
+template <bool GATED, bool KTAIL>
+__global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(StreamOp o) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[STR_LDS];
+    stream_units<GATED, KTAIL>(o, lds, blockIdx.x, gridDim.x, false);
+}
+
+// Block (t, y) finishes tile t; each thread 4 consecutive columns of one
+// token row.
+template <int EPI>
+__global__ __launch_bounds__(256) void stream_finalize_kernel(StreamOp o, GemmArgs out, int P) {
+    constexpr int cols = EPI == EPI_GATED_BF16 ? STR_BN / 2 : STR_BN;
+    const int64_t t = blockIdx.x;
+    const int idx = blockIdx.y * blockDim.x + threadIdx.x;
+    const int m = idx / (cols / 4), g4 = (idx % (cols / 4)) * 4;
+    if (m >= o.M) return;
+    stream_finish4<EPI>(o, out, P, t, stream_first_wg(o, P, t), m, g4);
+}
+
 // ---- fp32 VALU GEMM -----------------------------------------------------
 
 struct F32Args {
@@ -1396,17 +1693,25 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs p, int BM, int
 
 // ---- planning -------------------------------------------------------------
 
-enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DECODE = 5 };
+enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DECODE = 5, K_BF16_DEC4 = 6,
+            K_BF16_STREAM = 7 };
 
-// Tile configurations (BM tokens x BN weight rows, BK = 64):
-//   HUGE8 256x256, 2x4 waves of 128x64 (prefill-sized problems)
+// Tile configurations (BM tokens x BN weight rows):
+//   HUGE8 256x256, 2x4 waves of 128x64 (prefill-sized problems; deep-pipelined
+//         16x16x32 kernel when the operands allow direct-to-LDS loads)
 //   LARGE 128x128, 2x2 waves of 64x64
 //   SMALL  64x128, 1x2 waves of 64x64 (decode, M <= 64)
+//   DEC4   64x128, 1x4 waves of 64x32, deep-pipelined 16x16x32 kernel (decode,
+//          M <= 64; same tiling as SMALL, which serves it when the operands
+//          do not allow direct-to-LDS loads)
+//   STREAM 64x128 weight-streaming persistent kernel (decode, M <= 64, large
+//          weights): one workgroup per CU over equal ranges of (tile, K chunk)
 struct TileCfg { int bm, bn, wm, wn; };
 static TileCfg tile_cfg(int k) {
     switch (k) {
         case K_BF16_HUGE8: return TileCfg{256, 256, 2, 4};
         case K_BF16_SMALL: return TileCfg{64, 128, 1, 2};
+        case K_BF16_DEC4: return TileCfg{64, 128, 1, 4};
         default: return TileCfg{128, 128, 2, 2};
     }
 }
@@ -1463,6 +1768,28 @@ static bool pipe_enabled() {
     return on == 1;
 }
 
+// weight-streaming decode kernel switch (TPSHARD_GEMM_STREAM=0 turns it off)
+static bool stream_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TPSHARD_GEMM_STREAM");
+        on = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    return on == 1;
+}
+
+// CUs of an MI355X: the weight-streaming kernel runs one workgroup on each
+constexpr int kStreamWGs = 256;
+
+// fp32 partial-tile workspace of the weight-streaming kernel
+static size_t stream_ws_bytes(int64_t M, int64_t N, int64_t K, bool gated) {
+    const StreamOp o = make_stream_op(nullptr, nullptr, M, N, K, gated, nullptr, kStreamWGs);
+    return (size_t)kStreamWGs * o.maxseg * STR_BM * STR_BN * sizeof(float);
+}
+static int64_t stream_units_of(int64_t N, int64_t K, bool gated) {
+    return make_stream_op(nullptr, nullptr, 1, N, K, gated, nullptr, kStreamWGs).units;
+}
+
 // balanced-last-round switch (TPSHARD_GEMM_TAIL=0 turns it off)
 static bool tail_enabled() {
     static int on = -1;
@@ -1475,14 +1802,14 @@ static bool tail_enabled() {
 
 // Split-K target: about this many workgroups for shapes with fewer output
 // tiles than CUs (TPSHARD_SPLIT_TARGET overrides; tuning knob).
-static int64_t split_target() {
+static int64_t split_target(int64_t dflt) {
     static int64_t t = -1;
     if (t < 0) {
         const char* e = getenv("TPSHARD_SPLIT_TARGET");
-        t = e ? atoll(e) : 1024;
-        if (t < 1) t = 1024;
+        t = e ? atoll(e) : 0;
+        if (t < 1) t = 0;
     }
-    return t;
+    return t > 0 ? t : dflt;
 }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
@@ -1504,19 +1831,28 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
         pl.kernel = K_BF16_DECODE;     // weight streaming, full K per workgroup, no workspace
         return pl;
     }
+    if (M <= 64 && K % 8 == 0 && Nb0 * K * 2 < ((int64_t)1 << 31) && stream_enabled()) {
+        if (stream_units_of(N, K, gated) >= 2 * kStreamWGs) {
+            pl.kernel = K_BF16_STREAM;
+            pl.ws_bytes = stream_ws_bytes(M, N, K, gated);
+            return pl;
+        }
+    }
     if (M > 64) {
         tiles_for(K_BF16_HUGE8, M, N, gated, tm, tn);
         pl.kernel = (int64_t)tm * tn >= 512 ? huge_kernel() : K_BF16_LARGE;
     } else {
-        pl.kernel = K_BF16_SMALL;
+        pl.kernel = pipe_enabled() ? K_BF16_DEC4 : K_BF16_SMALL;
     }
     tiles_for(pl.kernel, M, N, gated, tm, tn);
     const int64_t tiles = (int64_t)tm * tn;
     const int64_t Nb = gated ? 2 * N : N;
-    // fewer tiles than CUs: split K so that the launch fills the machine
+    // fewer tiles than CUs: split K so that the launch fills the machine.
+    // DEC4 (48 KiB of LDS ring, three workgroups per CU) aims at one full
+    // round of 768 workgroups without exceeding it.
     if (tiles < 256 && K >= 1024) {
-        int64_t want = ceil_div(split_target(), tiles);
-        int64_t maxs = K / 512;
+        int64_t want = pl.kernel == K_BF16_DEC4 ? split_target(768) / tiles : ceil_div(split_target(1024), tiles);
+        int64_t maxs = pl.kernel == K_BF16_DEC4 ? K / 256 : K / 512;
         int64_t s = want < maxs ? want : maxs;
         if (s > 1) {
             int64_t ks = ceil_div(ceil_div(K, s), 64) * 64;
@@ -1565,28 +1901,15 @@ static void launch_tail_fixup(const GemmArgs& a, int ntiles, hipStream_t s) {
     }
 }
 
+static bool use_dl_kernels();
+
 template <int BM, int BN, int WM, int WN, int EPI, bool VEC>
 static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream_t s) {
-    static int use_dl = -1;
-    if (use_dl < 0) {
-        const char* e = getenv("TPSHARD_GEMM_DL");
-        use_dl = (e && atoi(e) == 0) ? 0 : 1;
-    }
-    if (VEC && use_dl) {
+    if (VEC && use_dl_kernels()) {
         // direct-to-LDS kernel: its LDS ring is a static allocation
         const int ntiles = a.tiles_m * a.tiles_n;
         const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
         dim3 grid((unsigned)units, (unsigned)splits);
-        if (pipe_enabled() && BM * BN >= 256 * 256) {
-            // deep-pipelined kernel (K steps of 32)
-            const bool kt32 = (a.K % 32) != 0 || (a.k_split % 32) != 0;
-            if (kt32)
-                hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, a);
-            else
-                hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, a);
-            launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
-            return;
-        }
         const bool ktail = (a.K % 64) != 0 || (a.k_split % 64) != 0;
         // LDS ring depth 2: deeper rings measured slower here because they
         // cost a second resident workgroup per CU (occupancy beats depth)
@@ -1612,6 +1935,30 @@ static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream
     hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), lds, s, a);
 }
 
+// deep-pipelined kernel (K steps of 32; direct-to-LDS operands only)
+template <int BM, int BN, int WM, int WN, int EPI>
+static void launch_pipe_one(const GemmArgs& a, int splits, hipStream_t s) {
+    const int ntiles = a.tiles_m * a.tiles_n;
+    const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
+    dim3 grid((unsigned)units, (unsigned)splits);
+    const bool kt32 = (a.K % 32) != 0 || (a.k_split % 32) != 0;
+    if (kt32)
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, a);
+    launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
+}
+
+template <int BM, int BN, int WM, int WN>
+static void launch_pipe_epi(int epi, const GemmArgs& a, int splits, hipStream_t s) {
+    switch (epi) {
+        case EPI_STORE_BF16: launch_pipe_one<BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, s); break;
+        case EPI_STORE_F32: launch_pipe_one<BM, BN, WM, WN, EPI_STORE_F32>(a, splits, s); break;
+        case EPI_GATED_BF16: launch_pipe_one<BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, s); break;
+        default: launch_pipe_one<BM, BN, WM, WN, EPI_SPLIT>(a, splits, s); break;
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI>
 static void launch_bf16_cfg(const GemmArgs& a, int splits, bool vec, size_t lds, hipStream_t s) {
     if (vec)
@@ -1630,10 +1977,28 @@ static void launch_bf16_epi(int epi, const GemmArgs& a, int splits, bool vec, si
     }
 }
 
+static bool use_dl_kernels() {
+    static int use_dl = -1;
+    if (use_dl < 0) {
+        const char* e = getenv("TPSHARD_GEMM_DL");
+        use_dl = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    return use_dl == 1;
+}
+
 static void launch_bf16_kern(int kern, int epi, const GemmArgs& a, int splits, bool vec, hipStream_t s) {
     const size_t lds = lds_bytes(kern);
+    const bool pipe = vec && pipe_enabled() && use_dl_kernels();
     switch (kern) {
-        case K_BF16_HUGE8: launch_bf16_epi<256, 256, 2, 4>(epi, a, splits, vec, lds, s); break;
+        case K_BF16_HUGE8:
+            if (pipe) launch_pipe_epi<256, 256, 2, 4>(epi, a, splits, s);
+            else launch_bf16_epi<256, 256, 2, 4>(epi, a, splits, vec, lds, s);
+            break;
+        case K_BF16_DEC4:
+            // same tiling as SMALL, which serves operands that DMA cannot load
+            if (pipe) launch_pipe_epi<64, 128, 1, 4>(epi, a, splits, s);
+            else launch_bf16_epi<64, 128, 1, 2>(epi, a, splits, vec, lds_bytes(K_BF16_SMALL), s);
+            break;
         case K_BF16_SMALL: launch_bf16_epi<64, 128, 1, 2>(epi, a, splits, vec, lds, s); break;
         default: launch_bf16_epi<128, 128, 2, 2>(epi, a, splits, vec, lds, s); break;
     }
@@ -1670,6 +2035,47 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         return hipGetLastError();
     }
     const bool vec = (K % 8) == 0 && (((uintptr_t)A | (uintptr_t)B) & 15u) == 0;
+    if (pl.kernel == K_BF16_STREAM) {
+        if (!vec || !ws || (((uintptr_t)ws) & 15u) != 0) {
+            // operands DMA cannot load: the element-wise tiled kernel, whole K
+            GemmPlan alt = pl;
+            alt.kernel = K_BF16_SMALL;
+            alt.splits = 1;
+            alt.k_split = K;
+            alt.ws_bytes = 0;
+            return launch_gemm(alt, A, B, bias, C, M, N, K, gated, dt, out_dt, ws, s);
+        }
+        const StreamOp o = make_stream_op(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), M, N, K,
+                                          gated, static_cast<float*>(ws), kStreamWGs);
+        const bool ktail = (K % STR_BK) != 0;
+        if (gated) {
+            if (ktail) hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, true>), dim3(kStreamWGs), dim3(256), 0, s, o);
+            else hipLaunchKernelGGL((gemm_bf16_stream_kernel<true, false>), dim3(kStreamWGs), dim3(256), 0, s, o);
+        } else {
+            if (ktail) hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, true>), dim3(kStreamWGs), dim3(256), 0, s, o);
+            else hipLaunchKernelGGL((gemm_bf16_stream_kernel<false, false>), dim3(kStreamWGs), dim3(256), 0, s, o);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // finalize: block (tile, y), thread = (token row, 4 columns)
+        GemmArgs a{};
+        a.bias = static_cast<const uint16_t*>(bias);
+        a.C = C;
+        a.M = M;
+        a.N = N;
+        a.Nb = Nb;
+        a.vec_out = (N % 4) == 0 && (((uintptr_t)C) & 15u) == 0;
+        const int cols = gated ? STR_BN / 2 : STR_BN;
+        const dim3 fgrid((unsigned)ceil_div(N, cols), (unsigned)ceil_div(M * (cols / 4), 256));
+        const int epi = gated ? EPI_GATED_BF16 : (out_dt == TP_F32 ? EPI_STORE_F32 : EPI_STORE_BF16);
+        if (epi == EPI_GATED_BF16)
+            hipLaunchKernelGGL(stream_finalize_kernel<EPI_GATED_BF16>, fgrid, dim3(256), 0, s, o, a, kStreamWGs);
+        else if (epi == EPI_STORE_F32)
+            hipLaunchKernelGGL(stream_finalize_kernel<EPI_STORE_F32>, fgrid, dim3(256), 0, s, o, a, kStreamWGs);
+        else
+            hipLaunchKernelGGL(stream_finalize_kernel<EPI_STORE_BF16>, fgrid, dim3(256), 0, s, o, a, kStreamWGs);
+        return hipGetLastError();
+    }
     if (pl.kernel == K_BF16_DECODE && !vec) {
         // unaligned operands: the element-wise tiled kernel, without split-K
         GemmPlan alt = pl;

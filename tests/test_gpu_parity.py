@@ -405,3 +405,56 @@ def test_tail_split_not_used_for_short_k_or_one_round():
     assert T.tp_linear_workspace_bytes(512, 1024, 75968, torch.bfloat16) == 0
     # 384 tiles of 128 at two resident workgroups per CU: a single round
     assert T.tp_linear_workspace_bytes(8192, 8192, 768, torch.bfloat16) == 0
+
+
+# --------------------------------------------------------------------------
+# weight-streaming decode kernel (M <= 64 tokens, at least 512 work units of
+# one 128-row tile x 128-wide K chunk): per-tile partials added in K order
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 33, 64])
+@pytest.mark.parametrize("k,m", [(2056, 4000), (4096, 4096)])
+def test_stream_decode_linear_matches_oracle(n, k, m):
+    """k = 2056 ends inside a 128-wide K chunk; m = 4000 leaves a ragged
+    last tile (32 x 17 = 544 and 32 x 32 = 1024 units)."""
+    x = rnd((n, k), 1.0, 190 + n, torch.bfloat16)
+    w = rnd((m, k), 0.05, 191, torch.bfloat16)
+    b = rnd((m,), 0.05, 192, torch.bfloat16)
+    assert T.tp_linear_workspace_bytes(n, k, m, torch.bfloat16) > 0
+    for bias in (None, b):
+        for out_dt in (torch.bfloat16, torch.float32):
+            y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+            ref = oracle.linear(to_f64(x), to_f64(w), to_f64(bias) if bias is not None else None)
+            assert relf(to_f64(y), ref) <= 1e-2, (bias is None, out_dt)
+
+
+@pytest.mark.parametrize("n", [1, 64])
+@pytest.mark.parametrize("h,fl", [(4000, 1100), (4096, 2048)])
+def test_stream_decode_gate_up_matches_oracle(n, h, fl):
+    """Gated tiles of 64 act columns: 18 x 32 = 576 and 32 x 32 = 1024 units;
+    h = 4000 ends inside a K chunk, fl = 1100 leaves a ragged last tile."""
+    x = rnd((n, h), 1.0, 200 + n, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.05, 201, torch.bfloat16)
+    act = T.tp_gate_up_act_rank(x, wgu)
+    xg, W = to_f64(x), to_f64(wgu)
+    ref = oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:]))
+    assert relf(to_f64(act), ref) <= 1e-2
+    assert torch.equal(act, T.tp_gate_up_act_rank(x, wgu))     # fixed order: deterministic
+
+
+
+@pytest.mark.parametrize("n", [1, 64])
+@pytest.mark.parametrize("h,fl", [(4000, 2040), (4096, 2048)])
+@pytest.mark.parametrize("out_dt", [torch.bfloat16, torch.float32])
+def test_streamed_decode_mlp_matches_oracle(n, h, fl, out_dt):
+    """Decode-sized MLP share whose two products both take the weight-
+    streaming kernel (at least 512 units each) through one workspace;
+    h = 4000 and fl = 2040 end inside K chunks and leave ragged last tiles."""
+    x = rnd((n, h), 1.0, 210 + n, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.05, 211, torch.bfloat16)
+    wd = rnd((h, fl), 0.05, 212, torch.bfloat16)
+    p = T.tp_mlp_rank_forward(x, wgu, wd, out_dtype=out_dt)
+    xg, W = to_f64(x), to_f64(wgu)
+    ref = oracle.linear(oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:])), to_f64(wd))
+    assert relf(to_f64(p), ref) <= 1e-2
+    assert torch.equal(p, T.tp_mlp_rank_forward(x, wgu, wd, out_dtype=out_dt))   # deterministic
