@@ -1655,39 +1655,44 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(F32Args p) {
 
 // Finishes the tiles of a balanced last round: adds each tile's K pieces in
 // piece order and applies the epilogue (gated SiLU(g)*u, or store + bias).
+// One thread per 4 consecutive output columns of a tile row (float4 reads).
 template <int EPI>
 __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs p, int BM, int BN) {
     constexpr bool GATED = EPI == EPI_GATED_BF16;
     const int ntail = p.tiles_m * p.tiles_n - p.full_tiles;
     const int cols = GATED ? BN / 2 : BN;
-    const int64_t per_tile = (int64_t)BM * cols;
+    const int q4 = cols / 4;
+    const int64_t per_tile = (int64_t)BM * q4;
     const int64_t total = (int64_t)ntail * per_tile;
+    const int64_t piece = (int64_t)BM * BN;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int t = (int)(idx / per_tile);
         const int64_t rem = idx - (int64_t)t * per_tile;
-        const int lm = (int)(rem / cols), lc = (int)(rem % cols);
+        const int lm = (int)(rem / q4), lc = (int)(rem % q4) * 4;
         int tm, tn;
         tile_of(p.full_tiles + t, p.tiles_m, p.tiles_n, tm, tn);
         const int64_t m = (int64_t)tm * BM + lm;
         const int64_t n = (int64_t)tn * cols + lc;
         if (m >= p.M || n >= p.N) continue;
-        const float* base = p.tail_ws + (int64_t)t * p.tail_split * BM * BN;
-        float v0 = base[(int64_t)lm * BN + lc];
-        float v1 = GATED ? base[(int64_t)lm * BN + BN / 2 + lc] : 0.0f;
+        const float* base = p.tail_ws + (int64_t)t * p.tail_split * piece + (int64_t)lm * BN + lc;
+        float4 g = *reinterpret_cast<const float4*>(base);
+        float4 u = GATED ? *reinterpret_cast<const float4*>(base + BN / 2) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         for (int s = 1; s < p.tail_split; ++s) {
-            v0 = v0 + base[(int64_t)s * BM * BN + (int64_t)lm * BN + lc];
-            if (GATED) v1 = v1 + base[(int64_t)s * BM * BN + (int64_t)lm * BN + BN / 2 + lc];
+            const float4 a = *reinterpret_cast<const float4*>(base + s * piece);
+            g.x = g.x + a.x; g.y = g.y + a.y; g.z = g.z + a.z; g.w = g.w + a.w;
+            if (GATED) {
+                const float4 b = *reinterpret_cast<const float4*>(base + s * piece + BN / 2);
+                u.x = u.x + b.x; u.y = u.y + b.y; u.z = u.z + b.z; u.w = u.w + b.w;
+            }
         }
+        float v[4];
         if (GATED) {
-            static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(silu_mul(v0, v1));
+            v[0] = silu_mul(g.x, u.x); v[1] = silu_mul(g.y, u.y); v[2] = silu_mul(g.z, u.z); v[3] = silu_mul(g.w, u.w);
         } else {
-            if (p.bias) v0 = v0 + bf16_to_f32(p.bias[n]);
-            if (EPI == EPI_STORE_F32)
-                static_cast<float*>(p.C)[m * p.N + n] = v0;
-            else
-                static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(v0);
+            v[0] = g.x; v[1] = g.y; v[2] = g.z; v[3] = g.w;
         }
+        store4<EPI>(p, m, n, v);
     }
 }
 
@@ -1895,7 +1900,7 @@ template <int BM, int BN, int EPI>
 static void launch_tail_fixup(const GemmArgs& a, int ntiles, hipStream_t s) {
     if (a.tail_split > 1 && EPI != EPI_SPLIT) {
         const int cols = EPI == EPI_GATED_BF16 ? BN / 2 : BN;
-        int64_t blocks = ceil_div((int64_t)(ntiles - a.full_tiles) * BM * cols, 256);
+        int64_t blocks = ceil_div((int64_t)(ntiles - a.full_tiles) * BM * (cols / 4), 256);
         if (blocks > 8192) blocks = 8192;
         hipLaunchKernelGGL((tail_fixup_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, a, BM, BN);
     }
