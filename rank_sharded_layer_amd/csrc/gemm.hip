@@ -1224,29 +1224,29 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float* __res
 // Decode multiplies a few token rows by a large weight matrix: HBM-bound on
 // the weights, which must stream in long contiguous runs (a 64-byte piece per
 // row, as a 32-wide K stage reads, runs at about two thirds of the bandwidth
-// that 256-byte and longer runs reach).  Design:
+// that 256-byte and longer runs reach) with many bytes in flight.  Design:
 //   * persistent grid, one workgroup per CU; the work is a list of units
 //     (output tile of 128 weight rows, K chunk of 128), tile-major, cut into
 //     gridDim.x equal contiguous ranges, so every CU streams the same number
 //     of weight bytes and its DMA never stops between tiles;
-//   * a unit stage holds the 64 token rows and the 128 weight rows over its
-//     K chunk: 256 contiguous bytes per row, fetched 4 rows x 256 B per wave
-//     instruction straight into LDS; a ring of 3 stages keeps two units of
-//     weights (64 KiB) in flight per CU;
-//   * 4 waves, each 32 weight rows x 64 tokens, 16x16x32 MFMAs;
+//   * LDS holds weights only: a unit stage is 128 weight rows x 256
+//     contiguous bytes, fetched 4 rows x 256 B per wave instruction straight
+//     into LDS; a ring of 4 stages keeps three units (96 KiB) in flight;
+//   * 4 waves, each 16 tokens x all 128 weight rows (16x16x32 MFMAs); a wave
+//     loads its tokens' fragments from global memory (the token rows are
+//     small and stay in L2) into registers two units ahead;
 //   * when a workgroup leaves a tile it writes its fp32 partial tile; a
 //     finalize pass adds a tile's partials in K order (deterministic) and
 //     applies the epilogue.
 // LDS rows are 256 bytes (16 chunks); chunk c of row r sits at position
 // c ^ (r & 15), so the 16 rows of a fragment read hit 16 distinct bank groups.
-constexpr int STR_BM = 64, STR_BN = 128, STR_BK = 128, STR_NST = 3;
+constexpr int STR_BM = 64, STR_BN = 128, STR_BK = 128, STR_NST = 4;
 constexpr int STR_ROWB = STR_BK * 2;
-constexpr int STR_A_BYTES = STR_BM * STR_ROWB;
-constexpr int STR_STAGE = (STR_BM + STR_BN) * STR_ROWB;         // 48 KiB
-constexpr int STR_LDS = STR_NST * STR_STAGE;                    // 144 KiB
+constexpr int STR_STAGE = STR_BN * STR_ROWB;                    // 32 KiB of weight rows
+constexpr int STR_LDS = STR_NST * STR_STAGE;                    // 128 KiB
 constexpr int STR_NW = 4;
 constexpr int STR_PW = STR_STAGE / 1024 / STR_NW;               // DMA instructions per wave and unit
-constexpr int STR_A_INSTR = STR_A_BYTES / 1024;
+constexpr int STR_TL = STR_BK / 32;                             // token loads per lane and unit (one per sub-step)
 
 __host__ __device__ __forceinline__ int64_t str_unit_begin(int w, int64_t units, int P) {
     return ((int64_t)w * units) / P;
@@ -1283,164 +1283,183 @@ __host__ __device__ __forceinline__ StreamOp make_stream_op(const uint16_t* A, c
     return o;
 }
 
-// Per-lane DMA bookkeeping of a streamed product (fixed for all its units):
-// instruction q of this wave fills tile rows 4 j + (lane >> 4), j = wid PW + q,
-// position lane & 15, i.e. chunk (lane & 15) ^ (row & 15).  boff: byte offset
-// relative to the tile's first row and the unit's K start (both folded into
-// the uniform buffer base); bcol: output column of a weight row within the
-// tile (token rows: 0, or -1 past M); kchunk: the chunk's K offset.
-template <bool GATED>
-struct StreamLanes {
-    uint32_t boff[STR_PW];
-    int bcol[STR_PW];
-    int kchunk[STR_PW];
-    __device__ __forceinline__ void init(const StreamOp& o, int wid, int lane) {
-#pragma unroll
-        for (int q = 0; q < STR_PW; ++q) {
-            const int jj = wid * STR_PW + q;
-            const int r = jj * 4 + (lane >> 4);
-            const int c = (lane & 15) ^ (r & 15);
-            kchunk[q] = c * 8;
-            if (jj < STR_A_INSTR) {
-                boff[q] = (uint32_t)(((int64_t)r * o.K + c * 8) * 2);
-                bcol[q] = r < o.M ? 0 : -1;
-            } else {
-                const int lr = r - STR_BM;
-                int64_t g;
-                if (GATED) {
-                    g = lr < STR_BN / 2 ? lr : o.N + (lr - STR_BN / 2);
-                    bcol[q] = lr < STR_BN / 2 ? lr : lr - STR_BN / 2;
-                } else {
-                    g = lr;
-                    bcol[q] = lr;
-                }
-                boff[q] = (uint32_t)((g * o.K + c * 8) * 2);
-            }
-        }
-    }
-    // DMA of unit u into ring slot st: token rows (PART & 1) and / or weight
-    // rows (PART & 2)
-    template <int PART, bool KTAIL>
-    __device__ __forceinline__ void issue(const StreamOp& o, uint8_t* lds, int64_t u, int st, int wid) const {
-        constexpr int cols = GATED ? STR_BN / 2 : STR_BN;
-        constexpr uint32_t SENT = 0x80000000u;
-        const int64_t t = u / o.kc;
-        const int64_t k0 = (u - t * o.kc) * STR_BK;
-        const int64_t n0 = t * cols;
-        const int ncols = (int)((o.N - n0) < cols ? (o.N - n0) : cols);
-        const int kleft = (int)((o.K - k0) < STR_BK ? (o.K - k0) : STR_BK);
-        __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(o.A + k0), (short)0, 0x7fffffff, 0x00020000);
-        __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(o.B + n0 * o.K + k0), (short)0, 0x7fffffff, 0x00020000);
-#pragma unroll
-        for (int q = 0; q < STR_PW; ++q) {
-            const int jj = wid * STR_PW + q;
-            const bool is_a = jj < STR_A_INSTR;
-            if (is_a && !(PART & 1)) continue;
-            if (!is_a && !(PART & 2)) continue;
-            bool ok = is_a ? bcol[q] >= 0 : bcol[q] < ncols;
-            if (KTAIL) ok = ok && kchunk[q] < kleft;
-            const uint32_t off = ok ? boff[q] : SENT;
-            auto* dst = (__attribute__((address_space(3))) void*)(lds + st * STR_STAGE + jj * 1024);
-            if (is_a)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, off, 0, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, off, 0, 0, 0);
+// (tile, K chunk) of a unit, advanced one unit at a time (no divisions in
+// the loop)
+struct UnitPos {
+    int t, kc;
+    __device__ __forceinline__ void next(int kcs) {
+        if (++kc == kcs) {
+            kc = 0;
+            ++t;
         }
     }
 };
 
-// Runs workgroup w's range of units of o.  With weights_ahead, the weight
-// rows of the range's first two units were already issued (into slots 0 and
-// 1) and only their token rows are fetched here.
+// Runs workgroup w's range of units of o.
 template <bool GATED, bool KTAIL>
-__device__ __forceinline__ void stream_units(const StreamOp& o, uint8_t* lds, int w, int P, bool weights_ahead) {
+__device__ __forceinline__ void stream_units(const StreamOp& o, uint8_t* lds, int w, int P) {
     constexpr int BM = STR_BM, BN = STR_BN, ROWB = STR_ROWB, NST = STR_NST, PW = STR_PW;
-    constexpr int WTN = BN / STR_NW;                     // 32 weight rows per wave
-    constexpr int TM = BM / 16, TN = WTN / 16;
+    constexpr int TB = BN / 16;                              // 16-row weight blocks (8)
+    constexpr int cols = GATED ? BN / 2 : BN;
+    constexpr uint32_t SENT = 0x80000000u;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t u0 = str_unit_begin(w, o.units, P), u1 = str_unit_begin(w + 1, o.units, P);
     const int n = (int)(u1 - u0);
-    StreamLanes<GATED> L;
-    L.init(o, wid, lane);
+    if (n <= 0) return;
 
-    int lo[4];
+    // weight DMA, per lane and instruction: instruction q fills tile rows
+    // 4 j + (lane >> 4), j = wid PW + q, position lane & 15, i.e. chunk
+    // (lane & 15) ^ (row & 15); byte offset relative to the tile's first row
+    // and the unit's K start (both in the uniform buffer base)
+    uint32_t boff[PW];
+    int bcol[PW], kch[PW];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) lo[kk] = (lane & 15) * ROWB + ((((4 * kk + (lane >> 4)) ^ (lane & 15))) * 16);
-    auto wrow = [&](int i) {
-        return GATED ? (i < TN / 2 ? wid * (WTN / 2) + i * 16 : BN / 2 + wid * (WTN / 2) + (i - TN / 2) * 16)
-                     : wid * WTN + i * 16;
+    for (int q = 0; q < PW; ++q) {
+        const int r = (wid * PW + q) * 4 + (lane >> 4);
+        kch[q] = ((lane & 15) ^ (r & 15)) * 8;
+        int64_t g;
+        if (GATED) {
+            g = r < BN / 2 ? r : o.N + (r - BN / 2);
+            bcol[q] = r < BN / 2 ? r : r - BN / 2;
+        } else {
+            g = r;
+            bcol[q] = r;
+        }
+        boff[q] = (uint32_t)((g * o.K + kch[q]) * 2);
+    }
+    auto issue_w = [&](const UnitPos& up, int st) {
+        const int64_t k0 = (int64_t)up.kc * STR_BK;
+        const int64_t n0 = (int64_t)up.t * cols;
+        const int ncols = (int)((o.N - n0) < cols ? (o.N - n0) : cols);
+        const int kleft = (int)((o.K - k0) < STR_BK ? (o.K - k0) : STR_BK);
+        __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(o.B + n0 * o.K + k0), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            bool ok = bcol[q] < ncols;
+            if (KTAIL) ok = ok && kch[q] < kleft;
+            auto* dst = (__attribute__((address_space(3))) void*)(lds + st * STR_STAGE + (wid * PW + q) * 1024);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, ok ? boff[q] : SENT, 0, 0, 0);
+        }
+    };
+    // token fragments: lane l holds token 16 wid + (l & 15), K chunk
+    // 4 kk + (l >> 4) of sub-step kk
+    const int tok = wid * 16 + (lane & 15);
+    uint32_t toff[STR_TL];
+#pragma unroll
+    for (int kk = 0; kk < STR_TL; ++kk)
+        toff[kk] = tok < o.M ? (uint32_t)(((int64_t)tok * o.K + (4 * kk + (lane >> 4)) * 8) * 2) : SENT;
+    bf16x8 tf[3][STR_TL];
+    auto load_t = [&](const UnitPos& up, auto slot_c) {
+        constexpr int SL = decltype(slot_c)::value;
+        const int64_t k0 = (int64_t)up.kc * STR_BK;
+        const int kleft = (int)((o.K - k0) < STR_BK ? (o.K - k0) : STR_BK);
+        __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(o.A + k0), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int kk = 0; kk < STR_TL; ++kk) {
+            uint32_t off = toff[kk];
+            if (KTAIL && (4 * kk + (lane >> 4)) * 8 >= kleft) off = SENT;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0);
+            tf[SL][kk] = __builtin_bit_cast(bf16x8, v);
+        }
     };
 
-    f32x4 acc[TN][TM];
+    int lo[STR_TL];
+#pragma unroll
+    for (int kk = 0; kk < STR_TL; ++kk) lo[kk] = (lane & 15) * ROWB + ((((4 * kk + (lane >> 4)) ^ (lane & 15))) * 16);
+
+    f32x4 acc[TB];
     auto zero_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
-#pragma unroll
-            for (int j = 0; j < TM; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < TB; ++i) acc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     };
     zero_acc();
-    bf16x8 wf[4][TN], xf[4][TM];
-    auto read_frags = [&](int st, int kk) {
-        const uint8_t* b = lds + st * STR_STAGE + lo[kk];
-#pragma unroll
-        for (int i = 0; i < TN; ++i) wf[kk][i] = *reinterpret_cast<const bf16x8*>(b + STR_A_BYTES + wrow(i) * ROWB);
-#pragma unroll
-        for (int j = 0; j < TM; ++j) xf[kk][j] = *reinterpret_cast<const bf16x8*>(b + j * 16 * ROWB);
-    };
-    auto mfma = [&](int kk) {
-#pragma unroll
-        for (int i = 0; i < TN; ++i)
-#pragma unroll
-            for (int j = 0; j < TM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[kk][i], xf[kk][j], acc[i][j], 0, 0, 0);
-    };
 
-    if (n <= 0) return;
-    constexpr int AHEAD = NST - 1;              // units in flight beyond the one multiplied
-    for (int a = 0; a < AHEAD; ++a)
-        if (a < n) {
-            if (weights_ahead) L.template issue<1, KTAIL>(o, lds, u0 + a, a, wid);
-            else L.template issue<3, KTAIL>(o, lds, u0 + a, a, wid);
-        }
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    constexpr int AHEAD = NST - 1;                   // weight units in flight beyond the one multiplied
+    // issue order, as if steps -3..-1 had run: each step issues the tokens
+    // of unit +2, then the weights of unit +3
+    UnitPos pw, pt, pc;                              // next weight issue, next token load, current unit
+    pc.t = (int)(u0 / o.kc);
+    pc.kc = (int)(u0 - (int64_t)pc.t * o.kc);
+    pw = pc;
+    pt = pc;
+    issue_w(pw, 0);
+    pw.next(o.kc);
+    load_t(pt, S0{});
+    pt.next(o.kc);
+    if (n > 1) {
+        issue_w(pw, 1);
+        pw.next(o.kc);
+        load_t(pt, S1{});
+        pt.next(o.kc);
+    }
+    if (n > 2) {
+        issue_w(pw, 2);
+        pw.next(o.kc);
+    }
+
     int seg = 0;
-    bool full_wait = weights_ahead;             // unit 1 may not be the newest DMA: wait for all once
-    for (int i = 0; i < n; ++i) {
-        const int64_t u = u0 + i;
-        const int st = i % NST;
-        // unit i has landed (this wave's DMA), then everyone's (barrier);
-        // the barrier also tells that unit i-1's slot has been read out
-        constexpr int NEWER = (AHEAD - 1) * PW;  // DMA instructions of newer units that may stay in flight
-        if (NEWER > 0 && i + AHEAD - 1 < n && !full_wait)
-            __builtin_amdgcn_s_waitcnt(0x0f70 | (NEWER & 15) | ((NEWER >> 4) << 14));
-        else
-            __builtin_amdgcn_s_waitcnt(0x0f70);
+    bool full_wait = false;
+    // unit i: its weights (DMA, slot i mod 4) and tokens (registers, slot
+    // i mod 3) have landed; it first issues the weights of unit i+3 and the
+    // tokens of unit i+2
+    auto step = [&](int i, auto slot_c, auto next2_c) {
+        // vector-memory operations issued after this unit's tokens (which
+        // follow its weights) may stay in flight: unit i+1's weights (issued
+        // with this unit's tokens), unit i+1's tokens and unit i+2's weights
+        constexpr int N2 = PW + STR_TL + PW, N1 = PW + STR_TL;
+        if (full_wait || i + 1 >= n) __builtin_amdgcn_s_waitcnt(0x0f70);
+        else if (i + 2 < n) __builtin_amdgcn_s_waitcnt(0x0f70 | (N2 & 15) | ((N2 >> 4) << 14));
+        else __builtin_amdgcn_s_waitcnt(0x0f70 | (N1 & 15) | ((N1 >> 4) << 14));
         full_wait = false;
         bare_barrier();
-        if (i + AHEAD < n) L.template issue<3, KTAIL>(o, lds, u + AHEAD, (i + AHEAD) % NST, wid);
-        // all four sub-steps' fragments at once: one LDS latency per unit
+        if (i + 2 < n) {
+            load_t(pt, next2_c);
+            pt.next(o.kc);
+        }
+        if (i + AHEAD < n) {
+            issue_w(pw, (i + AHEAD) % NST);
+            pw.next(o.kc);
+        }
+        constexpr int SL = decltype(slot_c)::value;
+        const uint8_t* b = lds + (i % NST) * STR_STAGE;
+        bf16x8 wf[STR_TL][TB];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) read_frags(st, kk);
+        for (int kk = 0; kk < STR_TL; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) mfma(kk);
-        const int64_t t = u / o.kc;
-        if (i + 1 == n || (u + 1) / o.kc != t) {
+            for (int ib = 0; ib < TB; ++ib) wf[kk][ib] = *reinterpret_cast<const bf16x8*>(b + lo[kk] + ib * 16 * ROWB);
+#pragma unroll
+        for (int kk = 0; kk < STR_TL; ++kk)
+#pragma unroll
+            for (int ib = 0; ib < TB; ++ib)
+                acc[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[kk][ib], tf[SL][kk], acc[ib], 0, 0, 0);
+        const bool last_of_tile = pc.kc + 1 == o.kc;
+        pc.next(o.kc);
+        if (i + 1 == n || last_of_tile) {
             // leaving tile t: fp32 partial tile [BM tokens][BN B rows]
             float* out = o.part + ((int64_t)w * o.maxseg + seg) * BM * BN;
 #pragma unroll
-            for (int i2 = 0; i2 < TN; ++i2)
-#pragma unroll
-                for (int j = 0; j < TM; ++j) {
-                    const int lm = j * 16 + (lane & 15);
-                    const int ln = wrow(i2) + 4 * (lane >> 4);
-                    *reinterpret_cast<float4*>(out + lm * BN + ln) =
-                        make_float4(acc[i2][j][0], acc[i2][j][1], acc[i2][j][2], acc[i2][j][3]);
-                }
+            for (int ib = 0; ib < TB; ++ib) {
+                const int ln = ib * 16 + 4 * (lane >> 4);
+                *reinterpret_cast<float4*>(out + tok * BN + ln) =
+                    make_float4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
+            }
             zero_acc();
             ++seg;
             full_wait = true;                   // stores in flight: the next wait counts them too
         }
+    };
+    int i = 0;
+    for (; i + 3 <= n; i += 3) {
+        step(i, S0{}, S2{});
+        step(i + 1, S1{}, S0{});
+        step(i + 2, S2{}, S1{});
     }
+    if (i < n) step(i, S0{}, S2{});
+    if (i + 1 < n) step(i + 1, S1{}, S0{});
 }
 
 // Adds tile t's partials (from the workgroups whose unit ranges cover it, in
@@ -1491,7 +1510,7 @@ __device__ __forceinline__ int stream_first_wg(const StreamOp& o, int P, int64_t
 template <bool GATED, bool KTAIL>
 __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(StreamOp o) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[STR_LDS];
-    stream_units<GATED, KTAIL>(o, lds, blockIdx.x, gridDim.x, false);
+    stream_units<GATED, KTAIL>(o, lds, blockIdx.x, gridDim.x);
 }
 
 // Block (t, y) finishes tile t; each thread 4 consecutive columns of one

@@ -72,9 +72,11 @@ def test_workspace_queries():
     # 896 gated tiles = 3 rounds + 128: the last 128 tiles are cut into two
     # K pieces each, whose fp32 256 x 256 partial tiles need a workspace
     assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 128 * 2 * 256 * 256 * 4
-    # decode shapes have few output tiles: split-K partial sums need a workspace
+    # decode shapes: the weight-streaming kernel keeps per-tile fp32 partials
     assert T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16) > 0
     assert T.tp_linear_workspace_bytes(64, 7168, 8192, torch.bfloat16) > 0
+    # few output tiles: split-K partial sums
+    assert T.tp_gate_up_workspace_bytes(64, 8192, 64, torch.bfloat16) > 0
     # few output tiles and a long K: split-K partial sums need a workspace
     assert T.tp_gate_up_workspace_bytes(80, 2048, 128, torch.bfloat16) > 0
     assert T.tp_linear_workspace_bytes(64, 7167, 8192, torch.bfloat16) > 0

@@ -458,3 +458,4 @@ def test_streamed_decode_mlp_matches_oracle(n, h, fl, out_dt):
     ref = oracle.linear(oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:])), to_f64(wd))
     assert relf(to_f64(p), ref) <= 1e-2
     assert torch.equal(p, T.tp_mlp_rank_forward(x, wgu, wd, out_dtype=out_dt))   # deterministic
+
