@@ -9,9 +9,11 @@
 //
 // HBM-streaming design: grid.y is the chunk, so the rotation of the partial
 // order is uniform per workgroup and the per-element index math is a single
-// add.  Each lane moves 16-byte vectors (8 bf16 or 4 fp32) and keeps
-// UNROLL x t loads in flight before it adds, so a CU has enough bytes
-// outstanding to cover HBM latency.  The unaligned head and tail of a chunk
+// add.  Each lane moves 16-byte vectors (8 bf16 or 4 fp32).  For t = 2, 4,
+// 8, 16 a kernel with t fixed at compile time issues all t loads of a vector
+// before the first add and gives each lane one vector (a large grid of short
+// workgroups); other t use a generic kernel that keeps UNROLL vectors per
+// partial in flight.  The unaligned head and tail of a chunk
 // (when its bounds are not multiples of the vector width) are done element
 // by element by the chunk's first workgroup.  No atomics: bit-reproducible.
 #include "common.hpp"
@@ -76,6 +78,78 @@ __device__ __forceinline__ int64_t chunk_lo(int64_t K, int t, int c) {
     return (int64_t)(((unsigned __int128)c * (unsigned __int128)K) / (unsigned)t);
 }
 
+// The chunk's unaligned head [lo, min(vlo, hi)) and tail [max(vhi, lo), hi),
+// element by element, in the same rotated order as the vector body.
+template <typename InT, typename OutT>
+__device__ __forceinline__ void reduce_edges(const PartPtrs& parts, int t, int c, int64_t lo,
+                                             int64_t hi, int64_t vlo, int64_t vhi,
+                                             OutT* __restrict__ out) {
+    auto src = [&](int j) -> const InT* {
+        int r = c + j;
+        if (r >= t) r -= t;
+        return static_cast<const InT*>(parts.p[r]);
+    };
+    const int64_t head_end = vlo < hi ? vlo : hi;
+    const int64_t tail_beg = vhi > head_end ? vhi : head_end;
+    for (int64_t i = lo + threadIdx.x; i < head_end; i += blockDim.x) {
+        float acc = Elem<InT>::load(src(0) + i);
+        for (int j = 1; j < t; ++j) acc = acc + Elem<InT>::load(src(j) + i);
+        Elem<OutT>::store(out + i, acc);
+    }
+    for (int64_t i = tail_beg + threadIdx.x; i < hi; i += blockDim.x) {
+        float acc = Elem<InT>::load(src(0) + i);
+        for (int j = 1; j < t; ++j) acc = acc + Elem<InT>::load(src(j) + i);
+        Elem<OutT>::store(out + i, acc);
+    }
+}
+
+// Same arithmetic with t fixed at compile time.  Each lane owns one 16-byte
+// vector per pass and issues all T loads of it before its first add, so
+// T x 16 bytes per lane are in flight (256 B at T = 16).  The adds then run
+// in the ring order with one rounding at the store: bit-identical to the
+// generic kernel.  The launcher gives every lane a single vector, so the grid
+// is large and each workgroup is short; the stride loop only runs when the
+// grid limit caps the workgroups per chunk.
+template <typename InT, typename OutT, int T>
+__global__ __launch_bounds__(256) void ring_reduce_fixed_kernel(PartPtrs parts, int64_t K,
+                                                                OutT* __restrict__ out,
+                                                                int blocks_per_chunk) {
+    using V = Vec<InT>;
+    constexpr int N = V::N;
+    const int c = blockIdx.y;
+    const int64_t lo = chunk_lo(K, T, c);
+    const int64_t hi = chunk_lo(K, T, c + 1);
+    int64_t vlo = (lo + N - 1) / N * N;
+    int64_t vhi = hi / N * N;
+    if (vhi < vlo) vhi = vlo;
+    if (blockIdx.x == 0) reduce_edges<InT, OutT>(parts, T, c, lo, hi, vlo, vhi, out);
+
+    // position j of the ring order reads rank (c + j) mod T; wave-uniform
+    const typename V::raw* s[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+        const int r = c + j < T ? c + j : c + j - T;
+        s[j] = reinterpret_cast<const typename V::raw*>(static_cast<const InT*>(parts.p[r]) + vlo);
+    }
+    OutT* o = out + vlo;
+    const int64_t nvec = (vhi - vlo) / N;
+    const int64_t stride = (int64_t)blocks_per_chunk * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+        typename V::raw raw[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) raw[j] = __builtin_nontemporal_load(s[j] + v);
+        float acc[N], f[N];
+        V::widen(raw[0], acc);
+#pragma unroll
+        for (int j = 1; j < T; ++j) {
+            V::widen(raw[j], f);
+#pragma unroll
+            for (int q = 0; q < N; ++q) acc[q] = acc[q] + f[q];
+        }
+        VecStore<OutT, N>::store(o + v * N, acc);
+    }
+}
+
 template <typename InT, typename OutT, int UNROLL>
 __global__ __launch_bounds__(256) void ring_reduce_kernel(PartPtrs parts, int t, int64_t K,
                                                           OutT* __restrict__ out,
@@ -99,21 +173,7 @@ __global__ __launch_bounds__(256) void ring_reduce_kernel(PartPtrs parts, int t,
         return static_cast<const InT*>(parts.p[r]);
     };
 
-    if (blockIdx.x == 0) {
-        // scalar head [lo, min(vlo, hi)) and tail [max(vhi, lo), hi)
-        int64_t head_end = vlo < hi ? vlo : hi;
-        int64_t tail_beg = vhi > head_end ? vhi : head_end;
-        for (int64_t i = lo + threadIdx.x; i < head_end; i += blockDim.x) {
-            float acc = Elem<InT>::load(src(0) + i);
-            for (int j = 1; j < t; ++j) acc = acc + Elem<InT>::load(src(j) + i);
-            Elem<OutT>::store(out + i, acc);
-        }
-        for (int64_t i = tail_beg + threadIdx.x; i < hi; i += blockDim.x) {
-            float acc = Elem<InT>::load(src(0) + i);
-            for (int j = 1; j < t; ++j) acc = acc + Elem<InT>::load(src(j) + i);
-            Elem<OutT>::store(out + i, acc);
-        }
-    }
+    if (blockIdx.x == 0) reduce_edges<InT, OutT>(parts, t, c, lo, hi, vlo, vhi, out);
 
     const int64_t nvec = (vhi - vlo) / N;
     const int64_t stride = (int64_t)blocks_per_chunk * blockDim.x;
@@ -182,6 +242,15 @@ __global__ __launch_bounds__(256) void ring_reduce_scalar_kernel(PartPtrs parts,
     }
 }
 
+// TPSHARD_REDUCE_FIXED=0 keeps every t on the generic kernel (A/B timing).
+static bool fixed_enabled() {
+    static const bool on = [] {
+        const char* e = getenv("TPSHARD_REDUCE_FIXED");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
 template <typename InT, typename OutT>
 static hipError_t launch_typed(const void* const* p, int t, int64_t K, void* out, hipStream_t s) {
     PartPtrs pp = {};
@@ -191,14 +260,25 @@ static hipError_t launch_typed(const void* const* p, int t, int64_t K, void* out
         g |= (uint64_t)(uintptr_t)p[r];
     }
     const int64_t chunk = ceil_div(K, t);
-    // ~8 vectors of 16 B per lane per workgroup pass; at least one workgroup per chunk,
-    // enough in total to put several workgroups on each of the 256 CUs.
-    const int64_t per_block = 256LL * 8 * (16 / (int64_t)sizeof(InT));
+    const bool fixed = (g & 15u) == 0 && fixed_enabled() && (t == 2 || t == 4 || t == 8 || t == 16);
+    // fixed-t kernel: one 16-byte vector per lane (measured best: many short
+    // workgroups); generic kernel: ~8 vectors per lane per workgroup pass.
+    // At least one workgroup per chunk either way.
+    const int64_t per_block = 256LL * (fixed ? 1 : 8) * (16 / (int64_t)sizeof(InT));
     int64_t bpc = ceil_div(chunk, per_block);
     if (bpc < 1) bpc = 1;
     if (bpc > 65535) bpc = 65535;
     dim3 grid((unsigned)bpc, (unsigned)t);
-    if ((g & 15u) == 0) {
+    if (fixed) {
+        OutT* o = static_cast<OutT*>(out);
+        const int b = (int)bpc;
+        switch (t) {
+        case 2: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 2>), grid, dim3(256), 0, s, pp, K, o, b); break;
+        case 4: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 4>), grid, dim3(256), 0, s, pp, K, o, b); break;
+        case 8: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 8>), grid, dim3(256), 0, s, pp, K, o, b); break;
+        default: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 16>), grid, dim3(256), 0, s, pp, K, o, b); break;
+        }
+    } else if ((g & 15u) == 0) {
         constexpr int UNROLL = sizeof(InT) == 2 ? 2 : 4;
         hipLaunchKernelGGL((ring_reduce_kernel<InT, OutT, UNROLL>), grid, dim3(256), 0, s, pp, t, K,
                            static_cast<OutT*>(out), (int)bpc);

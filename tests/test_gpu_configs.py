@@ -163,6 +163,16 @@ def test_llama70b_prefill_tp8_reduce_windows():
     check_reduce_windows(parts, y, torch.bfloat16)
 
 
+def test_reduce_chunks_beyond_grid_limit():
+    """t=2 with chunks longer than 65535 workgroups x 256 lanes x 8 elements,
+    so the grid-stride pass of the reduce runs near each chunk's end."""
+    t, K = 2, 2 * (65535 * 2048 + 3 * 2048) + 7
+    parts = [synth.normal((K,), 1.0, 4242 + r, torch.bfloat16, device=DEV) for r in range(t)]
+    y = T.tp_partial_reduce(parts)
+    torch.cuda.synchronize()
+    check_reduce_windows(parts, y, torch.bfloat16)
+
+
 def test_llama70b_attnproj_tp16_full():
     w = synth.get("llama70b_attnproj_tp16")
     hd, nq, nkv, t = w.head_dim, w.n_q, w.n_kv, w.tp

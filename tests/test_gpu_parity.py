@@ -95,6 +95,17 @@ def test_partial_reduce_ring_order_bit_exact(in_dt, out_dt, t, K):
     assert np.array_equal(bits(got), oracle_reduce_bits(parts, out_dt))
 
 
+@pytest.mark.parametrize("t", [2, 4, 8, 16])
+def test_partial_reduce_many_workgroups_per_chunk(t):
+    """Chunks spanning many workgroups, with a remainder after the unrolled
+    passes and unaligned chunk bounds (K odd)."""
+    K = 1_000_003
+    parts = [rnd((K,), 1.0, 1300 + 17 * r + t, torch.bfloat16) for r in range(t)]
+    got = T.tp_partial_reduce(parts)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), oracle_reduce_bits(parts, torch.bfloat16))
+
+
 @pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float32])
 def test_partial_reduce_unaligned_buffers(in_dt):
     t, K = 3, 4099
