@@ -28,6 +28,7 @@
 #include <stdlib.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 
@@ -1525,6 +1526,217 @@ __global__ __launch_bounds__(256) void stream_finalize_kernel(StreamOp o, GemmAr
     stream_finish4<EPI>(o, out, P, t, stream_first_wg(o, P, t), m, g4);
 }
 
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// ---- register-streaming decode GEMM (M <= 64) -----------------------------
+//
+// The decode product reads a large weight matrix once for at most 64 token
+// rows, so its time is the weight stream from HBM.  This kernel keeps LDS
+// out of that stream:
+//   * one workgroup of 8 waves per CU (two per SIMD).  Workgroup (q, g) owns
+//     K slice q (8 R elements) and the 16-row weight blocks g, g + G, ...,
+//     so at any time the G workgroups of a slice read G adjacent blocks;
+//     wave w owns the R-element K range w of the slice;
+//   * a wave loads the fragments of all 64 tokens over its K range once and
+//     keeps them in registers (R/2 VGPRs);
+//   * weights go straight from HBM into MFMA A-fragments: for K step i of a
+//     block, lane l reads the 16 bytes of block row l & 15 at K chunk
+//     4 i + (l >> 4), so one instruction reads 16 rows x 64 contiguous bytes
+//     and the R/32 instructions of a block walk along each row (the 8 waves
+//     together read 16 R contiguous bytes of every row);
+//   * two register slots of R/32 fragments: two blocks of loads per wave
+//     are in flight (16 KiB at R = 256);
+//   * after each block the waves' fp32 partials [64 tokens][16 rows] meet in
+//     LDS, are added in wave (= K) order and stored as the workgroup's
+//     partial tile; a finalize pass adds the S slices' tiles in slice order
+//     and applies the epilogue.  No atomics: the result is deterministic.
+constexpr int RS_WAVES = 8;
+
+struct RsOp {
+    const uint16_t* A;      // tokens [M, K]
+    const uint16_t* B;      // weights [Nb, K]
+    float* part;            // [S][rbn][64 tokens][16 rows] fp32 partial tiles
+    int64_t M, K, Nb;
+    int S, G, R, rbn;       // K slices, workgroups per slice, K per wave, 16-row blocks
+};
+
+// S = ceil(K / 2048) slices, R = K per wave rounded up to the 32 of a K step
+// (at most 256: the tokens' fragments take R/2 VGPRs), up to 256 / S
+// workgroups per slice.
+__host__ __device__ inline RsOp make_rs_op(const uint16_t* A, const uint16_t* B, float* part, int64_t M,
+                                           int64_t K, int64_t Nb) {
+    RsOp o;
+    o.A = A;
+    o.B = B;
+    o.part = part;
+    o.M = M;
+    o.K = K;
+    o.Nb = Nb;
+    o.S = (int)((K + 2047) / 2048);
+    const int64_t per_slice = (K + o.S - 1) / o.S;
+    o.R = (int)(((per_slice + RS_WAVES - 1) / RS_WAVES + 31) / 32 * 32);
+    o.rbn = (int)((Nb + 15) / 16);
+    o.G = 256 / o.S < o.rbn ? 256 / o.S : o.rbn;
+    return o;
+}
+
+template <int NKS, bool EDGE>
+__global__ __launch_bounds__(512) void gemm_bf16_rs_kernel(RsOp o) {
+    __shared__ __attribute__((aligned(16))) float red[2][RS_WAVES][1024];
+    constexpr uint32_t SENT = 0x80000000u;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = blockIdx.x / o.G, g = blockIdx.x - q * o.G;
+    const int nb = (o.rbn - g + o.G - 1) / o.G;                  // blocks g + j G, j < nb
+    const int64_t kw = ((int64_t)q * RS_WAVES + wid) * o.R;      // the wave's first K
+    const int r16 = lane & 15, ch = lane >> 4;
+
+    // tokens: fragment (i, tb) of lane l is token 16 tb + (l & 15), K chunk
+    // kw + 32 i + 8 (l >> 4); absent tokens and K past the end read as zero
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)o.A, (short)0, 0x7fffffff, 0x00020000);
+    bf16x8 tk[NKS][4];
+#pragma unroll
+    for (int i = 0; i < NKS; ++i)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int64_t m = tb * 16 + r16, k = kw + i * 32 + ch * 8;
+            const uint32_t off = (m < o.M && k < o.K) ? (uint32_t)((m * o.K + k) * 2) : SENT;
+            tk[i][tb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+        }
+
+    // weights: K steps of this lane that lie inside K (all of them unless EDGE)
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)o.B, (short)0, 0x7fffffff, 0x00020000);
+    uint32_t kok = 0;
+#pragma unroll
+    for (int i = 0; i < NKS; ++i)
+        if (kw + i * 32 + ch * 8 < o.K) kok |= 1u << i;
+    const uint32_t lane_off = (uint32_t)(((int64_t)r16 * o.K + kw + ch * 8) * 2);
+    const uint32_t blk_bytes = (uint32_t)(16 * o.K * 2);
+
+    bf16x8 wt[2][NKS];
+    // block j of the workgroup (weight block g + j G): byte offset for this
+    // lane, or the sentinel past the range
+    auto block_off = [&](int j) -> uint32_t {
+        const int b = g + j * o.G;
+        bool ok = j < nb;
+        if (EDGE) ok = ok && (int64_t)b * 16 + r16 < o.Nb;
+        return ok ? (uint32_t)b * blk_bytes + lane_off : SENT;
+    };
+    // load K step i of the block at `base` into slot SL
+    auto issue = [&](uint32_t base, auto slot_c, auto step_c) {
+        constexpr int SL = decltype(slot_c)::value, I = decltype(step_c)::value;
+        uint32_t off = base + (uint32_t)(I * 64);
+        if (EDGE && (base == SENT || !((kok >> I) & 1u))) off = SENT;
+        wt[SL][I] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsb, off, 0, 0));
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    // prologue: blocks 0 and 1, in step order: the compiler's wait counts
+    // merge this order with the loop's, and a different one would make
+    // every fragment of a slot wait for the slot's last load
+    {
+        const uint32_t p0 = block_off(0), p1 = block_off(1);
+        static_for(std::make_integer_sequence<int, NKS>{}, [&](auto i) {
+            issue(p0, S0{}, i);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        static_for(std::make_integer_sequence<int, NKS>{}, [&](auto i) {
+            issue(p1, S1{}, i);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    float* part = o.part + (int64_t)q * o.rbn * 1024;
+
+    auto block = [&](int j, auto slot_c) {
+        constexpr int SL = decltype(slot_c)::value;
+        const uint32_t nxt = block_off(j + 2);
+        static_for(std::make_integer_sequence<int, NKS>{}, [&](auto step_c) {
+            constexpr int I = decltype(step_c)::value;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wt[SL][I], tk[I][tb], acc[tb], 0, 0, 0);
+            // refill the fragment just multiplied (block j + 2): the loads in
+            // flight stay spread evenly over the block
+            issue(nxt, slot_c, step_c);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // lane l holds rows 4 (l >> 4) + 0..3 of token 16 tb + (l & 15)
+        float* mine = &red[j & 1][wid][0];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            *reinterpret_cast<f32x4*>(mine + (tb * 16 + r16) * 16 + 4 * ch) = acc[tb];
+            acc[tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): the LDS writes are done
+        bare_barrier();
+        const int e = threadIdx.x * 2;
+        float2 v = *reinterpret_cast<const float2*>(&red[j & 1][0][e]);
+#pragma unroll
+        for (int w = 1; w < RS_WAVES; ++w) {
+            const float2 t = *reinterpret_cast<const float2*>(&red[j & 1][w][e]);
+            v.x = v.x + t.x;
+            v.y = v.y + t.y;
+        }
+        *reinterpret_cast<float2*>(part + (int64_t)(g + j * o.G) * 1024 + e) = v;
+        // the next block's accumulators start after this barrier: without the
+        // opaque definition the compiler hoists their MFMAs above it (they
+        // start from zero), which forces a wait for every load in flight
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) asm volatile("" : "+v"(acc[tb]));
+    };
+    int j = 0;
+    for (; j + 1 < nb; j += 2) {
+        block(j, S0{});
+        block(j + 1, S1{});
+    }
+    if (j < nb) block(j, S0{});
+}
+
+// Thread (token m, columns j .. j+3): adds the S slices' partials in slice
+// order and stores through the epilogue of `out`.  A workgroup covers 16
+// columns of all 64 tokens; a wave reads 16 tokens x 64 contiguous bytes.
+template <int EPI>
+__global__ __launch_bounds__(256) void rs_finalize_kernel(RsOp o, GemmArgs out) {
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    const int t = threadIdx.x;
+    const int64_t m = (t & 15) + 16 * (t >> 6);
+    const int64_t j = (int64_t)blockIdx.x * 16 + ((t >> 4) & 3) * 4;
+    if (m >= o.M || j >= out.N) return;
+    auto at = [&](int q, int64_t row) -> int64_t {
+        return (((int64_t)q * o.rbn + (row >> 4)) * 64 + m) * 16 + (row & 15);
+    };
+    float v0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if ((out.N & 3) == 0) {
+        for (int q = 0; q < o.S; ++q) {
+            const float4 a = *reinterpret_cast<const float4*>(o.part + at(q, j));
+            v0[0] = v0[0] + a.x; v0[1] = v0[1] + a.y; v0[2] = v0[2] + a.z; v0[3] = v0[3] + a.w;
+            if (GATED) {
+                const float4 c = *reinterpret_cast<const float4*>(o.part + at(q, out.N + j));
+                v1[0] = v1[0] + c.x; v1[1] = v1[1] + c.y; v1[2] = v1[2] + c.z; v1[3] = v1[3] + c.w;
+            }
+        }
+    } else {
+        for (int q = 0; q < o.S; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e < out.N) {
+                    v0[e] = v0[e] + o.part[at(q, j + e)];
+                    if (GATED) v1[e] = v1[e] + o.part[at(q, out.N + j + e)];
+                }
+    }
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = GATED ? silu_mul(v0[e], v1[e]) : v0[e];
+    store4<EPI>(out, m, j, v);
+}
+
 // ---- fp32 VALU GEMM -----------------------------------------------------
 
 struct F32Args {
@@ -1718,7 +1930,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs p, int BM, int
 // ---- planning -------------------------------------------------------------
 
 enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DECODE = 5, K_BF16_DEC4 = 6,
-            K_BF16_STREAM = 7 };
+            K_BF16_STREAM = 7, K_BF16_RS = 8 };
 
 // Tile configurations (BM tokens x BN weight rows):
 //   HUGE8 256x256, 2x4 waves of 128x64 (prefill-sized problems; deep-pipelined
@@ -1814,6 +2026,21 @@ static int64_t stream_units_of(int64_t N, int64_t K, bool gated) {
     return make_stream_op(nullptr, nullptr, 1, N, K, gated, nullptr, kStreamWGs).units;
 }
 
+// register-streaming decode kernel switch (TPSHARD_GEMM_RS=0 turns it off)
+static bool rs_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TPSHARD_GEMM_RS");
+        on = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    return on == 1;
+}
+
+static size_t rs_ws_bytes(int64_t M, int64_t K, int64_t Nb) {
+    const RsOp o = make_rs_op(nullptr, nullptr, nullptr, M, K, Nb);
+    return (size_t)o.S * (size_t)o.rbn * 1024 * sizeof(float);
+}
+
 // balanced-last-round switch (TPSHARD_GEMM_TAIL=0 turns it off)
 static bool tail_enabled() {
     static int on = -1;
@@ -1854,6 +2081,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
         decode_enabled()) {
         pl.kernel = K_BF16_DECODE;     // weight streaming, full K per workgroup, no workspace
         return pl;
+    }
+    // register-streaming kernel: enough 16-row blocks for two per workgroup
+    if (M <= 64 && K % 8 == 0 && K >= 1024 && Nb0 * K * 2 < ((int64_t)1 << 31) && M * K * 2 < ((int64_t)1 << 31) &&
+        rs_enabled()) {
+        const RsOp o = make_rs_op(nullptr, nullptr, nullptr, M, K, Nb0);
+        if (o.rbn >= 2 * (256 / o.S)) {
+            pl.kernel = K_BF16_RS;
+            pl.ws_bytes = rs_ws_bytes(M, K, Nb0);
+            return pl;
+        }
     }
     if (M <= 64 && K % 8 == 0 && Nb0 * K * 2 < ((int64_t)1 << 31) && stream_enabled()) {
         if (stream_units_of(N, K, gated) >= 2 * kStreamWGs) {
@@ -2059,6 +2296,53 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         return hipGetLastError();
     }
     const bool vec = (K % 8) == 0 && (((uintptr_t)A | (uintptr_t)B) & 15u) == 0;
+    if (pl.kernel == K_BF16_RS) {
+        if (!vec || !ws || (((uintptr_t)ws) & 15u) != 0) {
+            // operands the 16-byte buffer loads cannot serve: the tiled kernel, whole K
+            GemmPlan alt = pl;
+            alt.kernel = K_BF16_SMALL;
+            alt.splits = 1;
+            alt.k_split = K;
+            alt.ws_bytes = 0;
+            return launch_gemm(alt, A, B, bias, C, M, N, K, gated, dt, out_dt, ws, s);
+        }
+        const RsOp o = make_rs_op(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B),
+                                  static_cast<float*>(ws), M, K, Nb);
+        const bool edge = (int64_t)o.S * RS_WAVES * o.R != K || (Nb % 16) != 0;
+        const dim3 grid((unsigned)(o.S * o.G));
+        switch (o.R / 32) {
+#define RS_LAUNCH(NKS)                                                                         \
+    case NKS:                                                                                  \
+        if (edge) hipLaunchKernelGGL((gemm_bf16_rs_kernel<NKS, true>), grid, dim3(512), 0, s, o);  \
+        else hipLaunchKernelGGL((gemm_bf16_rs_kernel<NKS, false>), grid, dim3(512), 0, s, o);      \
+        break;
+            RS_LAUNCH(4)
+            RS_LAUNCH(5)
+            RS_LAUNCH(6)
+            RS_LAUNCH(7)
+            RS_LAUNCH(8)
+#undef RS_LAUNCH
+            default: return hipErrorInvalidValue;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        GemmArgs a{};
+        a.bias = static_cast<const uint16_t*>(bias);
+        a.C = C;
+        a.M = M;
+        a.N = N;
+        a.Nb = Nb;
+        a.vec_out = (N % 4) == 0 && (((uintptr_t)C) & 15u) == 0;
+        const dim3 fgrid((unsigned)ceil_div(N, 16));
+        const int epi = gated ? EPI_GATED_BF16 : (out_dt == TP_F32 ? EPI_STORE_F32 : EPI_STORE_BF16);
+        if (epi == EPI_GATED_BF16)
+            hipLaunchKernelGGL(rs_finalize_kernel<EPI_GATED_BF16>, fgrid, dim3(256), 0, s, o, a);
+        else if (epi == EPI_STORE_F32)
+            hipLaunchKernelGGL(rs_finalize_kernel<EPI_STORE_F32>, fgrid, dim3(256), 0, s, o, a);
+        else
+            hipLaunchKernelGGL(rs_finalize_kernel<EPI_STORE_BF16>, fgrid, dim3(256), 0, s, o, a);
+        return hipGetLastError();
+    }
     if (pl.kernel == K_BF16_STREAM) {
         if (!vec || !ws || (((uintptr_t)ws) & 15u) != 0) {
             // operands DMA cannot load: the element-wise tiled kernel, whole K

@@ -454,6 +454,50 @@ def test_stream_decode_gate_up_matches_oracle(n, h, fl):
 
 
 
+# --------------------------------------------------------------------------
+# register-streaming decode kernel (M <= 64 tokens, K >= 1024, at least two
+# 16-row weight blocks per workgroup): one fp32 partial tile [64][16] per
+# K slice of at most 2048 and 16-row block, added in slice order
+# --------------------------------------------------------------------------
+
+def rs_ws(k, rows):
+    return -(-k // 2048) * -(-rows // 16) * 4096
+
+
+@pytest.mark.parametrize("n", [1, 33, 64])
+@pytest.mark.parametrize("k,m", [(4104, 2744), (2048, 8200), (7168, 8192)])
+def test_rs_decode_linear_matches_oracle(n, k, m):
+    """k = 4104: 3 slices of 8 x 192 with a ragged end; m = 2744 and 8200
+    end inside a 16-row block; (7168, 8192) is the 70B down shard at TP=4
+    (4 slices of 8 x 224)."""
+    assert T.tp_linear_workspace_bytes(n, k, m, torch.bfloat16) == rs_ws(k, m)
+    x = rnd((n, k), 1.0, 230 + n, torch.bfloat16)
+    w = rnd((m, k), 0.05, 231, torch.bfloat16)
+    b = rnd((m,), 0.05, 232, torch.bfloat16)
+    for bias in (None, b):
+        ref = oracle.linear(to_f64(x), to_f64(w), to_f64(bias) if bias is not None else None)
+        for out_dt in (torch.bfloat16, torch.float32):
+            y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+            assert relf(to_f64(y), ref) <= 1e-2, (bias is None, out_dt)
+            assert relf(to_f64(y[:, -20:]), ref[:, -20:]) <= 1e-2
+
+
+@pytest.mark.parametrize("n", [1, 64])
+@pytest.mark.parametrize("h,fl", [(4104, 1372), (4104, 1375), (8192, 4096)])
+def test_rs_decode_gate_up_matches_oracle(n, h, fl):
+    """fl = 1375: act columns not a multiple of 4 (element-wise finish) and
+    up rows that start inside a 16-row block."""
+    assert T.tp_gate_up_workspace_bytes(n, h, fl, torch.bfloat16) == rs_ws(h, 2 * fl)
+    x = rnd((n, h), 1.0, 240 + n, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.05, 241, torch.bfloat16)
+    act = T.tp_gate_up_act_rank(x, wgu)
+    xg, W = to_f64(x), to_f64(wgu)
+    ref = oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:]))
+    assert relf(to_f64(act), ref) <= 1e-2
+    assert relf(to_f64(act[:, -20:]), ref[:, -20:]) <= 1e-2
+    assert torch.equal(act, T.tp_gate_up_act_rank(x, wgu))     # fixed order: deterministic
+
+
 @pytest.mark.parametrize("n", [1, 64])
 @pytest.mark.parametrize("h,fl", [(4000, 2040), (4096, 2048)])
 @pytest.mark.parametrize("out_dt", [torch.bfloat16, torch.float32])
