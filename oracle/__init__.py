@@ -71,6 +71,9 @@ def _load():
                                           _i64, _f32p]),
         "orc_reduce_sum_f64": (None, [ctypes.POINTER(_f64p), _int, _i64, _f64p]),
         "orc_ring_traffic": (_int, [_int, _i64, _i64p, _i64p, ctypes.POINTER(ctypes.c_int)]),
+        "orc_sp_rows": (None, [_i64, _int, _int, _i64p, _i64p]),
+        "orc_rs_add_rmsnorm": (_int, [ctypes.POINTER(_f32p), _int, _int, _i64, _i64, _f32p, _f64p,
+                                      ctypes.c_double, _int, _f32p, _f64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -316,3 +319,30 @@ def reduce_sum_f64(parts) -> np.ndarray:
     out = np.empty(K, dtype=np.float64)
     _load().orc_reduce_sum_f64(arr, t, K, _p(out, _f64p))
     return out
+
+
+# --- sequence-parallel epilogue (reduce-scatter + residual add + RMSNorm) -------
+
+def sp_rows(n, t, c):
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    _load().orc_sp_rows(n, t, c, ctypes.byref(lo), ctypes.byref(hi))
+    return lo.value, hi.value
+
+
+def rs_add_rmsnorm(parts, rank, residual, weight, eps, round_bf16):
+    """Rank `rank`'s rows after the ring reduce-scatter of the t fp32 partials
+    [n, h], plus the residual, then RMSNorm.  residual: the owned chunk's rows
+    (fp32 values); returns (residual_out fp32 values, out fp64)."""
+    parts = [np.ascontiguousarray(p, dtype=np.float32) for p in parts]
+    t = len(parts)
+    n, h = parts[0].shape
+    lo, hi = sp_rows(n, t, (rank + 1) % t)
+    res = np.ascontiguousarray(residual, dtype=np.float32).reshape(hi - lo, h)
+    w = _f64(weight).reshape(h)
+    arr = (_f32p * t)(*[_p(p, _f32p) for p in parts])
+    res_out = np.empty((hi - lo, h), dtype=np.float32)
+    out = np.empty((hi - lo, h), dtype=np.float64)
+    _check(_load().orc_rs_add_rmsnorm(arr, t, rank, n, h, _p(res, _f32p), _p(w, _f64p), float(eps),
+                                      1 if round_bf16 else 0, _p(res_out, _f32p), _p(out, _f64p)),
+           "rs_add_rmsnorm")
+    return res_out, out

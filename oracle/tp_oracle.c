@@ -495,6 +495,79 @@ ORC_API void orc_reduce_sum_f64(const double* const* parts, int t, int64_t K, do
     }
 }
 
+/* Token-row chunk c of the sequence-parallel split: rows [floor(c n/t),
+ * floor((c+1) n/t)).  [SCRATCH] Exercises, item 1 (sequence parallelism):
+ * after the reduce-scatter every rank holds the complete result for 1/t of
+ * the tokens.  The split is along tokens (whole rows); the floor rule for n
+ * not divisible by t is the same reading as orc_chunk_bounds. */
+ORC_API void orc_sp_rows(int64_t n, int t, int c, int64_t* lo, int64_t* hi) {
+    *lo = (int64_t)(((__int128)c * n) / t);
+    *hi = (int64_t)(((__int128)(c + 1) * n) / t);
+}
+
+/* Sequence-parallel epilogue of a row-parallel layer for rank `rank`
+ * ([SCRATCH] Exercises, item 1: split the all-reduce into a reduce-scatter
+ * and an all-gather; each rank does the residual add and RMSNorm only on
+ * the tokens it holds).  Steps, in that order:
+ *   1. the reduce-scatter half of the ring of [VLLM13] §1.1.1 (the same
+ *      rounds as orc_ring_schedule's phase 0), simulated in fp32 on t
+ *      separate rank buffers, with the chunks being token-row ranges
+ *      (orc_sp_rows).  Afterwards rank r holds the complete chunk
+ *      c = (r + 1) mod t; only that chunk's rows are simulated (rows evolve
+ *      independently, so this is exact);
+ *   2. the residual add, one fp32 add per element: v = s + residual, then
+ *      one rounding to bf16 (RNE) if round_bf16 -- the new residual stream,
+ *      written to residual_out (fp32 values);
+ *   3. RMSNorm of each row of the rounded values, in fp64:
+ *      y_j = v_j / sqrt(mean_k v_k^2 + eps) * w_j.  The pages use RMSNorm
+ *      (fused with the all-reduce in serving engines, [SCRATCH] conclusions
+ *      list) but do not write it out; this is its usual definition, with eps
+ *      an argument.
+ * parts[r]: rank r's partial, n*h fp32 values; residual and residual_out:
+ * the chunk's rows, (hi-lo)*h; weight: h; out: (hi-lo)*h fp64.
+ * Returns 0, or 1 for bad arguments, 4 if out of memory. */
+ORC_API int orc_rs_add_rmsnorm(const float* const* parts, int t, int rank, int64_t n, int64_t h,
+                               const float* residual, const double* weight, double eps,
+                               int round_bf16, float* residual_out, double* out) {
+    if (t < 1 || rank < 0 || rank >= t || n < 0 || h < 1) return 1;
+    const int c = (rank + 1) % t;
+    int64_t lo, hi;
+    orc_sp_rows(n, t, c, &lo, &hi);
+    const int64_t w = (hi - lo) * h;            /* elements of the owned chunk */
+    float* buf = (float*)malloc(sizeof(float) * (size_t)(w > 0 ? w : 1) * (size_t)t);
+    float* snd = (float*)malloc(sizeof(float) * (size_t)(w > 0 ? w : 1) * (size_t)t);
+    if (!buf || !snd) { free(buf); free(snd); return 4; }
+    for (int r = 0; r < t; ++r) memcpy(buf + (int64_t)r * w, parts[r] + lo * h, sizeof(float) * (size_t)w);
+    /* reduce-scatter rounds s = 0..t-2: rank q sends chunk (q - s) mod t to
+     * q + 1, which adds it to its own copy; only transfers of chunk c touch
+     * the simulated rows */
+    for (int s = 0; s < t - 1; ++s) {
+        for (int q = 0; q < t; ++q)
+            if (((q - s) % t + t) % t == c) memcpy(snd + (int64_t)q * w, buf + (int64_t)q * w, sizeof(float) * (size_t)w);
+        for (int q = 0; q < t; ++q) {
+            if (((q - s) % t + t) % t != c) continue;
+            const int d = (q + 1) % t;
+            for (int64_t i = 0; i < w; ++i) buf[(int64_t)d * w + i] = buf[(int64_t)d * w + i] + snd[(int64_t)q * w + i];
+        }
+    }
+    const float* red = buf + (int64_t)rank * w;   /* what rank `rank` holds now */
+    for (int64_t i = 0; i < w; ++i) {
+        float v = red[i] + residual[i];
+        if (round_bf16) v = orc_bf16_to_f32(orc_f32_to_bf16(v));
+        residual_out[i] = v;
+    }
+    for (int64_t r = 0; r < hi - lo; ++r) {
+        const float* v = residual_out + r * h;
+        double ss = 0.0;
+        for (int64_t j = 0; j < h; ++j) ss += (double)v[j] * (double)v[j];
+        const double rms = sqrt(ss / (double)h + eps);
+        for (int64_t j = 0; j < h; ++j) out[r * h + j] = (double)v[j] / rms * weight[j];
+    }
+    free(buf);
+    free(snd);
+    return 0;
+}
+
 /* Per-rank traffic of the ring all-reduce: every rank sends (and receives)
  * one chunk per round for t-1 reduce-scatter and t-1 all-gather rounds, so
  * 2(t-1) rounds and, for t dividing K, 2(t-1)*K/t elements.  [VLLM13] §1.2.

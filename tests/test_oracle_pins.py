@@ -528,3 +528,121 @@ def test_ring_simulation_within_sequential_sum_bound(t):
     # a window simulation equals the same elements of the full simulation
     w = oracle.ring_allreduce_f32(parts, 1000, 3000)
     assert np.array_equal(w, out[1000:3000].astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# sequence-parallel epilogue: reduce-scatter + residual add + RMSNorm
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [8, 13])
+def test_sp_rank_owns_the_chunk_the_ring_completes_there(t, n):
+    """Rank r ends the reduce-scatter holding the chunk that the ring
+    schedule's last reduce-scatter round delivers to it, as whole token rows."""
+    sched = oracle.ring_schedule(t, n)
+    last = [s for s in sched if s["phase"] == 0 and s["step"] == t - 2]
+    owner = {s["dst"]: s["chunk"] for s in last}
+    # partial 0 carries each row's index, the others are zero
+    parts = [np.zeros((n, 3), np.float32) for _ in range(t)]
+    parts[0][:] = np.arange(n, dtype=np.float32)[:, None]
+    for r in range(t):
+        lo, hi = oracle.sp_rows(n, t, owner[r])
+        res = np.zeros((hi - lo, 3), np.float32)
+        got, _ = oracle.rs_add_rmsnorm(parts, r, res, np.ones(3), 1e-5, False)
+        assert got[:, 0].tolist() == list(range(lo, hi)), (t, n, r)
+        # whole rows: the chunks tile [0, n) in order
+    cuts = [oracle.sp_rows(n, t, c) for c in range(t)]
+    assert cuts[0][0] == 0 and cuts[-1][1] == n
+    assert all(cuts[c][1] == cuts[c + 1][0] for c in range(t - 1))
+
+
+def test_sp_sum_follows_ring_order():
+    """Row c is summed ((P_c + P_{c+1}) + P_{c+2}).  With two 2^-24 terms
+    first, 2^-24 + 2^-24 + 1 = 1 + 2^-23 exactly; any order that adds the 1
+    earlier rounds 1 + 2^-24 back to 1 (tie to even)."""
+    e = np.float32(2.0 ** -24)
+    n, t = 3, 3
+    parts = [np.zeros((n, 1), np.float32) for _ in range(t)]
+    for c in range(n):
+        parts[c][c, 0] = e
+        parts[(c + 1) % t][c, 0] = e
+        parts[(c + 2) % t][c, 0] = 1.0
+    for r in range(t):
+        got, _ = oracle.rs_add_rmsnorm(parts, r, np.zeros((1, 1), np.float32), np.ones(1), 0.0, False)
+        assert got[0, 0] == np.float32(1.0 + 2.0 ** -23), r
+
+
+def test_sp_residual_add_rounds_once():
+    """fp32 sum then one bf16 rounding: 1 + 2^-8 + 2^-16 rounds up to
+    1 + 2^-7.  Rounding the reduced sum first (1 + 2^-8 is a tie and goes to
+    1) and then adding 2^-16 would give 1."""
+    n, t = 2, 2
+    parts = [np.zeros((n, 1), np.float32) for _ in range(t)]
+    for c in range(n):
+        parts[c][c, 0] = 1.0
+        parts[(c + 1) % t][c, 0] = 2.0 ** -8
+    for r in range(t):
+        res = np.full((1, 1), 2.0 ** -16, np.float32)
+        got, _ = oracle.rs_add_rmsnorm(parts, r, res, np.ones(1), 1e-5, True)
+        assert got[0, 0] == np.float32(1.0 + 2.0 ** -7), r
+
+
+def test_rmsnorm_closed_forms():
+    t, n = 1, 3
+    rows = np.array([[3.0, 4.0], [-2.5, -2.5], [0.0, 0.0]], np.float32)
+    w = np.array([1.0, 0.5])
+    _, out = oracle.rs_add_rmsnorm([rows], 0, np.zeros_like(rows), w, 0.0, False)
+    # mean square of (3, 4) is 12.5: y = (3, 4) / (5 / sqrt 2) * w
+    assert np.allclose(out[0], [3 * math.sqrt(2) / 5, 0.5 * 4 * math.sqrt(2) / 5], rtol=1e-15, atol=0)
+    # a constant row normalises to sign * w
+    assert out[1].tolist() == [-1.0, -0.5]
+    # a zero row stays zero (eps keeps it finite): eps = 0 would divide by 0
+    _, out2 = oracle.rs_add_rmsnorm([rows], 0, np.zeros_like(rows), w, 1e-5, False)
+    assert out2[2].tolist() == [0.0, 0.0]
+
+
+def test_rmsnorm_invariances():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1, 64)).astype(np.float32)
+    w = rng.standard_normal(64)
+    z = np.zeros_like(x)
+    _, y1 = oracle.rs_add_rmsnorm([x], 0, z, w, 0.0, False)
+    _, y8 = oracle.rs_add_rmsnorm([x * np.float32(8.0)], 0, z, w, 0.0, False)
+    assert np.allclose(y1, y8, rtol=1e-14, atol=0)            # scale invariant
+    _, yu = oracle.rs_add_rmsnorm([x], 0, z, np.ones(64), 0.0, False)
+    assert abs(float(np.mean(yu ** 2)) - 1.0) < 1e-13           # unit mean square
+    assert np.allclose(yu * w, y1, rtol=1e-14, atol=0)          # gain is elementwise
+    # eps acts inside the root: y = x / sqrt(ms + eps)
+    eps = 0.25
+    _, ye = oracle.rs_add_rmsnorm([x], 0, z, np.ones(64), eps, False)
+    ms = float(np.mean(x.astype(np.float64) ** 2))
+    assert np.allclose(ye, x.astype(np.float64) / math.sqrt(ms + eps), rtol=1e-14, atol=0)
+
+
+def test_sp_single_rank_is_the_plain_add_norm():
+    rng = np.random.default_rng(9)
+    P = torch.randn(5, 16).to(torch.bfloat16).float().numpy()
+    R = torch.randn(5, 16).to(torch.bfloat16).float().numpy()
+    got, _ = oracle.rs_add_rmsnorm([P], 0, R, np.ones(16), 1e-5, True)
+    # one fp32 add then torch's own RNE conversion to bf16
+    ref = (torch.from_numpy(P) + torch.from_numpy(R)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_rmsnorm_reads_the_stored_residual():
+    """The norm is taken of the new residual stream as stored (bf16-rounded),
+    not of the unrounded fp32 sum: rows whose rounding moves the mean square
+    tell the two apart."""
+    n, t = 2, 2
+    parts = [np.zeros((n, 2), np.float32) for _ in range(t)]
+    for c in range(n):
+        parts[c][c] = [1.0, 1.0]
+        parts[(c + 1) % t][c] = [2.0 ** -8, 0.0]
+    res = np.full((1, 2), 2.0 ** -16, np.float32)
+    for r in range(t):
+        stored, out = oracle.rs_add_rmsnorm(parts, r, res, np.ones(2), 0.0, True)
+        assert stored[0].tolist() == [1.0 + 2.0 ** -7, 1.0]
+        v = np.array([1.0 + 2.0 ** -7, 1.0])
+        assert np.allclose(out[0], v / math.sqrt(np.mean(v * v)), rtol=1e-15, atol=0)
+        u = np.array([1.0 + 2.0 ** -8 + 2.0 ** -16, 1.0 + 2.0 ** -16])
+        assert not np.allclose(out[0], u / math.sqrt(np.mean(u * u)), rtol=1e-6, atol=0)
