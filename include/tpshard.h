@@ -182,6 +182,37 @@ TP_API tp_status tp_partial_reduce(const void* const* partials /*HOST array*/, i
 TP_API tp_status tp_ring_schedule(int t, int64_t K, tp_ring_step* steps /*HOST*/, int max_steps,
                            int* n_steps /*HOST*/);
 
+/* ---- sequence-parallel epilogue (reduce-scatter + residual add + RMSNorm) */
+
+/* HOST-only.  Token rows [lo, hi) that rank tp_rank holds after the ring
+ * reduce-scatter: chunk c = (tp_rank + 1) mod t, lo = floor(c n / t),
+ * hi = floor((c + 1) n / t).  [SCRATCH] Exercises, item 1 (sequence
+ * parallelism: the reduce-scatter leaves each rank the complete rows of 1/t
+ * of the tokens); the ring and its final owner as in tp_ring_schedule. */
+TP_API tp_status tp_sp_rows(int64_t n, int tp_rank, int tp_size, int64_t* lo /*HOST*/, int64_t* hi /*HOST*/);
+
+/* Rank tp_rank's share of the row-parallel layer's epilogue in sequence-
+ * parallel form ([SCRATCH] Exercises, item 1: reduce-scatter, then the
+ * residual add and RMSNorm on the rank's own tokens only; all-gather comes
+ * after).  For each row i in [lo, hi) of tp_sp_rows:
+ *   s   = ((P_c[i] + P_{c+1}[i]) + ...) + P_{c+t-1}[i]      fp32, ring order
+ *   v   = round(s + residual[i - lo])                       one fp32 add, one
+ *                                                           rounding to dt
+ *   out = round(v / sqrt(mean_j v_j^2 + eps) * weight)      fp32
+ * The pages name RMSNorm without writing it out; this is its usual form, and
+ * eps is the caller's (1e-5 in the Llama configurations).
+ *   partials: HOST array of t device pointers, each [n, h] dt (the ranks'
+ *             row-parallel partials); residual, residual_out, out:
+ *             [hi - lo, h] dt (the rank's rows only); weight: [h] dt.
+ *   residual_out may be residual (in-place update); out must not alias
+ *   the partials or residual.  dt: TP_BF16 or TP_F32.  1 <= t <= TP_MAX_RANKS,
+ *   0 <= tp_rank < t, n >= 0, h >= 1, eps >= 0.  A rank with no rows
+ *   (n < t) launches nothing, and its row buffers may then be null.
+ *   Deterministic (fixed reduction order). */
+TP_API tp_status tp_rs_add_rmsnorm(const void* const* partials /*HOST array*/, int t, int tp_rank, int64_t n,
+                                   int64_t h, tp_dtype dt, const void* residual, const void* weight, float eps,
+                                   void* residual_out, void* out, void* stream);
+
 /* ---- vocab-parallel embedding and LM head -------------------------------- */
 
 /* HOST-only.  Rank r's vocab range: per = ceil(V/t), start = r per,

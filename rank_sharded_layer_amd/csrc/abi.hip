@@ -284,6 +284,44 @@ tp_status tp_partial_reduce(const void* const* partials, int t, int64_t K, tp_dt
                       "tp_partial_reduce");
 }
 
+tp_status tp_sp_rows(int64_t n, int tp_rank, int tp_size, int64_t* lo, int64_t* hi) {
+    if (!lo || !hi) return fail(TP_EINVAL, "tp_sp_rows: null pointer");
+    if (tp_size < 1 || tp_size > TP_MAX_RANKS || tp_rank < 0 || tp_rank >= tp_size)
+        return fail(TP_EINVAL, "tp_sp_rows: rank %d of %d", tp_rank, tp_size);
+    if (n < 0 || n > kMaxElems) return fail(TP_EINVAL, "tp_sp_rows: n out of range");
+    const int c = (tp_rank + 1) % tp_size;
+    *lo = (int64_t)(((__int128)c * n) / tp_size);
+    *hi = (int64_t)(((__int128)(c + 1) * n) / tp_size);
+    return ok();
+}
+
+tp_status tp_rs_add_rmsnorm(const void* const* partials, int t, int tp_rank, int64_t n, int64_t h, tp_dtype dt,
+                            const void* residual, const void* weight, float eps, void* residual_out, void* out,
+                            void* stream) {
+    if (!partials || !weight) return fail(TP_EINVAL, "tp_rs_add_rmsnorm: null pointer");
+    if (t < 1 || t > TP_MAX_RANKS) return fail(TP_EINVAL, "tp_rs_add_rmsnorm: t %d outside [1, %d]", t, TP_MAX_RANKS);
+    if (tp_rank < 0 || tp_rank >= t) return fail(TP_EINVAL, "tp_rs_add_rmsnorm: rank %d of %d", tp_rank, t);
+    if (n < 0 || n > kMaxElems) return fail(TP_EINVAL, "tp_rs_add_rmsnorm: n out of range");
+    const int c = (tp_rank + 1) % t;
+    const bool rows = ((__int128)(c + 1) * n) / t > ((__int128)c * n) / t;
+    // the row buffers may be null when the rank holds no rows
+    if (rows && (!residual || !residual_out || !out)) return fail(TP_EINVAL, "tp_rs_add_rmsnorm: null pointer");
+    for (int r = 0; r < t; ++r) {
+        if (!partials[r]) return fail(TP_EINVAL, "tp_rs_add_rmsnorm: partials[%d] is null", r);
+        if (rows && (partials[r] == out || partials[r] == residual_out))
+            return fail(TP_EINVAL, "tp_rs_add_rmsnorm: an output aliases partials[%d]", r);
+    }
+    if (n < 0 || h < 1 || n > INT32_MAX || h > INT32_MAX || n * h > kMaxElems)
+        return fail(TP_EINVAL, "tp_rs_add_rmsnorm: bad shape n %lld h %lld", (long long)n, (long long)h);
+    if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_rs_add_rmsnorm: bad dtype %d", (int)dt);
+    if (!(eps >= 0.0f) || eps == INFINITY) return fail(TP_EINVAL, "tp_rs_add_rmsnorm: eps must be finite and >= 0");
+    if (rows && (out == residual || out == residual_out))
+        return fail(TP_EINVAL, "tp_rs_add_rmsnorm: out aliases the residual");
+    return hip_status(tpk::launch_rs_add_rmsnorm(partials, t, tp_rank, n, h, dt, residual, weight, eps, residual_out, out,
+                                                 as_stream(stream)),
+                      "tp_rs_add_rmsnorm");
+}
+
 tp_status tp_ring_schedule(int t, int64_t K, tp_ring_step* steps, int max_steps, int* n_steps) {
     if (!steps || !n_steps) return fail(TP_EINVAL, "tp_ring_schedule: null pointer");
     if (t < 1 || t > TP_MAX_RANKS) return fail(TP_EINVAL, "tp_ring_schedule: t %d outside [1, %d]", t, TP_MAX_RANKS);

@@ -56,6 +56,9 @@ _SIGS = {
     "tp_mlp_rank_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _sz, _vp]),
     "tp_partial_reduce": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _vp, _int, _int, _vp]),
     "tp_ring_schedule": (_int, [_int, _i64, ctypes.POINTER(RingStep), _int, ctypes.POINTER(_int)]),
+    "tp_sp_rows": (_int, [_i64, _int, _int, _i64p, _i64p]),
+    "tp_rs_add_rmsnorm": (_int, [ctypes.POINTER(_vp), _int, _int, _i64, _i64, _int, _vp, _vp, ctypes.c_float,
+                                 _vp, _vp, _vp]),
     "tp_vocab_range": (_int, [_i64, _int, _int, _i64p, _i64p]),
     "tp_vocab_embed_rank": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
     "tp_lm_head_rank": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _int, _vp, _sz, _vp]),
@@ -284,6 +287,40 @@ def tp_ring_schedule(t, K):
     _check(lib().tp_ring_schedule(t, K, arr, n, ctypes.byref(got)))
     return [dict(phase=s.phase, step=s.step, src=s.src, dst=s.dst, chunk=s.chunk, offset=s.offset,
                  len=s.len) for s in arr[:got.value]]
+
+
+# ---- sequence-parallel epilogue -------------------------------------------------
+
+def tp_sp_rows(n, tp_rank, tp_size):
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().tp_sp_rows(n, tp_rank, tp_size, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def tp_rs_add_rmsnorm(partials, tp_rank, residual, weight, eps, residual_out=None, out=None, stream=None):
+    """Rank tp_rank's rows after the ring reduce-scatter of `partials` ([n, h]
+    each), plus `residual` (the rank's rows), RMSNorm with `weight`.  Returns
+    (residual_out, out); residual_out may be `residual` (in place)."""
+    t = len(partials)
+    if t < 1:
+        raise TPError(1, "no partials")
+    p0 = partials[0]
+    n, h = p0.shape
+    lo, hi = tp_sp_rows(n, tp_rank, t)
+    ptrs = (ctypes.c_void_p * t)(*[_dev(p, f"partials[{i}]", p0.dtype, p0.shape).value
+                                   for i, p in enumerate(partials)])
+    rows = (hi - lo, h)
+    pr = _dev(residual, "residual", p0.dtype, rows)
+    pw = _dev(weight, "weight", p0.dtype, (h,))
+    if residual_out is None:
+        residual_out = torch.empty(rows, dtype=p0.dtype, device=p0.device)
+    if out is None:
+        out = torch.empty(rows, dtype=p0.dtype, device=p0.device)
+    pro = _dev(residual_out, "residual_out", p0.dtype, rows)
+    po = _dev(out, "out", p0.dtype, rows)
+    _check(lib().tp_rs_add_rmsnorm(ptrs, t, tp_rank, n, h, _dt(p0.dtype), pr, pw, float(eps), pro, po,
+                                   _stream(stream)))
+    return residual_out, out
 
 
 # ---- vocab parallel -----------------------------------------------------------

@@ -186,3 +186,44 @@ def test_binding_rejects_host_tensors():
         T.tp_partial_reduce([torch.zeros(8), torch.zeros(8)])
     with pytest.raises(ValueError):
         T.tp_shard_weights(torch.zeros(4, 4), 0, 0, 2)
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("n", [0, 5, 13, 8192])
+def test_sp_rows_match_oracle_ring_owner(t, n):
+    """The rows a rank holds after the reduce-scatter: the chunk the oracle's
+    ring schedule completes on that rank, cut as whole token rows."""
+    sched = oracle.ring_schedule(t, n)
+    owner = {s["dst"]: s["chunk"] for s in sched if s["phase"] == 0 and s["step"] == t - 2}
+    for r in range(t):
+        c = owner.get(r, 0)            # t = 1: the single rank holds chunk 0
+        assert T.tp_sp_rows(n, r, t) == oracle.sp_rows(n, t, c)
+
+
+@no_gpu
+def test_rs_add_rmsnorm_errors():
+    L = T.lib()
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    ok_args = dict(t=2, rank=0, n=8, h=16, dt=1, res=DUMMY, w=DUMMY, eps=1e-5, ro=ctypes.c_void_p(0x3000),
+                   out=ctypes.c_void_p(0x4000))
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return _status(L.tp_rs_add_rmsnorm, kw.get("arr", arr), a["t"], a["rank"], a["n"], a["h"], a["dt"], a["res"],
+                       a["w"], a["eps"], a["ro"], a["out"], NULL)
+
+    assert call(t=0)[0] == 1
+    assert call(rank=2)[0] == 1                      # rank outside [0, t)
+    assert call(h=0)[0] == 1
+    assert call(dt=7)[0] == 3
+    assert call(eps=-1.0)[0] == 1
+    assert call(eps=float("nan"))[0] == 1
+    assert call(w=NULL)[0] == 1
+    st, msg = call(out=ctypes.c_void_p(0x3000))
+    assert st == 1 and "alias" in msg                # out is residual_out
+    st, msg = call(ro=ctypes.c_void_p(0x2000))
+    assert st == 1 and "partials[1]" in msg          # residual_out is a partial
+    st, msg = call(arr=(ctypes.c_void_p * 2)(0x1000, None))
+    assert st == 1 and "partials[1]" in msg
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    assert L.tp_sp_rows(8, 3, 2, ctypes.byref(lo), ctypes.byref(hi)) == 1

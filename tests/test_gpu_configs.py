@@ -204,3 +204,33 @@ def test_llama70b_attnproj_tp16_full():
     for r in (0, 9):
         ref_r = oracle.linear(to_f64(attn[r][rows]), oracle.bf16_bits_to_f64(oracle.shard(ob, 1, r, t)))
         assert relf(to_f64(parts[r][rows]), ref_r) <= TOL[torch.bfloat16]
+
+
+def test_llama70b_prefill_tp8_sequence_parallel_epilogue_sampled():
+    """The benchmarked shape: rank 3 of TP=8 holds 1024 of the 8192 token rows
+    after the reduce-scatter.  Sampled rows are checked against the oracle on
+    a problem of t x 16 rows whose owned chunk holds exactly those rows (every
+    step is row-independent, so this is exact for them)."""
+    w = synth.get("llama70b_prefill_tp8")
+    t, n, h, rank = w.tp, w.n, w.h, 3
+    parts = [gen(w, synth.T_PARTIAL + q, (n, h), 1.0) for q in range(t)]
+    lo, hi = T.tp_sp_rows(n, rank, t)
+    assert (lo, hi) == (4096, 5120)
+    residual = gen(w, synth.T_RESIDUAL, (hi - lo, h), 1.0)
+    weight = gen(w, synth.T_NORM_W, (h,), 0.1) + 1.0
+    ro, out = T.tp_rs_add_rmsnorm(parts, rank, residual, weight, 1e-5)
+    torch.cuda.synchronize()
+    k = 16
+    rows = synth.sample_rows(hi - lo, k, w.seed(81))
+    c = (rank + 1) % t
+    P = []
+    for q in range(t):
+        a = np.zeros((t * k, h), np.float32)
+        a[c * k:(c + 1) * k] = f64_bits(bits(parts[q][[lo + i for i in rows]]), torch.bfloat16)
+        P.append(a)
+    R = f64_bits(bits(residual[rows]), torch.bfloat16).astype(np.float32)
+    exp_ro, exp_out = oracle.rs_add_rmsnorm(P, rank, R, f64_bits(bits(weight), torch.bfloat16),
+                                            float(np.float32(1e-5)), True)
+    assert np.array_equal(bits(ro[rows]), oracle.f32_to_bf16_bits(exp_ro))
+    g = f64_bits(bits(out[rows]), torch.bfloat16)
+    assert np.all(np.abs(g - exp_out) <= 2.0 ** -7 * np.abs(exp_out) + 1e-30)

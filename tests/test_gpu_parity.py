@@ -514,3 +514,103 @@ def test_streamed_decode_mlp_matches_oracle(n, h, fl, out_dt):
     assert relf(to_f64(p), ref) <= 1e-2
     assert torch.equal(p, T.tp_mlp_rank_forward(x, wgu, wd, out_dtype=out_dt))   # deterministic
 
+
+
+# --------------------------------------------------------------------------
+# sequence-parallel epilogue: ring reduce-scatter + residual add + RMSNorm.
+# residual_out bit-exact against the oracle's fp32 ring simulation (one
+# rounding); out within one unit in the last place of the storage type of
+# the fp64 RMSNorm of the stored residual (bf16: 2^-7 relative; fp32: the
+# fp32 mean-square and scaling, 1e-5 relative).
+# --------------------------------------------------------------------------
+
+SP_ULP = {torch.bfloat16: 2.0 ** -7, torch.float32: 1e-5}
+
+
+def sp_check(parts, rank, residual, weight, eps, ro, out):
+    dt = parts[0].dtype
+    P = [to_f64(p).astype(np.float32) for p in parts]          # exact widening
+    R = to_f64(residual).astype(np.float32)
+    exp_ro, exp_out = oracle.rs_add_rmsnorm(P, rank, R, to_f64(weight), float(np.float32(eps)),
+                                            dt == torch.bfloat16)
+    if dt == torch.bfloat16:
+        assert np.array_equal(bits(ro), oracle.f32_to_bf16_bits(exp_ro))
+    else:
+        assert np.array_equal(bits(ro), exp_ro.view(np.uint32))
+    g = to_f64(out)
+    assert g.shape == exp_out.shape
+    assert np.all(np.abs(g - exp_out) <= SP_ULP[dt] * np.abs(exp_out) + 1e-30)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("t,n,h", [(1, 5, 64), (2, 7, 1024), (3, 13, 1000), (4, 64, 8192), (8, 37, 12288),
+                                   (16, 50, 256), (5, 3, 512)])
+def test_rs_add_rmsnorm_matches_oracle(dt, t, n, h):
+    """h = 1000 (bf16) is not a whole number of 16-byte vectors (element-wise
+    path); h = 12288 keeps only 8192 per row in registers and reads the rest
+    back; n = 3 < t = 5 leaves two ranks without rows."""
+    parts = [rnd((n, h), 1.0, 600 + 13 * r + h, dt) for r in range(t)]
+    weight = rnd((h,), 0.5, 601, dt) + 1.0
+    eps = 1e-5
+    for rank in range(t):
+        lo, hi = T.tp_sp_rows(n, rank, t)
+        residual = rnd((hi - lo, h), 1.0, 602 + rank, dt)
+        ro, out = T.tp_rs_add_rmsnorm(parts, rank, residual, weight, eps)
+        torch.cuda.synchronize()
+        sp_check(parts, rank, residual, weight, eps, ro, out)
+
+
+def test_rs_add_rmsnorm_in_place_and_deterministic():
+    t, n, h = 4, 40, 4096
+    dt = torch.bfloat16
+    parts = [rnd((n, h), 1.0, 610 + r, dt) for r in range(t)]
+    weight = rnd((h,), 0.5, 611, dt) + 1.0
+    rank = 2
+    lo, hi = T.tp_sp_rows(n, rank, t)
+    residual = rnd((hi - lo, h), 1.0, 612, dt)
+    ro_a, out_a = T.tp_rs_add_rmsnorm(parts, rank, residual, weight, 1e-6)
+    buf = residual.clone()
+    ro_b, out_b = T.tp_rs_add_rmsnorm(parts, rank, buf, weight, 1e-6, residual_out=buf)
+    torch.cuda.synchronize()
+    assert ro_b.data_ptr() == buf.data_ptr()
+    assert torch.equal(ro_a, buf) and torch.equal(out_a, out_b)
+    sp_check(parts, rank, residual, weight, 1e-6, ro_a, out_a)
+
+
+def test_rs_add_rmsnorm_unaligned_buffers():
+    t, n, h = 3, 9, 256
+    dt = torch.bfloat16
+    bufs = [rnd((n * h + 1,), 1.0, 620 + r, dt) for r in range(t)]
+    parts = [b[1:].view(n, h) for b in bufs]                   # misaligned by one element
+    weight = rnd((h,), 0.5, 621, dt) + 1.0
+    rank = 1
+    lo, hi = T.tp_sp_rows(n, rank, t)
+    residual = rnd((hi - lo, h), 1.0, 622, dt)
+    ro, out = T.tp_rs_add_rmsnorm(parts, rank, residual, weight, 1e-5)
+    torch.cuda.synchronize()
+    sp_check(parts, rank, residual, weight, 1e-5, ro, out)
+
+
+def test_rs_add_rmsnorm_order_and_rounding_pins_on_gpu():
+    """The oracle's tie pins, on the GPU: ring order (2^-24 + 2^-24 + 1) and
+    the single rounding of the residual add (1 + 2^-8 + 2^-16 -> 1 + 2^-7)."""
+    e = 2.0 ** -24
+    n = t = 3
+    P = [torch.zeros(n, 4, device=DEV) for _ in range(t)]
+    for c in range(n):
+        P[c][c] = e
+        P[(c + 1) % t][c] = e
+        P[(c + 2) % t][c] = 1.0
+    w = torch.ones(4, device=DEV)
+    for r in range(t):
+        ro, _ = T.tp_rs_add_rmsnorm(P, r, torch.zeros(1, 4, device=DEV), w, 1e-5)
+        assert ro.tolist() == [[1.0 + 2.0 ** -23] * 4]
+    P = [torch.zeros(2, 8, device=DEV, dtype=torch.bfloat16) for _ in range(2)]
+    for c in range(2):
+        P[c][c] = 1.0
+        P[(c + 1) % 2][c] = 2.0 ** -8
+    wb = torch.ones(8, device=DEV, dtype=torch.bfloat16)
+    for r in range(2):
+        res = torch.full((1, 8), 2.0 ** -16, device=DEV, dtype=torch.bfloat16)
+        ro, _ = T.tp_rs_add_rmsnorm(P, r, res, wb, 1e-5)
+        assert ro.float().tolist() == [[1.0 + 2.0 ** -7] * 8]
