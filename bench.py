@@ -226,6 +226,48 @@ def leg_reduce(name, reps):
             "hbm_frac": b / ms / 1e6 / PEAK_HBM_GBPS, "algorithmic_bytes": b}
 
 
+def leg_spnorm(reps):
+    """Sequence-parallel epilogue at the 70B prefill shape: each rank's
+    reduce-scatter rows (1024 of 8192) + residual add + RMSNorm.  Calls cycle
+    over the 8 ranks, so consecutive calls read disjoint rows (8 x 151 MB
+    between two visits of a chunk: cold in the MALL), back to back between
+    one event pair; the library is called with pre-marshalled arguments so
+    that the host keeps ahead of the ~25 us calls."""
+    import ctypes
+    w = synth.get("llama70b_prefill_tp8")
+    t, n, h = w.tp, w.n, w.h
+    parts = [gen(w, synth.T_PARTIAL + q, (n, h), 1.0) for q in range(t)]
+    weight = gen(w, synth.T_NORM_W, (h,), 0.1) + 1.0
+    rows = n // t
+    res = [gen(w, synth.T_RESIDUAL + r, (rows, h), 1.0) for r in range(t)]
+    ro = [torch.empty((rows, h), dtype=w.dtype, device=DEV) for _ in range(t)]
+    out = [torch.empty((rows, h), dtype=w.dtype, device=DEV) for _ in range(t)]
+    L = T.lib()
+    ptrs = (ctypes.c_void_p * t)(*[p.data_ptr() for p in parts])
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    dt = 1 if w.dtype == torch.bfloat16 else 0
+    args = [(ptrs, t, r, n, h, dt, ctypes.c_void_p(res[r].data_ptr()), ctypes.c_void_p(weight.data_ptr()),
+             1e-5, ctypes.c_void_p(ro[r].data_ptr()), ctypes.c_void_p(out[r].data_ptr()), stream) for r in range(t)]
+    for r in range(t):
+        assert T.tp_sp_rows(n, r, t)[1] - T.tp_sp_rows(n, r, t)[0] == rows
+        assert L.tp_rs_add_rmsnorm(*args[r]) == 0
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    calls = reps * t
+    e0.record()
+    for i in range(calls):
+        L.tp_rs_add_rmsnorm(*args[i % t])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    b = (t * rows * h + rows * h + 2 * rows * h) * 2 + h * 2
+    del parts, res, ro, out
+    return {"workload": w.name, "t": t, "rows_per_rank": rows, "h": h, "ms_per_rank": ms, "GBps": b / ms / 1e6,
+            "hbm_frac": b / ms / 1e6 / PEAK_HBM_GBPS, "algorithmic_bytes": b,
+            "timing": "calls cycling over the 8 ranks, back to back between one event pair"}
+
+
 def leg_vocab(reps):
     w = synth.get("qwen3_vocab_tp2")
     table = gen(w, synth.T_TABLE, (w.vocab, w.h), 0.02)
@@ -410,7 +452,7 @@ def main():
         f"down {dn_ms:.3f} reduce {rd_ms:.3f} -> {value:.1f} TFLOP/s")
 
     legs = {}
-    names = ["decode", "reduce8", "reduce16", "vocab", "attnproj", "qwen_fp32"] if a.legs == "all" else \
+    names = ["decode", "reduce8", "reduce16", "spnorm", "vocab", "attnproj", "qwen_fp32"] if a.legs == "all" else \
         ([] if a.legs == "none" else a.legs.split(","))
     for nm in names:
         log(f"bench: leg {nm}")
@@ -420,6 +462,8 @@ def main():
             legs[nm] = leg_reduce("llama70b_prefill_tp8", 20)
         elif nm == "reduce16":
             legs[nm] = leg_reduce("llama70b_attnproj_tp16", 10)
+        elif nm == "spnorm":
+            legs[nm] = leg_spnorm(10)
         elif nm == "vocab":
             legs[nm] = leg_vocab(20)
         elif nm == "attnproj":

@@ -14,13 +14,17 @@
 // Transfers are not performed (one device); the arithmetic and the HBM
 // traffic of the rank's share are.
 //
-// Layout: one workgroup of 256 threads per row; a thread owns 16-byte
-// vectors tid, tid + 256, ... of the row.  For t = 2, 4, 8, 16 every partial
+// Layout: one workgroup of 1024 threads per row; a thread owns 16-byte
+// vectors tid, tid + 1024, ... of the row.  For t = 2, 4, 8, 16 every partial
 // load of a vector is issued before the first add.  The first KEEP vectors
 // of each thread stay in registers for step 3; further ones (rows longer than
-// 256 x KEEP vectors) are read back from residual_out, which the same thread
+// 1024 x KEEP vectors) are read back from residual_out, which the same thread
 // wrote.  The mean square is reduced in a fixed tree (wave shuffles, then the
-// four wave sums in order): deterministic.
+// wave sums in order): deterministic.  Both outputs are written with
+// non-temporal stores (nothing reads them back soon).  Measured at the 70B
+// prefill shard (8 x 1024 rows of 8192): 256-thread workgroups, 36.9 us
+// (one round of blocks: every block loads, then stores, at the same time);
+// 1024 threads, 34.3 us; plus non-temporal stores, 31.1 us = 74% of HBM.
 #include "common.hpp"
 
 namespace tpk {
@@ -79,26 +83,29 @@ template <> struct SpVec<float> {
     }
 };
 
-// sum over the 256 threads in a fixed order; every thread gets the result
-__device__ __forceinline__ float block_sum(float v, float* lds4) {
+// sum over the BS threads in a fixed order; every thread gets the result
+template <int BS>
+__device__ __forceinline__ float block_sum(float v, float* ldsw) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off, 64);
-    if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
+    if ((threadIdx.x & 63) == 0) ldsw[threadIdx.x >> 6] = v;
     __syncthreads();
-    const float s = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+    float s = ldsw[0];
+#pragma unroll
+    for (int w = 1; w < BS / 64; ++w) s = s + ldsw[w];
     return s;
 }
 
 // T = t fixed at compile time (all loads of a vector in flight), or 0 for a
 // runtime t
-template <typename InT, int T, int KEEP>
-__global__ __launch_bounds__(256) void rs_add_rmsnorm_kernel(SpParts parts, int t, int c, int64_t row0,
+template <typename InT, int T, int KEEP, int BS>
+__global__ __launch_bounds__(BS) void rs_add_rmsnorm_kernel(SpParts parts, int t, int c, int64_t row0,
                                                             int64_t h, const InT* residual,
                                                             const InT* __restrict__ weight, float eps,
                                                             InT* residual_out, InT* __restrict__ out) {
     using V = SpVec<InT>;
     constexpr int N = V::N;
-    __shared__ float lds4[4];
+    __shared__ float ldsw[BS / 64];
     const int tt = T > 0 ? T : t;
     const int64_t r = blockIdx.x;                        // row within the chunk
     const int64_t grow = row0 + r;                       // row within [n, h]
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(256) void rs_add_rmsnorm_kernel(SpParts parts, int 
         V::widen(res[v], g);
 #pragma unroll
         for (int q = 0; q < N; ++q) f[q] = acc[q] + g[q];
-        rout[v] = V::narrow(f);
+        __builtin_nontemporal_store(V::narrow(f), rout + v);
     };
 
     float keep[KEEP][N];
@@ -148,20 +155,20 @@ __global__ __launch_bounds__(256) void rs_add_rmsnorm_kernel(SpParts parts, int 
     const int64_t v0 = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < KEEP; ++k) {
-        const int64_t v = v0 + (int64_t)k * 256;
+        const int64_t v = v0 + (int64_t)k * BS;
         if (v < nvec) {
             reduce_vec(v, keep[k]);
 #pragma unroll
             for (int q = 0; q < N; ++q) ss = ss + keep[k][q] * keep[k][q];
         }
     }
-    for (int64_t v = v0 + (int64_t)KEEP * 256; v < nvec; v += 256) {
+    for (int64_t v = v0 + (int64_t)KEEP * BS; v < nvec; v += BS) {
         float f[N];
         reduce_vec(v, f);
 #pragma unroll
         for (int q = 0; q < N; ++q) ss = ss + f[q] * f[q];
     }
-    const float total = block_sum(ss, lds4);
+    const float total = block_sum<BS>(ss, ldsw);
     const float inv = 1.0f / __fsqrt_rn(total / (float)h + eps);
 
     const u32x4* wv = reinterpret_cast<const u32x4*>(weight);
@@ -171,14 +178,14 @@ __global__ __launch_bounds__(256) void rs_add_rmsnorm_kernel(SpParts parts, int 
         V::widen(wv[v], w);
 #pragma unroll
         for (int q = 0; q < N; ++q) f[q] = f[q] * inv * w[q];
-        ov[v] = V::narrow(f);
+        __builtin_nontemporal_store(V::narrow(f), ov + v);
     };
 #pragma unroll
     for (int k = 0; k < KEEP; ++k) {
-        const int64_t v = v0 + (int64_t)k * 256;
+        const int64_t v = v0 + (int64_t)k * BS;
         if (v < nvec) norm_vec(v, keep[k]);
     }
-    for (int64_t v = v0 + (int64_t)KEEP * 256; v < nvec; v += 256) {
+    for (int64_t v = v0 + (int64_t)KEEP * BS; v < nvec; v += BS) {
         float f[N];
         V::widen(rout[v], f);
         norm_vec(v, f);
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(256) void rs_add_rmsnorm_scalar_kernel(SpParts part
         const float s = Elem<InT>::load(residual_out + r * h + j);     // the stored value
         ss = ss + s * s;
     }
-    const float total = block_sum(ss, lds4);
+    const float total = block_sum<256>(ss, lds4);
     const float inv = 1.0f / __fsqrt_rn(total / (float)h + eps);
     for (int64_t j = threadIdx.x; j < h; j += 256) {
         const float s = Elem<InT>::load(residual_out + r * h + j);
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(256) void rs_add_rmsnorm_scalar_kernel(SpParts part
     }
 }
 
-template <typename InT, int KEEP>
+template <typename InT, int KEEP, int BS>
 hipError_t launch_vec(const SpParts& pp, int t, int c, int64_t row0, int64_t rows, int64_t h, const void* residual,
                       const void* weight, float eps, void* residual_out, void* out, hipStream_t s) {
     const dim3 grid((unsigned)rows);
@@ -224,11 +231,11 @@ hipError_t launch_vec(const SpParts& pp, int t, int c, int64_t row0, int64_t row
     InT* ro = static_cast<InT*>(residual_out);
     InT* o = static_cast<InT*>(out);
     switch (t) {
-        case 2: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 2, KEEP>), grid, dim3(256), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
-        case 4: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 4, KEEP>), grid, dim3(256), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
-        case 8: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 8, KEEP>), grid, dim3(256), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
-        case 16: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 16, KEEP>), grid, dim3(256), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
-        default: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 0, KEEP>), grid, dim3(256), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
+        case 2: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 2, KEEP, BS>), grid, dim3(BS), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
+        case 4: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 4, KEEP, BS>), grid, dim3(BS), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
+        case 8: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 8, KEEP, BS>), grid, dim3(BS), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
+        case 16: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 16, KEEP, BS>), grid, dim3(BS), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
+        default: hipLaunchKernelGGL((rs_add_rmsnorm_kernel<InT, 0, KEEP, BS>), grid, dim3(BS), 0, s, pp, t, c, row0, h, res, w, eps, ro, o); break;
     }
     return hipGetLastError();
 }
@@ -248,7 +255,11 @@ hipError_t launch_typed(const void* const* partials, int t, int c, int64_t row0,
     if ((g & 15u) == 0 && h % N == 0) {
         // keep up to 4 vectors per thread (8192 bf16 / 4096 fp32 elements per
         // row) in registers
-        return launch_vec<InT, 4>(pp, t, c, row0, rows, h, residual, weight, eps, residual_out, out, s);
+        // 1024 threads, one vector each in registers (8192 bf16 / 4096 fp32
+        // elements per row; longer rows read the rest back).  A second one
+        // would take the t = 8 kernel past 64 VGPRs and leave one workgroup
+        // per CU instead of two (measured 35.7 us against 31.1 us).
+        return launch_vec<InT, 1, 1024>(pp, t, c, row0, rows, h, residual, weight, eps, residual_out, out, s);
     }
     hipLaunchKernelGGL((rs_add_rmsnorm_scalar_kernel<InT>), dim3((unsigned)rows), dim3(256), 0, s, pp, t, c, row0, h,
                        static_cast<const InT*>(residual), static_cast<const InT*>(weight), eps,

@@ -25,9 +25,10 @@ BASE_SEED = 42
 # tensor ids within a workload
 T_X, T_GATE, T_UP, T_DOWN, T_TABLE, T_IDS = 0, 1, 2, 3, 4, 5
 T_WQ, T_WK, T_WV, T_WO = 6, 7, 8, 9
-T_RESIDUAL, T_NORM_W = 10, 11
+T_NORM_W = 10
 T_ATTN_OUT = 100      # + rank
 T_PARTIAL = 200       # + rank
+T_RESIDUAL = 300      # + rank
 
 W_STD = 0.02
 X_STD = 1.0

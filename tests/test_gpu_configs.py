@@ -216,7 +216,7 @@ def test_llama70b_prefill_tp8_sequence_parallel_epilogue_sampled():
     parts = [gen(w, synth.T_PARTIAL + q, (n, h), 1.0) for q in range(t)]
     lo, hi = T.tp_sp_rows(n, rank, t)
     assert (lo, hi) == (4096, 5120)
-    residual = gen(w, synth.T_RESIDUAL, (hi - lo, h), 1.0)
+    residual = gen(w, synth.T_RESIDUAL + rank, (hi - lo, h), 1.0)
     weight = gen(w, synth.T_NORM_W, (h,), 0.1) + 1.0
     ro, out = T.tp_rs_add_rmsnorm(parts, rank, residual, weight, 1e-5)
     torch.cuda.synchronize()
