@@ -72,6 +72,8 @@ def _load():
         "orc_reduce_sum_f64": (None, [ctypes.POINTER(_f64p), _int, _i64, _f64p]),
         "orc_ring_traffic": (_int, [_int, _i64, _i64p, _i64p, ctypes.POINTER(ctypes.c_int)]),
         "orc_sp_rows": (None, [_i64, _int, _int, _i64p, _i64p]),
+        "orc_reduce_rank_f32": (None, [ctypes.POINTER(_f32p), _int, _i64, _f32p]),
+        "orc_logits_gather_argmax": (_int, [ctypes.POINTER(_f64p), _int, _i64, _i64, _f64p, _i64p]),
         "orc_rs_add_rmsnorm": (_int, [ctypes.POINTER(_f32p), _int, _int, _i64, _i64, _f32p, _f64p,
                                       ctypes.c_double, _int, _f32p, _f64p]),
     }
@@ -346,3 +348,30 @@ def rs_add_rmsnorm(parts, rank, residual, weight, eps, round_bf16):
                                       1 if round_bf16 else 0, _p(res_out, _f32p), _p(out, _f64p)),
            "rs_add_rmsnorm")
     return res_out, out
+
+
+# --- one-shot (rank-order) reduce; vocab logits gather + greedy argmax -----------
+
+def reduce_rank_f32(parts) -> np.ndarray:
+    """((0 + P_0) + P_1) + ... in fp32, the one-shot all-reduce's order."""
+    parts = [np.ascontiguousarray(p, dtype=np.float32).reshape(-1) for p in parts]
+    t = len(parts)
+    K = parts[0].size
+    arr = (_f32p * t)(*[_p(p, _f32p) for p in parts])
+    out = np.empty(K, dtype=np.float32)
+    _load().orc_reduce_rank_f32(arr, t, K, _p(out, _f32p))
+    return out
+
+
+def logits_gather_argmax(shards, vocab):
+    """Concatenation of the t logits shards [n, end_r - start_r] along the
+    vocabulary (fp64) and the first index of each row's maximum."""
+    shards = [_f64(s) for s in shards]
+    t = len(shards)
+    n = shards[0].shape[0]
+    arr = (_f64p * t)(*[_p(s, _f64p) for s in shards])
+    full = np.empty((n, vocab), dtype=np.float64)
+    am = np.empty(n, dtype=np.int64)
+    _check(_load().orc_logits_gather_argmax(arr, t, n, vocab, _p(full, _f64p), _p(am, _i64p)),
+           "logits_gather_argmax")
+    return full, am

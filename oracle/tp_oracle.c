@@ -495,6 +495,62 @@ ORC_API void orc_reduce_sum_f64(const double* const* parts, int t, int64_t K, do
     }
 }
 
+/* One-shot all-reduce: every rank reads all ranks' buffers and adds them,
+ * in rank order, into an accumulator that starts at zero ([VLLM13] §1.2,
+ * the low-latency all-reduce pseudocode: out = zeros_like(x), then
+ * out += load_from(buf) for each peer buffer; [GUIDE62] §6.3: each GPU
+ * reads the others' buffers and sums).  fp32 adds:
+ * out[i] = ((0 + P_0[i]) + P_1[i]) + ... + P_{t-1}[i].  Every rank computes
+ * the same sum, so one result stands for all of them. */
+ORC_API void orc_reduce_rank_f32(const float* const* parts, int t, int64_t K, float* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < K; ++i) {
+        float acc = 0.0f;
+        for (int r = 0; r < t; ++r) acc = acc + parts[r][i];
+        out[i] = acc;
+    }
+}
+
+/* Full logits from the vocab-parallel LM head and the greedy next token.
+ * [SCRATCH] TPTransformer.forward all-gathers every rank's logits,
+ * concatenates them along the vocabulary and truncates to the vocabulary
+ * size; its generation loop then takes argmax of the logits ([VLLM13] §2.4.2:
+ * Y = gather([Y_1, Y_2])).  Shard r holds columns [start_r, end_r) of
+ * orc_vocab_range without padding, so concatenating the shards gives the
+ * truncated result directly.  argmax: the first index of the maximum, a NaN
+ * counting as larger than every number (the rule of the torch.argmax the
+ * demo calls).  shards[r]: n x (end_r - start_r) values; full (may be NULL):
+ * n x vocab; argmax: n.  Returns 0, or 1 for bad arguments. */
+ORC_API int orc_logits_gather_argmax(const double* const* shards, int t, int64_t n, int64_t vocab,
+                                     double* full, int64_t* argmax) {
+    if (t < 1 || n < 0 || vocab < 1) return 1;
+    for (int64_t i = 0; i < n; ++i) {
+        double best = 0.0;
+        int64_t bi = -1;
+        int nan_seen = 0;
+        for (int r = 0; r < t; ++r) {
+            int64_t start, end;
+            if (orc_vocab_range(vocab, r, t, &start, &end)) return 1;
+            const int64_t w = end - start;
+            for (int64_t j = 0; j < w; ++j) {
+                const double v = shards[r][i * w + j];
+                const int64_t col = start + j;
+                if (full) full[i * vocab + col] = v;
+                if (nan_seen) continue;
+                if (v != v) {
+                    nan_seen = 1;
+                    bi = col;
+                } else if (bi < 0 || v > best) {
+                    best = v;
+                    bi = col;
+                }
+            }
+        }
+        argmax[i] = bi;
+    }
+    return 0;
+}
+
 /* Token-row chunk c of the sequence-parallel split: rows [floor(c n/t),
  * floor((c+1) n/t)).  [SCRATCH] Exercises, item 1 (sequence parallelism):
  * after the reduce-scatter every rank holds the complete result for 1/t of

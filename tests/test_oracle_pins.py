@@ -646,3 +646,58 @@ def test_rmsnorm_reads_the_stored_residual():
         assert np.allclose(out[0], v / math.sqrt(np.mean(v * v)), rtol=1e-15, atol=0)
         u = np.array([1.0 + 2.0 ** -8 + 2.0 ** -16, 1.0 + 2.0 ** -16])
         assert not np.allclose(out[0], u / math.sqrt(np.mean(u * u)), rtol=1e-6, atol=0)
+
+
+# --------------------------------------------------------------------------
+# one-shot (rank-order) reduce; logits gather + greedy argmax
+# --------------------------------------------------------------------------
+
+def test_rank_order_reduce_ties_and_zero_start():
+    """((0 + P_0) + P_1) + P_2: on the ring pin's data the 1 + 2^-23 lands on
+    element 2 (ring order puts it on element 1); the zero start turns a sum
+    of negative zeros into +0."""
+    e = np.float32(2.0 ** -24)
+    one = np.float32(1.0)
+    P0 = np.array([e, one, e], dtype=np.float32)
+    P1 = np.array([one, e, e], dtype=np.float32)
+    P2 = np.array([e, e, one], dtype=np.float32)
+    assert oracle.reduce_rank_f32([P0, P1, P2]).tolist() == [1.0, 1.0, 1.0 + 2.0 ** -23]
+    assert oracle.ring_allreduce_f32([P0, P1, P2]).tolist() == [1.0, 1.0 + 2.0 ** -23, 1.0]
+    z = oracle.reduce_rank_f32([np.array([-0.0], np.float32)] * 3)
+    assert z[0] == 0.0 and not np.signbit(z[0])
+
+
+@pytest.mark.parametrize("t", [1, 2, 5, 8])
+def test_rank_order_reduce_is_exact_on_representable_sums(t):
+    K = 37
+    parts = [np.full(K, float(1 << r), np.float32) * (1 + np.arange(K) % 5) for r in range(t)]
+    out = oracle.reduce_rank_f32(parts)
+    assert np.array_equal(out, sum(p.astype(np.float64) for p in parts).astype(np.float32))
+
+
+@pytest.mark.parametrize("V,t", [(10, 3), (11, 4), (7, 8), (151936, 2)])
+def test_logits_gather_is_the_full_logits_and_argmax_matches_torch(V, t):
+    """Concatenating the rank shards gives X.E^T over the whole vocabulary
+    (trailing ranks may be short or empty); the greedy pick is
+    torch.argmax of that row (the call the pages' generation loop makes)."""
+    rng = np.random.default_rng(V + t)
+    n, h = 3, 8
+    X = rng.standard_normal((n, h))
+    E = rng.standard_normal((V, h))
+    shards = [oracle.lm_head_rank(X, E, r, t) for r in range(t)]
+    full, am = oracle.logits_gather_argmax(shards, V)
+    assert np.allclose(full, X @ E.T, rtol=1e-12, atol=1e-12)
+    assert am.tolist() == torch.argmax(torch.from_numpy(full), dim=1).tolist()
+
+
+def test_argmax_ties_take_the_first_index_and_nan_wins():
+    t, V = 3, 7                                   # shards of 3, 3, 1 columns
+    row_tie = [[1.0, 5.0, 2.0], [5.0, 0.0, 5.0], [-1.0]]
+    row_nan = [[1.0, 2.0, 3.0], [9.0, float("nan"), 10.0], [float("nan")]]
+    row_neg = [[-3.0, -2.0, -2.0], [-7.0, -2.5, -9.0], [-2.0]]
+    shards = [np.array([row_tie[r], row_nan[r], row_neg[r]]) for r in range(t)]
+    _, am = oracle.logits_gather_argmax(shards, V)
+    assert am.tolist() == [1, 4, 1]
+    full = torch.tensor([[1.0, 5.0, 2.0, 5.0, 0.0, 5.0, -1.0], [1.0, 2.0, 3.0, 9.0, float("nan"), 10.0, float("nan")],
+                         [-3.0, -2.0, -2.0, -7.0, -2.5, -9.0, -2.0]], dtype=torch.float64)
+    assert torch.argmax(full, dim=1).tolist() == [1, 4, 1]
