@@ -63,7 +63,8 @@ typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
 
 /* Summation order of tp_partial_reduce. */
 typedef enum {
-    TP_ORDER_RING = 0   /* ring reduce-scatter chunk order (see tp_partial_reduce) */
+    TP_ORDER_RING = 0,  /* ring reduce-scatter chunk order (see tp_partial_reduce) */
+    TP_ORDER_RANK = 1   /* one-shot order: ((0 + P_0) + P_1) + ... for every element */
 } tp_order;
 
 /* One transfer of the ring all-reduce schedule (tp_ring_schedule). */
@@ -163,11 +164,16 @@ TP_API tp_status tp_mlp_rank_forward(const void* x, int64_t n, int64_t h, const 
 
 /* ---- sum of the t partials (the all-reduce's arithmetic, one device) ----- */
 
-/* out = sum_r partials[r], element-wise over K elements, in the order a ring
- * reduce-scatter adds them ([VLLM13] §1.1.1): the K elements are cut into t
- * chunks [floor(c K/t), floor((c+1) K/t)); chunk c is accumulated in fp32 as
- * ((P_c + P_{c+1}) + P_{c+2}) + ... + P_{c+t-1} (indices mod t) and rounded
+/* out = sum_r partials[r], element-wise over K elements, in fp32, rounded
  * once to out_dt.  Deterministic and bit-reproducible; no atomics.
+ *   order TP_ORDER_RING: the order a ring reduce-scatter adds them
+ *     ([VLLM13] §1.1.1): the K elements are cut into t chunks
+ *     [floor(c K/t), floor((c+1) K/t)); chunk c is accumulated as
+ *     ((P_c + P_{c+1}) + P_{c+2}) + ... + P_{c+t-1} (indices mod t).
+ *   order TP_ORDER_RANK: the one-shot all-reduce, where every rank reads all
+ *     buffers and adds them into a zero accumulator ([VLLM13] §1.2, the
+ *     low-latency all-reduce; [GUIDE62] §6.3): ((0 + P_0) + P_1) + ... +
+ *     P_{t-1} for every element (a sum of negative zeros is +0).
  *   partials: HOST array of t device pointers, each [K] in_dt; out [K] out_dt
  *   (may alias partials[c] only if t == 1).  1 <= t <= TP_MAX_RANKS. */
 TP_API tp_status tp_partial_reduce(const void* const* partials /*HOST array*/, int t, int64_t K,
@@ -181,6 +187,22 @@ TP_API tp_status tp_partial_reduce(const void* const* partials /*HOST array*/, i
  * 2(t-1) rounds ([VLLM13] §1.2).  steps: HOST array of max_steps entries. */
 TP_API tp_status tp_ring_schedule(int t, int64_t K, tp_ring_step* steps /*HOST*/, int max_steps,
                            int* n_steps /*HOST*/);
+
+/* The full logits and the greedy next token from the t vocab-parallel LM-head
+ * shards (the gather that follows tp_lm_head_rank).  [SCRATCH]
+ * TPTransformer.forward all-gathers the ranks' logits, concatenates them
+ * along the vocabulary and truncates to `vocab`; its generation loop takes
+ * argmax ([VLLM13] §2.4.2: Y = gather([Y_1, Y_2])).  Shard r holds columns
+ * [start_r, end_r) of tp_vocab_range without padding, so
+ *   full[i, start_r + j] = shards[r][i, j]                 (bit-exact copy)
+ *   argmax[i] = first column of the maximum of full[i, :], a NaN counting
+ *               as larger than every number (torch.argmax's rule).
+ *   shards: HOST array of t device pointers, shard r [n, end_r - start_r]
+ *   fp32 (an empty trailing shard may be null); full [n, vocab] fp32 or
+ *   NULL; argmax [n] int64 (device) or NULL; at least one of the two.
+ *   dt must be TP_F32.  Deterministic. */
+TP_API tp_status tp_logits_gather_argmax(const void* const* shards /*HOST array*/, int t, int64_t n, int64_t vocab,
+                                         tp_dtype dt, void* full, int64_t* argmax, void* stream);
 
 /* ---- sequence-parallel epilogue (reduce-scatter + residual add + RMSNorm) */
 

@@ -279,9 +279,29 @@ tp_status tp_partial_reduce(const void* const* partials, int t, int64_t K, tp_dt
     if (K < 0 || K > kMaxElems) return fail(TP_EINVAL, "tp_partial_reduce: K %lld out of range", (long long)K);
     if (!valid_dt(in_dt) || !valid_dt(out_dt) || !valid_pair(in_dt, out_dt))
         return fail(TP_EDTYPE, "tp_partial_reduce: unsupported dtype pair (%d -> %d)", (int)in_dt, (int)out_dt);
-    if (order != TP_ORDER_RING) return fail(TP_EINVAL, "tp_partial_reduce: unknown order %d", (int)order);
-    return hip_status(tpk::launch_ring_reduce(partials, t, K, in_dt, out, out_dt, as_stream(stream)),
+    if (order != TP_ORDER_RING && order != TP_ORDER_RANK)
+        return fail(TP_EINVAL, "tp_partial_reduce: unknown order %d", (int)order);
+    return hip_status(tpk::launch_ring_reduce(partials, t, K, in_dt, out, out_dt, order, as_stream(stream)),
                       "tp_partial_reduce");
+}
+
+tp_status tp_logits_gather_argmax(const void* const* shards, int t, int64_t n, int64_t vocab, tp_dtype dt, void* full,
+                                  int64_t* argmax, void* stream) {
+    if (!shards || (!full && !argmax)) return fail(TP_EINVAL, "tp_logits_gather_argmax: null pointer");
+    if (t < 1 || t > TP_MAX_RANKS)
+        return fail(TP_EINVAL, "tp_logits_gather_argmax: t %d outside [1, %d]", t, TP_MAX_RANKS);
+    if (dt != TP_F32) return fail(TP_EDTYPE, "tp_logits_gather_argmax: logits must be fp32");
+    if (n < 0 || n > INT32_MAX || vocab < 1 || vocab > kMaxElems || n * vocab > kMaxElems)
+        return fail(TP_EINVAL, "tp_logits_gather_argmax: bad shape n %lld vocab %lld", (long long)n, (long long)vocab);
+    for (int r = 0; r < t; ++r) {
+        int64_t s, e;
+        if (tp_status st = tp_vocab_range(vocab, r, t, &s, &e)) return st;
+        if (e > s && !shards[r]) return fail(TP_EINVAL, "tp_logits_gather_argmax: shards[%d] is null", r);
+        if (full && shards[r] == full) return fail(TP_EINVAL, "tp_logits_gather_argmax: full aliases shards[%d]", r);
+    }
+    ok();
+    return hip_status(tpk::launch_logits_gather_argmax(shards, t, n, vocab, full, argmax, as_stream(stream)),
+                      "tp_logits_gather_argmax");
 }
 
 tp_status tp_sp_rows(int64_t n, int tp_rank, int tp_size, int64_t* lo, int64_t* hi) {

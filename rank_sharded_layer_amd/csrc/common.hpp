@@ -60,11 +60,14 @@ hipError_t launch_copy2d(const void* src, int64_t src_ld_bytes, void* dst, int64
                          int64_t rows, int64_t row_bytes, hipStream_t s);
 
 hipError_t launch_ring_reduce(const void* const* parts, int t, int64_t K, tp_dtype in_dt,
-                              void* out, tp_dtype out_dt, hipStream_t s);
+                              void* out, tp_dtype out_dt, tp_order order, hipStream_t s);
 
 hipError_t launch_rs_add_rmsnorm(const void* const* partials, int t, int tp_rank, int64_t n, int64_t h, tp_dtype dt,
                                  const void* residual, const void* weight, float eps, void* residual_out, void* out,
                                  hipStream_t s);
+
+hipError_t launch_logits_gather_argmax(const void* const* shards, int t, int64_t n, int64_t vocab, void* full,
+                                       int64_t* argmax, hipStream_t s);
 
 hipError_t launch_vocab_embed(const int64_t* ids, int64_t n, const void* table, int64_t start,
                               int64_t end, int64_t h, int esize, void* out, hipStream_t s);

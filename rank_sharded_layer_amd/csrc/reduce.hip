@@ -7,6 +7,12 @@
 // chunk unchanged in the all-gather (§1.1.2).  This kernel performs exactly
 // that arithmetic (fp32 adds, one rounding at the end) without the transfers.
 //
+// TP_ORDER_RANK is the one-shot form instead (the low-latency all-reduce of
+// "vLLM source analysis 13" §1.2 and the custom all-reduce of "AIInfraGuide
+// 6.2" §6.3: every rank reads all buffers and adds them into a zero
+// accumulator): ((0 + P_0) + P_1) + ... + P_{t-1} for every element, on the
+// same kernels with the rotation off and a +0 start.
+//
 // HBM-streaming design: grid.y is the chunk, so the rotation of the partial
 // order is uniform per workgroup and the per-element index math is a single
 // add.  Each lane moves 16-byte vectors (8 bf16 or 4 fp32).  For t = 2, 4,
@@ -81,23 +87,25 @@ __device__ __forceinline__ int64_t chunk_lo(int64_t K, int t, int c) {
 // The chunk's unaligned head [lo, min(vlo, hi)) and tail [max(vhi, lo), hi),
 // element by element, in the same rotated order as the vector body.
 template <typename InT, typename OutT>
-__device__ __forceinline__ void reduce_edges(const PartPtrs& parts, int t, int c, int64_t lo,
+__device__ __forceinline__ void reduce_edges(const PartPtrs& parts, int t, int c, int rank_order, int64_t lo,
                                              int64_t hi, int64_t vlo, int64_t vhi,
                                              OutT* __restrict__ out) {
+    const int c0 = rank_order ? 0 : c;
     auto src = [&](int j) -> const InT* {
-        int r = c + j;
+        int r = c0 + j;
         if (r >= t) r -= t;
         return static_cast<const InT*>(parts.p[r]);
     };
+    const float z = rank_order ? 0.0f : -0.0f;      // -0 + x == x for every x
     const int64_t head_end = vlo < hi ? vlo : hi;
     const int64_t tail_beg = vhi > head_end ? vhi : head_end;
     for (int64_t i = lo + threadIdx.x; i < head_end; i += blockDim.x) {
-        float acc = Elem<InT>::load(src(0) + i);
+        float acc = z + Elem<InT>::load(src(0) + i);
         for (int j = 1; j < t; ++j) acc = acc + Elem<InT>::load(src(j) + i);
         Elem<OutT>::store(out + i, acc);
     }
     for (int64_t i = tail_beg + threadIdx.x; i < hi; i += blockDim.x) {
-        float acc = Elem<InT>::load(src(0) + i);
+        float acc = z + Elem<InT>::load(src(0) + i);
         for (int j = 1; j < t; ++j) acc = acc + Elem<InT>::load(src(j) + i);
         Elem<OutT>::store(out + i, acc);
     }
@@ -113,7 +121,7 @@ __device__ __forceinline__ void reduce_edges(const PartPtrs& parts, int t, int c
 template <typename InT, typename OutT, int T>
 __global__ __launch_bounds__(256) void ring_reduce_fixed_kernel(PartPtrs parts, int64_t K,
                                                                 OutT* __restrict__ out,
-                                                                int blocks_per_chunk) {
+                                                                int blocks_per_chunk, int rank_order) {
     using V = Vec<InT>;
     constexpr int N = V::N;
     const int c = blockIdx.y;
@@ -122,13 +130,16 @@ __global__ __launch_bounds__(256) void ring_reduce_fixed_kernel(PartPtrs parts, 
     int64_t vlo = (lo + N - 1) / N * N;
     int64_t vhi = hi / N * N;
     if (vhi < vlo) vhi = vlo;
-    if (blockIdx.x == 0) reduce_edges<InT, OutT>(parts, T, c, lo, hi, vlo, vhi, out);
+    if (blockIdx.x == 0) reduce_edges<InT, OutT>(parts, T, c, rank_order, lo, hi, vlo, vhi, out);
 
-    // position j of the ring order reads rank (c + j) mod T; wave-uniform
+    // position j of the ring order reads rank (c + j) mod T (rank order:
+    // rank j); wave-uniform
+    const int c0 = rank_order ? 0 : c;
+    const float z = rank_order ? 0.0f : -0.0f;      // the one-shot sum starts at +0
     const typename V::raw* s[T];
 #pragma unroll
     for (int j = 0; j < T; ++j) {
-        const int r = c + j < T ? c + j : c + j - T;
+        const int r = c0 + j < T ? c0 + j : c0 + j - T;
         s[j] = reinterpret_cast<const typename V::raw*>(static_cast<const InT*>(parts.p[r]) + vlo);
     }
     OutT* o = out + vlo;
@@ -140,6 +151,8 @@ __global__ __launch_bounds__(256) void ring_reduce_fixed_kernel(PartPtrs parts, 
         for (int j = 0; j < T; ++j) raw[j] = __builtin_nontemporal_load(s[j] + v);
         float acc[N], f[N];
         V::widen(raw[0], acc);
+#pragma unroll
+        for (int q = 0; q < N; ++q) acc[q] = z + acc[q];
 #pragma unroll
         for (int j = 1; j < T; ++j) {
             V::widen(raw[j], f);
@@ -153,7 +166,7 @@ __global__ __launch_bounds__(256) void ring_reduce_fixed_kernel(PartPtrs parts, 
 template <typename InT, typename OutT, int UNROLL>
 __global__ __launch_bounds__(256) void ring_reduce_kernel(PartPtrs parts, int t, int64_t K,
                                                           OutT* __restrict__ out,
-                                                          int blocks_per_chunk) {
+                                                          int blocks_per_chunk, int rank_order) {
     using V = Vec<InT>;
     constexpr int N = V::N;
     const int c = blockIdx.y;
@@ -164,16 +177,18 @@ __global__ __launch_bounds__(256) void ring_reduce_kernel(PartPtrs parts, int t,
     int64_t vhi = hi / N * N;
     if (vhi < vlo) vhi = vlo;
 
-    // the rotated order for this chunk: position j reads rank (c + j) mod t.
-    // The index is wave-uniform, so the pointer comes straight from the
-    // kernel-argument segment with a scalar load.
+    // the rotated order for this chunk: position j reads rank (c + j) mod t
+    // (rank order: rank j).  The index is wave-uniform, so the pointer comes
+    // straight from the kernel-argument segment with a scalar load.
+    const int c0 = rank_order ? 0 : c;
+    const float z = rank_order ? 0.0f : -0.0f;      // the one-shot sum starts at +0
     auto src = [&](int j) -> const InT* {
-        int r = c + j;
+        int r = c0 + j;
         if (r >= t) r -= t;
         return static_cast<const InT*>(parts.p[r]);
     };
 
-    if (blockIdx.x == 0) reduce_edges<InT, OutT>(parts, t, c, lo, hi, vlo, vhi, out);
+    if (blockIdx.x == 0) reduce_edges<InT, OutT>(parts, t, c, rank_order, lo, hi, vlo, vhi, out);
 
     const int64_t nvec = (vhi - vlo) / N;
     const int64_t stride = (int64_t)blocks_per_chunk * blockDim.x;
@@ -187,7 +202,11 @@ __global__ __launch_bounds__(256) void ring_reduce_kernel(PartPtrs parts, int t,
             raw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename V::raw*>(src(0) + e));
         }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) V::widen(raw[u], acc[u]);
+        for (int u = 0; u < UNROLL; ++u) {
+            V::widen(raw[u], acc[u]);
+#pragma unroll
+            for (int q = 0; q < N; ++q) acc[u][q] = z + acc[u][q];
+        }
         for (int j = 1; j < t; ++j) {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
@@ -212,6 +231,8 @@ __global__ __launch_bounds__(256) void ring_reduce_kernel(PartPtrs parts, int t,
         const int64_t e = vlo + v * N;
         float acc[N];
         V::widen(*reinterpret_cast<const typename V::raw*>(src(0) + e), acc);
+#pragma unroll
+        for (int q = 0; q < N; ++q) acc[q] = z + acc[q];
         for (int j = 1; j < t; ++j) {
             float f[N];
             V::widen(*reinterpret_cast<const typename V::raw*>(src(j) + e), f);
@@ -226,14 +247,15 @@ __global__ __launch_bounds__(256) void ring_reduce_kernel(PartPtrs parts, int t,
 template <typename InT, typename OutT>
 __global__ __launch_bounds__(256) void ring_reduce_scalar_kernel(PartPtrs parts, int t, int64_t K,
                                                                  OutT* __restrict__ out,
-                                                                 int blocks_per_chunk) {
+                                                                 int blocks_per_chunk, int rank_order) {
     const int c = blockIdx.y;
     const int64_t lo = chunk_lo(K, t, c);
     const int64_t hi = chunk_lo(K, t, c + 1);
+    const float z = rank_order ? 0.0f : -0.0f;      // the one-shot sum starts at +0
     for (int64_t i = lo + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < hi;
          i += (int64_t)blocks_per_chunk * blockDim.x) {
-        int r = c;
-        float acc = Elem<InT>::load(static_cast<const InT*>(parts.p[r]) + i);
+        int r = rank_order ? 0 : c;
+        float acc = z + Elem<InT>::load(static_cast<const InT*>(parts.p[r]) + i);
         for (int j = 1; j < t; ++j) {
             r = r + 1 == t ? 0 : r + 1;
             acc = acc + Elem<InT>::load(static_cast<const InT*>(parts.p[r]) + i);
@@ -252,7 +274,7 @@ static bool fixed_enabled() {
 }
 
 template <typename InT, typename OutT>
-static hipError_t launch_typed(const void* const* p, int t, int64_t K, void* out, hipStream_t s) {
+static hipError_t launch_typed(const void* const* p, int t, int64_t K, void* out, int ro, hipStream_t s) {
     PartPtrs pp = {};
     uint64_t g = (uint64_t)(uintptr_t)out;
     for (int r = 0; r < t; ++r) {
@@ -273,28 +295,29 @@ static hipError_t launch_typed(const void* const* p, int t, int64_t K, void* out
         OutT* o = static_cast<OutT*>(out);
         const int b = (int)bpc;
         switch (t) {
-        case 2: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 2>), grid, dim3(256), 0, s, pp, K, o, b); break;
-        case 4: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 4>), grid, dim3(256), 0, s, pp, K, o, b); break;
-        case 8: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 8>), grid, dim3(256), 0, s, pp, K, o, b); break;
-        default: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 16>), grid, dim3(256), 0, s, pp, K, o, b); break;
+        case 2: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 2>), grid, dim3(256), 0, s, pp, K, o, b, ro); break;
+        case 4: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 4>), grid, dim3(256), 0, s, pp, K, o, b, ro); break;
+        case 8: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 8>), grid, dim3(256), 0, s, pp, K, o, b, ro); break;
+        default: hipLaunchKernelGGL((ring_reduce_fixed_kernel<InT, OutT, 16>), grid, dim3(256), 0, s, pp, K, o, b, ro); break;
         }
     } else if ((g & 15u) == 0) {
         constexpr int UNROLL = sizeof(InT) == 2 ? 2 : 4;
         hipLaunchKernelGGL((ring_reduce_kernel<InT, OutT, UNROLL>), grid, dim3(256), 0, s, pp, t, K,
-                           static_cast<OutT*>(out), (int)bpc);
+                           static_cast<OutT*>(out), (int)bpc, ro);
     } else {
         hipLaunchKernelGGL((ring_reduce_scalar_kernel<InT, OutT>), grid, dim3(256), 0, s, pp, t, K,
-                           static_cast<OutT*>(out), (int)bpc);
+                           static_cast<OutT*>(out), (int)bpc, ro);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_ring_reduce(const void* const* parts, int t, int64_t K, tp_dtype in_dt,
-                              void* out, tp_dtype out_dt, hipStream_t s) {
+                              void* out, tp_dtype out_dt, tp_order order, hipStream_t s) {
     if (K <= 0) return hipSuccess;
-    if (in_dt == TP_BF16 && out_dt == TP_BF16) return launch_typed<uint16_t, uint16_t>(parts, t, K, out, s);
-    if (in_dt == TP_BF16 && out_dt == TP_F32) return launch_typed<uint16_t, float>(parts, t, K, out, s);
-    return launch_typed<float, float>(parts, t, K, out, s);
+    const int ro = order == TP_ORDER_RANK ? 1 : 0;
+    if (in_dt == TP_BF16 && out_dt == TP_BF16) return launch_typed<uint16_t, uint16_t>(parts, t, K, out, ro, s);
+    if (in_dt == TP_BF16 && out_dt == TP_F32) return launch_typed<uint16_t, float>(parts, t, K, out, ro, s);
+    return launch_typed<float, float>(parts, t, K, out, ro, s);
 }
 
 }  // namespace tpk

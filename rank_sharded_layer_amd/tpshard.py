@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libtpshard.so")
 
 TP_F32, TP_BF16 = 0, 1
 TP_ORDER_RING = 0
+TP_ORDER_RANK = 1
 TP_MAX_RANKS = 64
 STATUS_NAMES = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_ESHAPE", 3: "TP_EDTYPE", 4: "TP_EALIGN",
                 5: "TP_EHIP", 6: "TP_EWORKSPACE"}
@@ -57,6 +58,7 @@ _SIGS = {
     "tp_partial_reduce": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _vp, _int, _int, _vp]),
     "tp_ring_schedule": (_int, [_int, _i64, ctypes.POINTER(RingStep), _int, ctypes.POINTER(_int)]),
     "tp_sp_rows": (_int, [_i64, _int, _int, _i64p, _i64p]),
+    "tp_logits_gather_argmax": (_int, [ctypes.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _vp]),
     "tp_rs_add_rmsnorm": (_int, [ctypes.POINTER(_vp), _int, _int, _i64, _i64, _int, _vp, _vp, ctypes.c_float,
                                  _vp, _vp, _vp]),
     "tp_vocab_range": (_int, [_i64, _int, _int, _i64p, _i64p]),
@@ -287,6 +289,30 @@ def tp_ring_schedule(t, K):
     _check(lib().tp_ring_schedule(t, K, arr, n, ctypes.byref(got)))
     return [dict(phase=s.phase, step=s.step, src=s.src, dst=s.dst, chunk=s.chunk, offset=s.offset,
                  len=s.len) for s in arr[:got.value]]
+
+
+def tp_logits_gather_argmax(shards, vocab, full=None, argmax=None, want_full=True, stream=None):
+    """Concatenation of the t fp32 logits shards [n, end_r - start_r] along the
+    vocabulary ([n, vocab]) and each row's first argmax (int64).  Returns
+    (full or None, argmax)."""
+    t = len(shards)
+    if t < 1:
+        raise TPError(1, "no shards")
+    n = shards[0].shape[0]
+    dev = shards[0].device
+    ptrs = []
+    for r, sh in enumerate(shards):
+        s, e = tp_vocab_range(vocab, r, t)
+        ptrs.append(_dev(sh, f"shards[{r}]", torch.float32, (n, e - s)).value if e > s else None)
+    arr = (ctypes.c_void_p * t)(*ptrs)
+    if want_full and full is None:
+        full = torch.empty((n, vocab), dtype=torch.float32, device=dev)
+    pf = _dev(full, "full", torch.float32, (n, vocab)) if full is not None else None
+    if argmax is None:
+        argmax = torch.empty((n,), dtype=torch.int64, device=dev)
+    pa = _dev(argmax, "argmax", torch.int64, (n,))
+    _check(lib().tp_logits_gather_argmax(arr, t, n, vocab, _dt(torch.float32), pf, pa, _stream(stream)))
+    return full, argmax
 
 
 # ---- sequence-parallel epilogue -------------------------------------------------

@@ -234,3 +234,25 @@ def test_llama70b_prefill_tp8_sequence_parallel_epilogue_sampled():
     assert np.array_equal(bits(ro[rows]), oracle.f32_to_bf16_bits(exp_ro))
     g = f64_bits(bits(out[rows]), torch.bfloat16)
     assert np.all(np.abs(g - exp_out) <= 2.0 ** -7 * np.abs(exp_out) + 1e-30)
+
+
+def test_qwen3_vocab_tp2_logits_gather_argmax():
+    """The LM head of both ranks, then the gather and greedy pick, against
+    the oracle's full logits X.E^T (fp64) and its first-maximum rule on the
+    GPU's own fp32 logits."""
+    w = synth.get("qwen3_vocab_tp2")
+    V, t, n, h = w.vocab, w.tp, w.n, w.h
+    table = gen(w, synth.T_TABLE, (V, h), 0.02)
+    x = gen(w, synth.T_X, (n, h), 1.0)
+    shards = []
+    for r in range(t):
+        s, e = T.tp_vocab_range(V, r, t)
+        shards.append(T.tp_lm_head_rank(x, table[s:e].contiguous(), out_dtype=torch.float32))
+    full, am = T.tp_logits_gather_argmax(shards, V)
+    torch.cuda.synchronize()
+    exp_full, exp_am = oracle.logits_gather_argmax([f64_bits(bits(sh), torch.float32) for sh in shards], V)
+    assert np.array_equal(bits(full), exp_full.astype(np.float32).view(np.uint32))
+    assert am.cpu().tolist() == exp_am.tolist()
+    rows = synth.sample_rows(n, 8, w.seed(82))
+    ref = oracle.linear(f64_bits(bits(x[rows]), torch.bfloat16), f64_bits(bits(table), torch.bfloat16))
+    assert relf(to_f64(full[rows]), ref) <= TOL[torch.bfloat16]

@@ -614,3 +614,89 @@ def test_rs_add_rmsnorm_order_and_rounding_pins_on_gpu():
         res = torch.full((1, 8), 2.0 ** -16, device=DEV, dtype=torch.bfloat16)
         ro, _ = T.tp_rs_add_rmsnorm(P, r, res, wb, 1e-5)
         assert ro.float().tolist() == [[1.0 + 2.0 ** -7] * 8]
+
+
+# --------------------------------------------------------------------------
+# one-shot (rank-order) reduce: bit-exact against the oracle's zero-started
+# fp32 rank-order sum, rounded once
+# --------------------------------------------------------------------------
+
+def oracle_rank_bits(parts, out_dtype):
+    f32 = [to_f64(p).astype(np.float32) for p in parts]
+    s = oracle.reduce_rank_f32(f32)
+    return oracle.f32_to_bf16_bits(s) if out_dtype == torch.bfloat16 else s.view(np.uint32)
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [(torch.bfloat16, torch.bfloat16), (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.float32)])
+@pytest.mark.parametrize("t", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("K", [1, 7, 8 * 1000 + 5, 1_000_003])
+def test_partial_reduce_rank_order_bit_exact(in_dt, out_dt, t, K):
+    parts = [rnd((K,), 1.0, 700 + 31 * r + K % 97, in_dt) for r in range(t)]
+    got = T.tp_partial_reduce(parts, out_dtype=out_dt, order=T.TP_ORDER_RANK)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), oracle_rank_bits(parts, out_dt))
+
+
+def test_partial_reduce_rank_order_pins_on_gpu():
+    e = 2.0 ** -24
+    P0 = torch.tensor([e, 1.0, e], device=DEV)
+    P1 = torch.tensor([1.0, e, e], device=DEV)
+    P2 = torch.tensor([e, e, 1.0], device=DEV)
+    assert T.tp_partial_reduce([P0, P1, P2], order=T.TP_ORDER_RANK).tolist() == [1.0, 1.0, 1.0 + 2.0 ** -23]
+    assert T.tp_partial_reduce([P0, P1, P2]).tolist() == [1.0, 1.0 + 2.0 ** -23, 1.0]
+    nz = [torch.full((4099,), -0.0, device=DEV) for _ in range(4)]
+    r = T.tp_partial_reduce(nz, order=T.TP_ORDER_RANK)
+    assert not torch.signbit(r).any()                    # 0 + (-0) = +0
+    assert torch.signbit(T.tp_partial_reduce(nz)).all()  # the ring has no zero start
+
+
+def test_partial_reduce_rank_order_unaligned():
+    t, K = 3, 4099
+    bufs = [rnd((K + 1,), 1.0, 720 + r, torch.bfloat16) for r in range(t)]
+    parts = [b[1:] for b in bufs]
+    got = T.tp_partial_reduce(parts, order=T.TP_ORDER_RANK)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), oracle_rank_bits(parts, torch.bfloat16))
+
+
+# --------------------------------------------------------------------------
+# vocab logits gather + greedy argmax: full logits bit-exact (a copy), argmax
+# exact against the oracle's first-maximum rule
+# --------------------------------------------------------------------------
+
+def gather_check(shards, vocab, full, am):
+    exp_full, exp_am = oracle.logits_gather_argmax([to_f64(s) for s in shards], vocab)
+    if full is not None:
+        assert np.array_equal(bits(full), exp_full.astype(np.float32).view(np.uint32))
+    assert am.cpu().tolist() == exp_am.tolist()
+
+
+@pytest.mark.parametrize("V,t,n", [(10, 3, 5), (11, 4, 3), (7, 8, 2), (4096, 4, 9), (151936, 2, 17), (1000, 3, 4)])
+def test_logits_gather_argmax_matches_oracle(V, t, n):
+    """Ragged shard widths (10 = 4 + 4 + 2; 11 = 3 + 3 + 3 + 2; 7 over 8
+    ranks leaves the last empty; 1000 = 334 + 334 + 332 takes the element-wise
+    path); values drawn from a few levels so that ties are common."""
+    shards = []
+    for r in range(t):
+        s, e = T.tp_vocab_range(V, r, t)
+        g = torch.Generator(device="cpu").manual_seed(800 + r + V)
+        shards.append(torch.randint(-3, 4, (n, e - s), generator=g).float().to(DEV) if e > s
+                      else torch.empty((n, 0), device=DEV))
+    full, am = T.tp_logits_gather_argmax(shards, V)
+    torch.cuda.synchronize()
+    gather_check(shards, V, full, am)
+    _, am2 = T.tp_logits_gather_argmax(shards, V, want_full=False)
+    assert torch.equal(am, am2)
+
+
+def test_logits_gather_argmax_nan_and_signed_zero():
+    V, t, n = 12, 3, 3
+    rows = torch.tensor([[0.0, -0.0, 0.0, -1.0, 0.0, 0.0, -0.0, 0.0, -5.0, 0.0, 0.0, 0.0],
+                         [1.0, 2.0, 3.0, float("nan"), 9.0, float("nan"), 1.0, 1.0, 1.0, 1.0, 1.0, 1.0],
+                         [-3.0] * 11 + [-2.0]], device=DEV)
+    shards = [rows[:, 4 * r:4 * r + 4].contiguous() for r in range(t)]
+    full, am = T.tp_logits_gather_argmax(shards, V)
+    torch.cuda.synchronize()
+    assert am.tolist() == torch.argmax(rows.cpu(), dim=1).tolist() == [0, 3, 11]
+    gather_check(shards, V, full, am)
