@@ -218,12 +218,20 @@ def leg_reduce(name, reps):
         T.tp_partial_reduce(parts, out=y)
         if i >= 2:
             tm.stop("reduce")
+    for i in range(2 + reps):
+        if i >= 2:
+            tm.start("rank")
+        T.tp_partial_reduce(parts, out=y, order=T.TP_ORDER_RANK)
+        if i >= 2:
+            tm.stop("rank")
     torch.cuda.synchronize()
     b = (w.tp + 1) * w.n * w.h * 2
     ms = tm.ms("reduce")
+    msr = tm.ms("rank")
     del parts
     return {"workload": name, "t": w.tp, "K": w.n * w.h, "ms": ms, "GBps": b / ms / 1e6,
-            "hbm_frac": b / ms / 1e6 / PEAK_HBM_GBPS, "algorithmic_bytes": b}
+            "hbm_frac": b / ms / 1e6 / PEAK_HBM_GBPS, "algorithmic_bytes": b,
+            "rank_order_ms": msr, "rank_order_hbm_frac": b / msr / 1e6 / PEAK_HBM_GBPS}
 
 
 def leg_spnorm(reps):
@@ -299,10 +307,31 @@ def leg_vocab(reps):
     fl = 2.0 * w.n * w.h * v_local
     by = v_local * w.h * 2 + w.n * w.h * 2 + w.n * v_local * 4
     ms = tm.ms("lm_head")
+    # gather of both ranks' logits into [n, V] and the greedy pick
+    rank_logits = [T.tp_lm_head_rank(xemb, shards[r]) for r in range(w.tp)]
+    full = torch.empty((w.n, w.vocab), dtype=torch.float32, device=DEV)
+    am = torch.empty((w.n,), dtype=torch.int64, device=DEV)
+    tg = EventTimer()
+    for i in range(2 + reps):
+        if i >= 2:
+            tg.start("gather")
+        T.tp_logits_gather_argmax(rank_logits, w.vocab, full=full, argmax=am)
+        if i >= 2:
+            tg.stop("gather")
+            tg.start("argmax")
+        T.tp_logits_gather_argmax(rank_logits, w.vocab, argmax=am, want_full=False)
+        if i >= 2:
+            tg.stop("argmax")
+    torch.cuda.synchronize()
+    gb = w.n * w.vocab * 4
     return {"workload": w.name, "embed_ms_all_ranks": tm.ms("embed"), "reduce_ms": tm.ms("reduce"),
             "lm_head_ms": ms, "lm_head_TFLOPs": fl / ms / 1e9, "lm_head_GBps": by / ms / 1e6,
             "lm_head_hbm_frac": by / ms / 1e6 / PEAK_HBM_GBPS,
-            "lm_head_mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+            "lm_head_mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "gather_argmax_ms": tg.ms("gather"), "gather_argmax_GBps": 2 * gb / tg.ms("gather") / 1e6,
+            "gather_argmax_hbm_frac": 2 * gb / tg.ms("gather") / 1e6 / PEAK_HBM_GBPS,
+            "argmax_only_ms": tg.ms("argmax"), "argmax_only_GBps": gb / tg.ms("argmax") / 1e6,
+            "argmax_only_hbm_frac": gb / tg.ms("argmax") / 1e6 / PEAK_HBM_GBPS}
 
 
 def leg_attnproj(reps):

@@ -10,10 +10,11 @@
 // argmax of the logits: the first column holding the maximum, a NaN counting
 // as larger than every number (the rule of the torch.argmax it calls).
 //
-// One workgroup per token row.  Thread k scans columns k, k + 256, ... of
-// each shard in column order (16-byte vectors where the shard width and the
-// buffers allow), copies them to the full row when asked, and keeps the first
-// best (value, column) it sees; the 256 candidates then meet in a fixed tree
+// One workgroup of 1024 threads per token row.  Thread k scans 16-byte
+// vectors k, k + 1024, ... of each shard in column order (4 loads in flight;
+// element-wise where the shard width or the buffers do not allow vectors),
+// copies them to the full row when asked, and keeps the first best
+// (value, column) it sees; the 1024 candidates then meet in a fixed tree
 // whose combine rule (NaN first, then the larger value, ties to the smaller
 // column) is associative and commutative, so the result is the row's first
 // maximum whatever the tree.  Deterministic.
@@ -57,12 +58,15 @@ __device__ __forceinline__ void offer(Best& b, float v, int64_t col) {
     }
 }
 
+constexpr int GB = 1024;     // threads per row
+constexpr int GU = 4;        // 16-byte loads per thread in flight
+
 template <bool VEC>
-__global__ __launch_bounds__(256) void logits_gather_argmax_kernel(ShardPtrs shards, int t, int64_t vocab,
-                                                                  int64_t per, float* __restrict__ full,
-                                                                  int64_t* __restrict__ argmax) {
-    __shared__ float sv[256];
-    __shared__ int64_t si[256];
+__global__ __launch_bounds__(GB) void logits_gather_argmax_kernel(ShardPtrs shards, int t, int64_t vocab,
+                                                                 int64_t per, float* __restrict__ full,
+                                                                 int64_t* __restrict__ argmax) {
+    __shared__ float sv[GB];
+    __shared__ int64_t si[GB];
     const int64_t row = blockIdx.x;
     Best b{0.0f, -1};
     for (int r = 0; r < t; ++r) {
@@ -74,10 +78,29 @@ __global__ __launch_bounds__(256) void logits_gather_argmax_kernel(ShardPtrs sha
         const float* src = shards.p[r] + row * w;
         float* dst = full ? full + row * vocab + start : nullptr;
         if (VEC) {
+            // GU independent vectors per thread per pass (columns still
+            // increase per thread, so offer() keeps the first maximum)
+            const f32x4v* s4 = reinterpret_cast<const f32x4v*>(src);
+            f32x4v* d4 = reinterpret_cast<f32x4v*>(dst);
             const int64_t nv = w / 4;
-            for (int64_t v = threadIdx.x; v < nv; v += 256) {
-                const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src) + v);
-                if (dst) __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(dst) + v);
+            int64_t v = threadIdx.x;
+            for (; v + (GU - 1) * GB < nv; v += GU * GB) {
+                f32x4v x[GU];
+#pragma unroll
+                for (int u = 0; u < GU; ++u) x[u] = __builtin_nontemporal_load(s4 + v + u * GB);
+#pragma unroll
+                for (int u = 0; u < GU; ++u) {
+                    if (dst) __builtin_nontemporal_store(x[u], d4 + v + u * GB);
+                    const int64_t c = start + (v + u * GB) * 4;
+                    offer(b, x[u].x, c);
+                    offer(b, x[u].y, c + 1);
+                    offer(b, x[u].z, c + 2);
+                    offer(b, x[u].w, c + 3);
+                }
+            }
+            for (; v < nv; v += GB) {
+                const f32x4v x = __builtin_nontemporal_load(s4 + v);
+                if (dst) __builtin_nontemporal_store(x, d4 + v);
                 const int64_t c = start + v * 4;
                 offer(b, x.x, c);
                 offer(b, x.y, c + 1);
@@ -85,7 +108,7 @@ __global__ __launch_bounds__(256) void logits_gather_argmax_kernel(ShardPtrs sha
                 offer(b, x.w, c + 3);
             }
         } else {
-            for (int64_t j = threadIdx.x; j < w; j += 256) {
+            for (int64_t j = threadIdx.x; j < w; j += GB) {
                 const float x = src[j];
                 if (dst) dst[j] = x;
                 offer(b, x, start + j);
@@ -95,7 +118,7 @@ __global__ __launch_bounds__(256) void logits_gather_argmax_kernel(ShardPtrs sha
     sv[threadIdx.x] = b.v;
     si[threadIdx.x] = b.i;
     __syncthreads();
-    for (int s = 128; s >= 1; s >>= 1) {
+    for (int s = GB / 2; s >= 1; s >>= 1) {
         if ((int)threadIdx.x < s) {
             const Best o{sv[threadIdx.x + s], si[threadIdx.x + s]};
             const Best m{sv[threadIdx.x], si[threadIdx.x]};
@@ -130,10 +153,10 @@ hipError_t launch_logits_gather_argmax(const void* const* shards, int t, int64_t
     if ((g & 15u) != 0 || (full && vocab % 4 != 0)) vec = false;
     float* f = static_cast<float*>(full);
     if (vec)
-        hipLaunchKernelGGL((logits_gather_argmax_kernel<true>), dim3((unsigned)n), dim3(256), 0, s, sp, t, vocab, per,
+        hipLaunchKernelGGL((logits_gather_argmax_kernel<true>), dim3((unsigned)n), dim3(GB), 0, s, sp, t, vocab, per,
                            f, argmax);
     else
-        hipLaunchKernelGGL((logits_gather_argmax_kernel<false>), dim3((unsigned)n), dim3(256), 0, s, sp, t, vocab,
+        hipLaunchKernelGGL((logits_gather_argmax_kernel<false>), dim3((unsigned)n), dim3(GB), 0, s, sp, t, vocab,
                            per, f, argmax);
     return hipGetLastError();
 }
