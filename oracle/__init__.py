@@ -73,6 +73,7 @@ def _load():
         "orc_ring_traffic": (_int, [_int, _i64, _i64p, _i64p, ctypes.POINTER(ctypes.c_int)]),
         "orc_sp_rows": (None, [_i64, _int, _int, _i64p, _i64p]),
         "orc_reduce_rank_f32": (None, [ctypes.POINTER(_f32p), _int, _i64, _f32p]),
+        "orc_attention_rank": (_int, [_f64p, _i64, _int, _int, _int, _int, _i64p, _i64, _f64p]),
         "orc_logits_gather_argmax": (_int, [ctypes.POINTER(_f64p), _int, _i64, _i64, _f64p, _i64p]),
         "orc_rs_add_rmsnorm": (_int, [ctypes.POINTER(_f32p), _int, _int, _i64, _i64, _f32p, _f64p,
                                       ctypes.c_double, _int, _f32p, _f64p]),
@@ -375,3 +376,19 @@ def logits_gather_argmax(shards, vocab):
     _check(_load().orc_logits_gather_argmax(arr, t, n, vocab, _p(full, _f64p), _p(am, _i64p)),
            "logits_gather_argmax")
     return full, am
+
+
+# --- head-parallel attention core -------------------------------------------------
+
+def attention_rank(qkv, nq, nkv, head_dim, causal, rows=None) -> np.ndarray:
+    """softmax(q k^T / sqrt(d) [causal mask]) v for the rank's nq query heads
+    over its nkv KV heads (GQA), from the packed QKV projection output
+    [n, (nq + 2 nkv) d]; rows: query rows to compute (default all)."""
+    qkv = _f64(qkv)
+    n = qkv.shape[0]
+    assert qkv.shape[1] == (nq + 2 * nkv) * head_dim
+    rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, nq * head_dim), dtype=np.float64)
+    _check(_load().orc_attention_rank(_p(qkv, _f64p), n, nq, nkv, head_dim, 1 if causal else 0,
+                                      _p(rows, _i64p), rows.size, _p(out, _f64p)), "attention_rank")
+    return out

@@ -495,6 +495,66 @@ ORC_API void orc_reduce_sum_f64(const double* const* parts, int t, int64_t K, do
     }
 }
 
+/* Head-parallel attention core of one rank ([VLLM13] §2.3.3: each rank runs
+ * self-attention on its own heads, scores = q k^T / sqrt(head_dim), a
+ * max-subtracted softmax along the keys, then probs . v; [SCRATCH]
+ * TPAttention.forward: the rank's nq query heads share its nkv KV heads by
+ * repeat_interleave, so query head j reads KV head j / (nq / nkv), under the
+ * causal mask tril(ones(T, S)) when causal).  RoPE and the q/k norms come
+ * before this step and are not part of it.
+ *   qkv: [n, (nq + 2 nkv) d] fp64, the rank's QKV projection output (q heads,
+ *   then k heads, then v heads, d columns each); rows: the query rows to
+ *   compute (every step is independent per query row); out: [n_rows, nq d].
+ * Returns 0, or 1 for bad arguments, 4 if out of memory. */
+ORC_API int orc_attention_rank(const double* qkv, int64_t n, int nq, int nkv, int d, int causal,
+                               const int64_t* rows, int64_t n_rows, double* out) {
+    if (n < 1 || nq < 1 || nkv < 1 || nq % nkv != 0 || d < 1) return 1;
+    const int64_t ld = (int64_t)(nq + 2 * nkv) * d;
+    const int rep = nq / nkv;
+    const double scale = 1.0 / sqrt((double)d);
+    int rc = 0;
+#pragma omp parallel
+    {
+        double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+        if (!sc) {
+#pragma omp atomic write
+            rc = 4;
+        } else {
+#pragma omp for schedule(dynamic, 1) collapse(2)
+            for (int64_t ri = 0; ri < n_rows; ++ri) {
+                for (int h = 0; h < nq; ++h) {
+                    const int64_t i = rows[ri];
+                    const int g = h / rep;
+                    const double* q = qkv + i * ld + (int64_t)h * d;
+                    const int64_t S = causal ? i + 1 : n;     /* keys 0 .. S-1 */
+                    double mx = -INFINITY;
+                    for (int64_t s = 0; s < S; ++s) {
+                        const double* k = qkv + s * ld + (int64_t)(nq + g) * d;
+                        double dot = 0.0;
+                        for (int e = 0; e < d; ++e) dot += q[e] * k[e];
+                        sc[s] = dot * scale;
+                        if (sc[s] > mx) mx = sc[s];
+                    }
+                    double sum = 0.0;
+                    for (int64_t s = 0; s < S; ++s) {
+                        sc[s] = exp(sc[s] - mx);
+                        sum += sc[s];
+                    }
+                    double* o = out + ri * (int64_t)nq * d + (int64_t)h * d;
+                    for (int e = 0; e < d; ++e) o[e] = 0.0;
+                    for (int64_t s = 0; s < S; ++s) {
+                        const double* v = qkv + s * ld + (int64_t)(nq + nkv + g) * d;
+                        const double p = sc[s] / sum;
+                        for (int e = 0; e < d; ++e) o[e] += p * v[e];
+                    }
+                }
+            }
+            free(sc);
+        }
+    }
+    return rc;
+}
+
 /* One-shot all-reduce: every rank reads all ranks' buffers and adds them,
  * in rank order, into an accumulator that starts at zero ([VLLM13] §1.2,
  * the low-latency all-reduce pseudocode: out = zeros_like(x), then

@@ -701,3 +701,81 @@ def test_argmax_ties_take_the_first_index_and_nan_wins():
     full = torch.tensor([[1.0, 5.0, 2.0, 5.0, 0.0, 5.0, -1.0], [1.0, 2.0, 3.0, 9.0, float("nan"), 10.0, float("nan")],
                          [-3.0, -2.0, -2.0, -7.0, -2.5, -9.0, -2.0]], dtype=torch.float64)
     assert torch.argmax(full, dim=1).tolist() == [1, 4, 1]
+
+
+# --------------------------------------------------------------------------
+# head-parallel attention core
+# --------------------------------------------------------------------------
+
+def _sdpa64(qkv, nq, nkv, d, causal):
+    n = qkv.shape[0]
+    t = torch.from_numpy(qkv)
+    q = t[:, :nq * d].reshape(n, nq, d).transpose(0, 1)
+    k = t[:, nq * d:(nq + nkv) * d].reshape(n, nkv, d).transpose(0, 1).repeat_interleave(nq // nkv, 0)
+    v = t[:, (nq + nkv) * d:].reshape(n, nkv, d).transpose(0, 1).repeat_interleave(nq // nkv, 0)
+    mask = torch.ones(n, n, dtype=torch.bool).tril() if causal else None
+    return F.scaled_dot_product_attention(q, k, v, attn_mask=mask).transpose(0, 1).reshape(n, nq * d).numpy()
+
+
+@pytest.mark.parametrize("nq,nkv", [(4, 4), (4, 2), (4, 1), (8, 2)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_matches_torch_sdpa(nq, nkv, causal):
+    """The library routine the pages' TP attention calls, in float64, with
+    the KV heads repeated for GQA and the causal tril mask."""
+    rng = np.random.default_rng(nq * 10 + nkv + causal)
+    n, d = 23, 16
+    qkv = rng.standard_normal((n, (nq + 2 * nkv) * d))
+    got = oracle.attention_rank(qkv, nq, nkv, d, causal)
+    assert np.allclose(got, _sdpa64(qkv, nq, nkv, d, causal), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_closed_forms():
+    n, nq, nkv, d = 6, 2, 1, 4
+    rng = np.random.default_rng(3)
+    qkv = rng.standard_normal((n, (nq + 2 * nkv) * d))
+    # identical keys: uniform weights, so each query averages the visible V rows
+    qkv[:, nq * d:(nq + nkv) * d] = qkv[0, nq * d:(nq + nkv) * d]
+    V = qkv[:, (nq + nkv) * d:]
+    causal = oracle.attention_rank(qkv, nq, nkv, d, True)
+    full = oracle.attention_rank(qkv, nq, nkv, d, False)
+    for i in range(n):
+        for h in range(nq):
+            assert np.allclose(causal[i, h * d:(h + 1) * d], V[:i + 1].mean(axis=0), rtol=1e-14, atol=1e-14)
+            assert np.allclose(full[i, h * d:(h + 1) * d], V.mean(axis=0), rtol=1e-14, atol=1e-14)
+    # the first query sees only key 0: its output is V[0] exactly
+    qkv2 = rng.standard_normal((n, (nq + 2 * nkv) * d))
+    out = oracle.attention_rank(qkv2, nq, nkv, d, True)
+    assert np.array_equal(out[0, :d], qkv2[0, (nq + nkv) * d:])
+    # one dominant key: the output is (to fp64 rounding) that key's V row
+    qkv3 = np.zeros((n, (nq + 2 * nkv) * d))
+    qkv3[:, 0] = 1.0                                   # query head 0: e_0
+    qkv3[4, nq * d] = 200.0                            # key 4 along e_0
+    qkv3[:, (nq + nkv) * d:] = np.arange(n)[:, None]
+    out3 = oracle.attention_rank(qkv3, nq, nkv, d, False)
+    assert np.allclose(out3[:, :d], 4.0, rtol=0, atol=1e-12)
+
+
+def test_attention_head_parallel_ranks_concatenate_to_full():
+    """[VLLM13] §2.3.3: each rank computes attention for its own heads with no
+    communication; the ranks' outputs side by side are the full output."""
+    rng = np.random.default_rng(11)
+    n, nq, nkv, d, t = 17, 8, 4, 8, 2
+    qkv = rng.standard_normal((n, (nq + 2 * nkv) * d))
+    full = oracle.attention_rank(qkv, nq, nkv, d, True)
+    q, k, v = qkv[:, :nq * d], qkv[:, nq * d:(nq + nkv) * d], qkv[:, (nq + nkv) * d:]
+    lq, lk = nq // t, nkv // t
+    parts = []
+    for r in range(t):
+        sub = np.concatenate([q[:, r * lq * d:(r + 1) * lq * d], k[:, r * lk * d:(r + 1) * lk * d],
+                              v[:, r * lk * d:(r + 1) * lk * d]], axis=1)
+        parts.append(oracle.attention_rank(sub, lq, lk, d, True))
+    assert np.allclose(np.concatenate(parts, axis=1), full, rtol=1e-13, atol=1e-14)
+
+
+def test_attention_rows_are_independent():
+    rng = np.random.default_rng(12)
+    n, nq, nkv, d = 19, 4, 1, 8
+    qkv = rng.standard_normal((n, (nq + 2 * nkv) * d))
+    full = oracle.attention_rank(qkv, nq, nkv, d, True)
+    rows = [18, 0, 7]
+    assert np.array_equal(oracle.attention_rank(qkv, nq, nkv, d, True, rows=rows), full[rows])
