@@ -235,6 +235,24 @@ TP_API tp_status tp_rs_add_rmsnorm(const void* const* partials /*HOST array*/, i
                                    int64_t h, tp_dtype dt, const void* residual, const void* weight, float eps,
                                    void* residual_out, void* out, void* stream);
 
+/* ---- head-parallel attention core ----------------------------------------- */
+
+/* The rank's share of self-attention, between its QKV projection and its
+ * o_proj ([VLLM13] §2.3.3: each rank runs attention on its own heads with no
+ * communication; [SCRATCH] TPAttention.forward: the rank's query heads share
+ * its KV heads by repeat_interleave, under a causal mask):
+ *   out[i, h] = sum_s softmax_s(q[i,h] . k[s,g] / sqrt(d)) v[s,g],
+ *   g = h / (nq / nkv), keys s <= i when causal, all n keys otherwise.
+ * RoPE and the q/k norms come before this step.  fp32 softmax and
+ * accumulation; the probabilities are rounded to bf16 for the product with
+ * v; out is rounded once to bf16.
+ *   qkv [n, (nq + 2 nkv) head_dim] bf16: the QKV projection output of the
+ *   rank (q heads, then k heads, then v heads), 16-byte aligned;
+ *   out [n, nq head_dim] bf16, 16-byte aligned, must not overlap qkv.
+ *   head_dim must be 128; nkv divides nq; dt must be TP_BF16. */
+TP_API tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int head_dim, tp_dtype dt,
+                                   int causal, void* out, void* stream);
+
 /* ---- vocab-parallel embedding and LM head -------------------------------- */
 
 /* HOST-only.  Rank r's vocab range: per = ceil(V/t), start = r per,

@@ -285,6 +285,24 @@ tp_status tp_partial_reduce(const void* const* partials, int t, int64_t K, tp_dt
                       "tp_partial_reduce");
 }
 
+tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int head_dim, tp_dtype dt, int causal,
+                            void* out, void* stream) {
+    if (!qkv || !out) return fail(TP_EINVAL, "tp_attention_rank: null pointer");
+    if (dt != TP_BF16) return fail(TP_EDTYPE, "tp_attention_rank: bf16 only");
+    if (head_dim != 128) return fail(TP_EINVAL, "tp_attention_rank: head_dim %d (128 supported)", head_dim);
+    if (nq < 1 || nkv < 1 || nq > 4096 || nkv > 4096) return fail(TP_EINVAL, "tp_attention_rank: bad head counts");
+    if (nq % nkv != 0) return fail(TP_ESHAPE, "tp_attention_rank: nkv %d does not divide nq %d", nkv, nq);
+    if (n < 0 || n > INT32_MAX / 2 || n * (int64_t)(nq + 2 * nkv) * head_dim > kMaxElems)
+        return fail(TP_EINVAL, "tp_attention_rank: n out of range");
+    if ((((uintptr_t)qkv) | ((uintptr_t)out)) & 15u)
+        return fail(TP_EINVAL, "tp_attention_rank: qkv and out must be 16-byte aligned");
+    const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)(n * (int64_t)(nq + 2 * nkv) * head_dim * 2);
+    const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)(n * (int64_t)nq * head_dim * 2);
+    if (n > 0 && o0 < q1 && q0 < o1) return fail(TP_EINVAL, "tp_attention_rank: out overlaps qkv");
+    return hip_status(tpk::launch_attention(qkv, n, nq, nkv, head_dim, causal, out, as_stream(stream)),
+                      "tp_attention_rank");
+}
+
 tp_status tp_logits_gather_argmax(const void* const* shards, int t, int64_t n, int64_t vocab, tp_dtype dt, void* full,
                                   int64_t* argmax, void* stream) {
     if (!shards || (!full && !argmax)) return fail(TP_EINVAL, "tp_logits_gather_argmax: null pointer");

@@ -1,0 +1,265 @@
+// Head-parallel attention core of one rank ("vLLM source analysis 13"
+// §2.3.3: each rank runs self-attention on its own heads; "Tensor
+// parallelism: implemented from scratch", TPAttention.forward: the rank's
+// query heads share its KV heads by repeat_interleave, under a causal mask):
+//   out[i, h] = softmax_s(q_i,h . k_s,g / sqrt(d) [s <= i if causal]) . v_s,g,
+//   g = h / (nq / nkv), d = 128.
+// The input is the rank's packed QKV projection output [n, (nq + 2 nkv) d]
+// (q heads, then k heads, then v heads); the output [n, nq d] is the
+// row-parallel o_proj's input.  bf16 in and out, fp32 softmax and
+// accumulation, probabilities rounded to bf16 for the P.V product.
+//
+// Design (flash-attention order, one pass over the keys):
+//   * workgroup = 4 waves = up to 4 query heads of one KV group on the same
+//     32 queries; the 64-key K and V blocks are staged once in LDS and read
+//     by all four;
+//   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
+//     keys as rows, queries as columns), so a lane owns one query and 32 of
+//     the block's 64 scores: the running max and sum need one exchange with
+//     the partner lane (l ^ 32) per block;
+//   * O^T = V^T P^T: the probabilities are the B operand straight from the
+//     score accumulators -- the 16 keys of a K step are taken in the order
+//     the accumulator holds them (keys 4h..4h+3 and 8+4h..8+4h+3 of each 16
+//     for lane half h), and V^T is read in the same order;
+//   * K in LDS is row-major with 16-byte chunk c of key r at c ^ (r & 15)
+//     (conflict-free fragment reads); V is stored transposed [d][key] with
+//     136-byte rows (conflict-free 8-byte fragment reads);
+//   * the next block's K and V are loaded into registers while the current
+//     one is multiplied;
+//   * causal: a tile stops at its last query's block, the diagonal block is
+//     masked, and tiles are dispatched heaviest first.
+#include "common.hpp"
+
+namespace tpk {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int AD = 128;          // head_dim
+constexpr int AQ = 32;           // queries per tile
+constexpr int AK = 64;           // keys per block
+constexpr int VT_LD = AK + 4;    // V^T row: 64 keys + 4 pad (136 bytes)
+
+struct AttnArgs {
+    const uint16_t* qkv;
+    uint16_t* out;
+    int64_t n;
+    int64_t ld;                  // qkv row length (elements)
+    int nq, nkv, rep, causal;
+    int ntiles;
+    float scale_log2;            // log2(e) / sqrt(d)
+};
+
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t ks[AK * AD];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[AD * VT_LD];
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int tile = a.causal ? a.ntiles - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int g = blockIdx.y;
+    const int hsub = blockIdx.z * 4 + wid;            // head within the group
+    const bool active = hsub < a.rep;
+    const int head = g * a.rep + (active ? hsub : 0);
+    const int64_t q0 = (int64_t)tile * AQ;
+    const int r = lane & 31, hh = lane >> 5;
+    const int64_t qi = q0 + r;                        // this lane's query
+
+    // Q fragments (B operand): query qi, d = 16 s + 8 hh .. + 8
+    bf16x8 qf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (qi < a.n) v = *reinterpret_cast<const u32x4*>(a.qkv + qi * a.ld + (int64_t)head * AD + 16 * s + 8 * hh);
+        qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+
+    // key range
+    int nb = (int)((a.n + AK - 1) / AK);
+    if (a.causal) {
+        int64_t last = q0 + AQ - 1;
+        if (last > a.n - 1) last = a.n - 1;
+        nb = (int)(last / AK) + 1;
+    }
+    const uint16_t* kbase = a.qkv + (int64_t)(a.nq + g) * AD;
+    const uint16_t* vbase = a.qkv + (int64_t)(a.nq + a.nkv + g) * AD;
+
+    // staging: K items (key, chunk) = tid + 256 i; V items (key pair, chunk) = tid + 256 i
+    u32x4 kreg[4], vreg[2][2];
+    auto load_block = [&](int kb) {
+        const int64_t k0 = (int64_t)kb * AK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, key = idx >> 4, c = idx & 15;
+            kreg[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (k0 + key < a.n) kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (k0 + key) * a.ld + 8 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, kp = idx & 31, c = idx >> 5;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int64_t key = k0 + 2 * kp + e;
+                vreg[i][e] = (u32x4){0u, 0u, 0u, 0u};
+                if (key < a.n) vreg[i][e] = *reinterpret_cast<const u32x4*>(vbase + key * a.ld + 8 * c);
+            }
+        }
+    };
+    auto store_block = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, key = idx >> 4, c = idx & 15;
+            *reinterpret_cast<u32x4*>(ks + key * AD + ((c ^ (key & 15)) * 8)) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, kp = idx & 31, c = idx >> 5;
+            const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
+            const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // d = 8 c + e: (V[2kp][d], V[2kp+1][d]) as one 32-bit word
+                const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
+                const uint32_t hi = (e & 1) ? (w1[e >> 1] & 0xffff0000u) : (w1[e >> 1] << 16);
+                *reinterpret_cast<uint32_t*>(vt + (8 * c + e) * VT_LD + 2 * kp) = lo | hi;
+            }
+        }
+    };
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) oacc[t][q] = 0.0f;
+    float m = -INFINITY, lsum = 0.0f;
+
+    load_block(0);
+    for (int kb = 0; kb < nb; ++kb) {
+        store_block();
+        __syncthreads();
+        if (kb + 1 < nb) load_block(kb + 1);
+        if (active) {
+            // S^T = K Q^T for the block's two 32-key tiles
+            f32x16 sacc[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) sacc[tt][q] = 0.0f;
+                const int key = 32 * tt + r;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + key * AD + (((2 * s + hh) ^ (key & 15)) * 8));
+                    sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[tt], 0, 0, 0);
+                }
+            }
+            // scale (base-2 units), mask, running max and sum for query qi;
+            // lane half hh holds keys 8 j + 4 hh + i of each tile
+            const int64_t kbase_i = (int64_t)kb * AK;
+            const bool diag = a.causal ? (kbase_i + AK - 1 > q0) : (kbase_i + AK > a.n);
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    float v = sacc[tt][q] * a.scale_log2;
+                    if (diag) {
+                        const int64_t key = kbase_i + 32 * tt + 8 * (q >> 2) + 4 * hh + (q & 3);
+                        if ((a.causal && key > qi) || key >= a.n) v = -INFINITY;
+                    }
+                    sacc[tt][q] = v;
+                    mloc = fmaxf(mloc, v);
+                }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            const float mnew = fmaxf(m, mloc);
+            const float alpha = exp2f(m - mnew);         // 0 on the first block (m = -inf)
+            float psum = 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const float p = exp2f(sacc[tt][q] - mnew);
+                    sacc[tt][q] = p;
+                    psum += p;
+                }
+            psum += __shfl_xor(psum, 32, 64);
+            lsum = lsum * alpha + psum;
+            m = mnew;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) oacc[t][q] *= alpha;
+            // P^T fragments: K step (tt, q2) = accumulator values 8 q2 .. 8 q2 + 7
+            bf16x8 pf[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(sacc[tt][8 * q2 + 2 * e], sacc[tt][8 * q2 + 2 * e + 1]);
+                    pf[tt][q2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+                }
+            // O^T += V^T P^T: lane (d row, hh) reads keys 16 q2 + 4 hh + 0..3
+            // and 16 q2 + 8 + 4 hh + 0..3 of tile tt
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint16_t* vrow = vt + (32 * dt + r) * VT_LD;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        const int kk = 32 * tt + 16 * q2 + 4 * hh;
+                        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + kk);
+                        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + kk + 8);
+                        const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4){x0.x, x0.y, x1.x, x1.y});
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[tt][q2], oacc[dt], 0, 0, 0);
+                    }
+            }
+        }
+        __syncthreads();
+    }
+
+    // out[qi, head, d]: lane holds d = 32 dt + 8 j + 4 hh + i
+    if (active && qi < a.n) {
+        const float inv = 1.0f / lsum;
+        uint16_t* o = a.out + qi * (int64_t)a.nq * AD + (int64_t)head * AD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 32 * dt + 8 * j + 4 * hh;
+                const float v0 = oacc[dt][4 * j], v1 = oacc[dt][4 * j + 1];
+                const float v2 = oacc[dt][4 * j + 2], v3 = oacc[dt][4 * j + 3];
+                *reinterpret_cast<u32x2*>(o + d) =
+                    (u32x2){pack_bf16x2(v0 * inv, v1 * inv), pack_bf16x2(v2 * inv, v3 * inv)};
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int head_dim, int causal, void* out,
+                            hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (head_dim != AD) return hipErrorInvalidValue;
+    AttnArgs a;
+    a.qkv = static_cast<const uint16_t*>(qkv);
+    a.out = static_cast<uint16_t*>(out);
+    a.n = n;
+    a.ld = (int64_t)(nq + 2 * nkv) * AD;
+    a.nq = nq;
+    a.nkv = nkv;
+    a.rep = nq / nkv;
+    a.causal = causal ? 1 : 0;
+    a.ntiles = (int)((n + AQ - 1) / AQ);
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)AD);
+    const dim3 grid((unsigned)a.ntiles, (unsigned)nkv, (unsigned)((a.rep + 3) / 4));
+    hipLaunchKernelGGL(attention_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace tpk

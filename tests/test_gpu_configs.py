@@ -256,3 +256,19 @@ def test_qwen3_vocab_tp2_logits_gather_argmax():
     rows = synth.sample_rows(n, 8, w.seed(82))
     ref = oracle.linear(f64_bits(bits(x[rows]), torch.bfloat16), f64_bits(bits(table), torch.bfloat16))
     assert relf(to_f64(full[rows]), ref) <= TOL[torch.bfloat16]
+
+
+def test_llama70b_attnproj_tp16_attention_core_sampled():
+    """The benchmarked launch: one rank of TP=16, 4 query heads on 1 KV head,
+    8192 tokens, causal; sampled query rows (first, last, tile and block
+    edges) against the oracle."""
+    w = synth.get("llama70b_attnproj_tp16")
+    nq, nkv = w.n_q // w.tp, 1
+    qkv = gen(w, synth.T_ATTN_OUT + 50, (w.n, (nq + 2 * nkv) * w.head_dim), 1.0)
+    out = T.tp_attention_rank(qkv, nq, nkv, head_dim=w.head_dim, causal=True)
+    torch.cuda.synchronize()
+    rows = sorted(set(synth.sample_rows(w.n, 8, w.seed(83)) + [0, 31, 32, 63, 64, 4095, w.n - 1]))
+    ref = oracle.attention_rank(f64_bits(bits(qkv), torch.bfloat16), nq, nkv, w.head_dim, True, rows=rows)
+    got = f64_bits(bits(out[rows]), torch.bfloat16)
+    for h in range(nq):
+        assert relf(got[:, h * 128:(h + 1) * 128], ref[:, h * 128:(h + 1) * 128]) <= 1e-2

@@ -700,3 +700,47 @@ def test_logits_gather_argmax_nan_and_signed_zero():
     torch.cuda.synchronize()
     assert am.tolist() == torch.argmax(rows.cpu(), dim=1).tolist() == [0, 3, 11]
     gather_check(shards, V, full, am)
+
+
+# --------------------------------------------------------------------------
+# head-parallel attention core: rel-Frobenius <= 1e-2 per head against the
+# fp64 oracle (bf16 inputs, fp32 softmax, bf16 probabilities and output)
+# --------------------------------------------------------------------------
+
+def attn_check(qkv, nq, nkv, causal, out, rows=None):
+    ref = oracle.attention_rank(to_f64(qkv), nq, nkv, 128, causal, rows=rows)
+    got = to_f64(out) if rows is None else to_f64(out[rows])
+    for h in range(nq):
+        e = relf(got[:, h * 128:(h + 1) * 128], ref[:, h * 128:(h + 1) * 128])
+        assert e <= 1e-2, (h, e)
+
+
+@pytest.mark.parametrize("n,nq,nkv,causal", [(1, 4, 1, True), (31, 4, 1, True), (33, 4, 1, False), (64, 4, 2, True),
+                                             (100, 8, 2, True), (129, 4, 4, False), (200, 12, 2, True),
+                                             (257, 4, 1, False)])
+def test_attention_rank_matches_oracle(n, nq, nkv, causal):
+    """Partial query tiles and key blocks, GQA groups of 4 (one wave per
+    head), MHA (three idle waves), groups of 6 (a second head quad)."""
+    qkv = rnd((n, (nq + 2 * nkv) * 128), 1.0, 900 + n + nq, torch.bfloat16)
+    out = T.tp_attention_rank(qkv, nq, nkv, causal=causal)
+    torch.cuda.synchronize()
+    attn_check(qkv, nq, nkv, causal, out)
+    assert torch.equal(out, T.tp_attention_rank(qkv, nq, nkv, causal=causal))     # deterministic
+
+
+def test_attention_rank_peaked_and_flat_scores():
+    """Large logits (scores of several hundred: the running max must carry
+    the scale) and identical keys (uniform weights)."""
+    n, nq, nkv = 96, 4, 1
+    qkv = rnd((n, (nq + 2 * nkv) * 128), 1.0, 950, torch.bfloat16)
+    big = qkv.clone()
+    big[:, :nq * 128] *= 8.0
+    big[:, nq * 128:(nq + 1) * 128] *= 8.0
+    out = T.tp_attention_rank(big, nq, nkv, causal=True)
+    torch.cuda.synchronize()
+    attn_check(big, nq, nkv, True, out)
+    flat = qkv.clone()
+    flat[:, nq * 128:(nq + 1) * 128] = flat[0, nq * 128:(nq + 1) * 128]
+    out = T.tp_attention_rank(flat, nq, nkv, causal=False)
+    torch.cuda.synchronize()
+    attn_check(flat, nq, nkv, False, out)
