@@ -346,8 +346,9 @@ def leg_attnproj(reps):
     wqkv = T.tp_shard_qkv(wq, wk, wv, w.n_q, w.n_kv, hd, r, t)
     wo_r = T.tp_shard_weights(wo, 1, r, t)
     del wq, wk, wv, wo
-    a_r = gen(w, synth.T_ATTN_OUT + r, (w.n, w.n_q // t * hd), 1.0)
+    nq_r, nkv_r = w.n_q // t, max(w.n_kv // t, 1)
     qkv = torch.empty((w.n, wqkv.shape[0]), dtype=w.dtype, device=DEV)
+    a_r = torch.empty((w.n, nq_r * hd), dtype=w.dtype, device=DEV)
     part = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
     tm = EventTimer()
     for i in range(2 + reps):
@@ -357,6 +358,10 @@ def leg_attnproj(reps):
         T.tp_linear_rank_forward(x, wqkv, y=qkv)
         if t_:
             t_.stop("qkv")
+            t_.start("attn")
+        T.tp_attention_rank(qkv, nq_r, nkv_r, head_dim=hd, causal=True, out=a_r)
+        if t_:
+            t_.stop("attn")
             t_.start("o_proj")
         T.tp_linear_rank_forward(a_r, wo_r, y=part)
         if t_:
@@ -364,10 +369,14 @@ def leg_attnproj(reps):
     torch.cuda.synchronize()
     fq = 2.0 * w.n * w.h * wqkv.shape[0]
     fo = 2.0 * w.n * a_r.shape[1] * w.h
+    fa = 4.0 * nq_r * hd * w.n * (w.n + 1) / 2        # causal: QK^T and PV over s <= i
     return {"workload": w.name, "qkv_ms": tm.ms("qkv"), "qkv_TFLOPs": fq / tm.ms("qkv") / 1e9,
+            "attn_ms": tm.ms("attn"), "attn_TFLOPs": fa / tm.ms("attn") / 1e9,
+            "attn_mfma_frac": fa / tm.ms("attn") / 1e9 / PEAK_BF16_TFLOPS,
             "o_proj_ms": tm.ms("o_proj"), "o_proj_TFLOPs": fo / tm.ms("o_proj") / 1e9,
             "qkv_mfma_frac": fq / tm.ms("qkv") / 1e9 / PEAK_BF16_TFLOPS,
-            "o_proj_mfma_frac": fo / tm.ms("o_proj") / 1e9 / PEAK_BF16_TFLOPS}
+            "o_proj_mfma_frac": fo / tm.ms("o_proj") / 1e9 / PEAK_BF16_TFLOPS,
+            "chain": "x -> QKV projection -> attention core (causal, 4 q heads / 1 kv head) -> o_proj partial"}
 
 
 def leg_qwen_fp32(reps):

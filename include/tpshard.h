@@ -249,7 +249,8 @@ TP_API tp_status tp_rs_add_rmsnorm(const void* const* partials /*HOST array*/, i
  *   qkv [n, (nq + 2 nkv) head_dim] bf16: the QKV projection output of the
  *   rank (q heads, then k heads, then v heads), 16-byte aligned;
  *   out [n, nq head_dim] bf16, 16-byte aligned, must not overlap qkv.
- *   head_dim must be 128; nkv divides nq; dt must be TP_BF16. */
+ *   head_dim must be 128; nkv divides nq; dt must be TP_BF16; qkv under
+ *   2 GiB. */
 TP_API tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int head_dim, tp_dtype dt,
                                    int causal, void* out, void* stream);
 

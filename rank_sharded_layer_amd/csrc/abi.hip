@@ -292,8 +292,8 @@ tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int hea
     if (head_dim != 128) return fail(TP_EINVAL, "tp_attention_rank: head_dim %d (128 supported)", head_dim);
     if (nq < 1 || nkv < 1 || nq > 4096 || nkv > 4096) return fail(TP_EINVAL, "tp_attention_rank: bad head counts");
     if (nq % nkv != 0) return fail(TP_ESHAPE, "tp_attention_rank: nkv %d does not divide nq %d", nkv, nq);
-    if (n < 0 || n > INT32_MAX / 2 || n * (int64_t)(nq + 2 * nkv) * head_dim > kMaxElems)
-        return fail(TP_EINVAL, "tp_attention_rank: n out of range");
+    if (n < 0 || n * (int64_t)(nq + 2 * nkv) * head_dim * 2 >= ((int64_t)1 << 31))
+        return fail(TP_EINVAL, "tp_attention_rank: qkv must be under 2 GiB");
     if ((((uintptr_t)qkv) | ((uintptr_t)out)) & 15u)
         return fail(TP_EINVAL, "tp_attention_rank: qkv and out must be 16-byte aligned");
     const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)(n * (int64_t)(nq + 2 * nkv) * head_dim * 2);

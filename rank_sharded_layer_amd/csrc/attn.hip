@@ -38,6 +38,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats to packed bf16 with the hardware conversion (round to nearest
+// even; the values here are finite)
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
 
 constexpr int AD = 128;          // head_dim
 constexpr int AQ = 32;           // queries per tile
@@ -54,7 +64,7 @@ struct AttnArgs {
     float scale_log2;            // log2(e) / sqrt(d)
 };
 
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[AK * AD];
     __shared__ __attribute__((aligned(16))) uint16_t vt[AD * VT_LD];
     const int lane = threadIdx.x & 63;
@@ -69,14 +79,16 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     const int r = lane & 31, hh = lane >> 5;
     const int64_t qi = q0 + r;                        // this lane's query
 
+    // every load is a buffer load over [n, ld]: rows past n read as zero
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.qkv, (short)0, (int)(a.n * a.ld * 2), 0x00020000);
+    auto ld16 = [&](int64_t row, int col) -> u32x4 {
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((row * a.ld + col) * 2), 0, 0);
+    };
     // Q fragments (B operand): query qi, d = 16 s + 8 hh .. + 8
     bf16x8 qf[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (qi < a.n) v = *reinterpret_cast<const u32x4*>(a.qkv + qi * a.ld + (int64_t)head * AD + 16 * s + 8 * hh);
-        qf[s] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qi, head * AD + 16 * s + 8 * hh));
 
     // key range
     int nb = (int)((a.n + AK - 1) / AK);
@@ -85,8 +97,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
         if (last > a.n - 1) last = a.n - 1;
         nb = (int)(last / AK) + 1;
     }
-    const uint16_t* kbase = a.qkv + (int64_t)(a.nq + g) * AD;
-    const uint16_t* vbase = a.qkv + (int64_t)(a.nq + a.nkv + g) * AD;
+    const int kcol = (a.nq + g) * AD, vcol = (a.nq + a.nkv + g) * AD;
 
     // staging: K items (key, chunk) = tid + 256 i; V items (key pair, chunk) = tid + 256 i
     u32x4 kreg[4], vreg[2][2];
@@ -95,18 +106,13 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + 256 * i, key = idx >> 4, c = idx & 15;
-            kreg[i] = (u32x4){0u, 0u, 0u, 0u};
-            if (k0 + key < a.n) kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (k0 + key) * a.ld + 8 * c);
+            kreg[i] = ld16(k0 + key, kcol + 8 * c);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int idx = tid + 256 * i, kp = idx & 31, c = idx >> 5;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int64_t key = k0 + 2 * kp + e;
-                vreg[i][e] = (u32x4){0u, 0u, 0u, 0u};
-                if (key < a.n) vreg[i][e] = *reinterpret_cast<const u32x4*>(vbase + key * a.ld + 8 * c);
-            }
+            for (int e = 0; e < 2; ++e) vreg[i][e] = ld16(k0 + 2 * kp + e, vcol + 8 * c);
         }
     };
     auto store_block = [&]() {
@@ -158,8 +164,9 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
             }
             // scale (base-2 units), mask, running max and sum for query qi;
             // lane half hh holds keys 8 j + 4 hh + i of each tile
-            const int64_t kbase_i = (int64_t)kb * AK;
-            const bool diag = a.causal ? (kbase_i + AK - 1 > q0) : (kbase_i + AK > a.n);
+            const int kbase_i = kb * AK;
+            const int qi32 = (int)qi, n32 = (int)a.n;
+            const bool diag = a.causal ? (kbase_i + AK - 1 > (int)q0) : (kbase_i + AK > n32);
             float mloc = -INFINITY;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -167,21 +174,21 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
                 for (int q = 0; q < 16; ++q) {
                     float v = sacc[tt][q] * a.scale_log2;
                     if (diag) {
-                        const int64_t key = kbase_i + 32 * tt + 8 * (q >> 2) + 4 * hh + (q & 3);
-                        if ((a.causal && key > qi) || key >= a.n) v = -INFINITY;
+                        const int key = kbase_i + 32 * tt + 8 * (q >> 2) + 4 * hh + (q & 3);
+                        if ((a.causal && key > qi32) || key >= n32) v = -INFINITY;
                     }
                     sacc[tt][q] = v;
                     mloc = fmaxf(mloc, v);
                 }
             mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
             const float mnew = fmaxf(m, mloc);
-            const float alpha = exp2f(m - mnew);         // 0 on the first block (m = -inf)
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // 0 on the first block (m = -inf)
             float psum = 0.0f;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
-                    const float p = exp2f(sacc[tt][q] - mnew);
+                    const float p = __builtin_amdgcn_exp2f(sacc[tt][q] - mnew);
                     sacc[tt][q] = p;
                     psum += p;
                 }
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
                 for (int q2 = 0; q2 < 2; ++q2) {
                     uint32_t w[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(sacc[tt][8 * q2 + 2 * e], sacc[tt][8 * q2 + 2 * e + 1]);
+                    for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(sacc[tt][8 * q2 + 2 * e], sacc[tt][8 * q2 + 2 * e + 1]);
                     pf[tt][q2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
                 }
             // O^T += V^T P^T: lane (d row, hh) reads keys 16 q2 + 4 hh + 0..3
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
                 const float v0 = oacc[dt][4 * j], v1 = oacc[dt][4 * j + 1];
                 const float v2 = oacc[dt][4 * j + 2], v3 = oacc[dt][4 * j + 3];
                 *reinterpret_cast<u32x2*>(o + d) =
-                    (u32x2){pack_bf16x2(v0 * inv, v1 * inv), pack_bf16x2(v2 * inv, v3 * inv)};
+                    (u32x2){cvt_bf16x2(v0 * inv, v1 * inv), cvt_bf16x2(v2 * inv, v3 * inv)};
             }
     }
 }
