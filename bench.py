@@ -349,6 +349,8 @@ def leg_attnproj(reps):
     nq_r, nkv_r = w.n_q // t, max(w.n_kv // t, 1)
     qkv = torch.empty((w.n, wqkv.shape[0]), dtype=w.dtype, device=DEV)
     a_r = torch.empty((w.n, nq_r * hd), dtype=w.dtype, device=DEV)
+    aws = torch.empty(max(T.tp_attention_workspace_bytes(w.n, nq_r, nkv_r, hd, causal=True), 16),
+                      dtype=torch.uint8, device=DEV)
     part = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
     tm = EventTimer()
     for i in range(2 + reps):
@@ -359,7 +361,7 @@ def leg_attnproj(reps):
         if t_:
             t_.stop("qkv")
             t_.start("attn")
-        T.tp_attention_rank(qkv, nq_r, nkv_r, head_dim=hd, causal=True, out=a_r)
+        T.tp_attention_rank(qkv, nq_r, nkv_r, head_dim=hd, causal=True, out=a_r, workspace=aws)
         if t_:
             t_.stop("attn")
             t_.start("o_proj")

@@ -250,9 +250,15 @@ TP_API tp_status tp_rs_add_rmsnorm(const void* const* partials /*HOST array*/, i
  *   rank (q heads, then k heads, then v heads), 16-byte aligned;
  *   out [n, nq head_dim] bf16, 16-byte aligned, must not overlap qkv.
  *   head_dim must be 128; nkv divides nq; dt must be TP_BF16; qkv under
- *   2 GiB. */
+ *   2 GiB.
+ * workspace: at least tp_attention_workspace_bytes(...) bytes, 16-byte
+ *   aligned (zero bytes, and NULL allowed, when every query tile's keys fit
+ *   one chunk of 2048 keys); it holds fp32 partial results of tiles whose
+ *   keys are cut into several chunks, merged by a second launch. */
+TP_API tp_status tp_attention_workspace_bytes(int64_t n, int nq, int nkv, int head_dim, tp_dtype dt, int causal,
+                                              size_t* bytes /*HOST*/);
 TP_API tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int head_dim, tp_dtype dt,
-                                   int causal, void* out, void* stream);
+                                   int causal, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- vocab-parallel embedding and LM head -------------------------------- */
 

@@ -285,21 +285,39 @@ tp_status tp_partial_reduce(const void* const* partials, int t, int64_t K, tp_dt
                       "tp_partial_reduce");
 }
 
-tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int head_dim, tp_dtype dt, int causal,
-                            void* out, void* stream) {
-    if (!qkv || !out) return fail(TP_EINVAL, "tp_attention_rank: null pointer");
-    if (dt != TP_BF16) return fail(TP_EDTYPE, "tp_attention_rank: bf16 only");
-    if (head_dim != 128) return fail(TP_EINVAL, "tp_attention_rank: head_dim %d (128 supported)", head_dim);
-    if (nq < 1 || nkv < 1 || nq > 4096 || nkv > 4096) return fail(TP_EINVAL, "tp_attention_rank: bad head counts");
-    if (nq % nkv != 0) return fail(TP_ESHAPE, "tp_attention_rank: nkv %d does not divide nq %d", nkv, nq);
+static tp_status check_attention(int64_t n, int nq, int nkv, int head_dim, tp_dtype dt, const char* fn) {
+    if (dt != TP_BF16) return fail(TP_EDTYPE, "%s: bf16 only", fn);
+    if (head_dim != 128) return fail(TP_EINVAL, "%s: head_dim %d (128 supported)", fn, head_dim);
+    if (nq < 1 || nkv < 1 || nq > 4096 || nkv > 4096) return fail(TP_EINVAL, "%s: bad head counts", fn);
+    if (nq % nkv != 0) return fail(TP_ESHAPE, "%s: nkv %d does not divide nq %d", fn, nkv, nq);
     if (n < 0 || n * (int64_t)(nq + 2 * nkv) * head_dim * 2 >= ((int64_t)1 << 31))
-        return fail(TP_EINVAL, "tp_attention_rank: qkv must be under 2 GiB");
+        return fail(TP_EINVAL, "%s: qkv must be under 2 GiB", fn);
+    return TP_OK;
+}
+
+tp_status tp_attention_workspace_bytes(int64_t n, int nq, int nkv, int head_dim, tp_dtype dt, int causal,
+                                       size_t* bytes) {
+    if (!bytes) return fail(TP_EINVAL, "tp_attention_workspace_bytes: null pointer");
+    if (tp_status st = check_attention(n, nq, nkv, head_dim, dt, "tp_attention_workspace_bytes")) return st;
+    *bytes = tpk::attention_ws_bytes(n, nq, nkv, causal);
+    return ok();
+}
+
+tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int head_dim, tp_dtype dt, int causal,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!qkv || !out) return fail(TP_EINVAL, "tp_attention_rank: null pointer");
+    if (tp_status st = check_attention(n, nq, nkv, head_dim, dt, "tp_attention_rank")) return st;
+    const size_t need = tpk::attention_ws_bytes(n, nq, nkv, causal);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(TP_EWORKSPACE, "tp_attention_rank: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need && (((uintptr_t)workspace) & 15u)) return fail(TP_EINVAL, "tp_attention_rank: workspace not 16-byte aligned");
     if ((((uintptr_t)qkv) | ((uintptr_t)out)) & 15u)
         return fail(TP_EINVAL, "tp_attention_rank: qkv and out must be 16-byte aligned");
     const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)(n * (int64_t)(nq + 2 * nkv) * head_dim * 2);
     const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)(n * (int64_t)nq * head_dim * 2);
     if (n > 0 && o0 < q1 && q0 < o1) return fail(TP_EINVAL, "tp_attention_rank: out overlaps qkv");
-    return hip_status(tpk::launch_attention(qkv, n, nq, nkv, head_dim, causal, out, as_stream(stream)),
+    return hip_status(tpk::launch_attention(qkv, n, nq, nkv, head_dim, causal, out, workspace, as_stream(stream)),
                       "tp_attention_rank");
 }
 

@@ -27,7 +27,12 @@
 //   * the next block's K and V are loaded into registers while the current
 //     one is multiplied;
 //   * causal: a tile stops at its last query's block, the diagonal block is
-//     masked, and tiles are dispatched heaviest first.
+//     masked, and tiles are dispatched heaviest first;
+//   * a tile's keys are cut into chunks of at most 32 blocks, one workgroup
+//     each, so that long (causal: late) tiles do not set the kernel's
+//     length; a tile with more than one chunk writes fp32 partials (O, the
+//     running max and sum) to the workspace, and a second kernel merges its
+//     chunks in order.
 #include "common.hpp"
 
 namespace tpk {
@@ -53,6 +58,8 @@ constexpr int AD = 128;          // head_dim
 constexpr int AQ = 32;           // queries per tile
 constexpr int AK = 64;           // keys per block
 constexpr int VT_LD = AK + 4;    // V^T row: 64 keys + 4 pad (136 bytes)
+constexpr int ACH = 32;          // key blocks per chunk (a workgroup's share of a long tile)
+constexpr int APART = AQ * AD + 2 * AQ;   // floats of one wave's partial: O, m, l
 
 struct AttnArgs {
     const uint16_t* qkv;
@@ -61,8 +68,18 @@ struct AttnArgs {
     int64_t ld;                  // qkv row length (elements)
     int nq, nkv, rep, causal;
     int ntiles;
+    int cmax;                    // chunks of the longest tile
     float scale_log2;            // log2(e) / sqrt(d)
+    float* part;                 // [ntiles][cmax][heads/4 quads][4 waves][APART] fp32
 };
+
+// key blocks of query tile `tile`
+__host__ __device__ __forceinline__ int tile_blocks(int tile, int64_t n, int causal) {
+    if (!causal) return (int)((n + AK - 1) / AK);
+    int64_t last = (int64_t)tile * AQ + AQ - 1;
+    if (last > n - 1) last = n - 1;
+    return (int)(last / AK) + 1;
+}
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[AK * AD];
@@ -70,7 +87,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
     const int tid = threadIdx.x;
-    const int tile = a.causal ? a.ntiles - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    // unit = (tile, chunk of at most ACH key blocks); heaviest tiles first
+    const int ut = (int)blockIdx.x / a.cmax, uc = (int)blockIdx.x - ut * a.cmax;
+    const int tile = a.causal ? a.ntiles - 1 - ut : ut;
     const int g = blockIdx.y;
     const int hsub = blockIdx.z * 4 + wid;            // head within the group
     const bool active = hsub < a.rep;
@@ -90,13 +109,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qi, head * AD + 16 * s + 8 * hh));
 
-    // key range
-    int nb = (int)((a.n + AK - 1) / AK);
-    if (a.causal) {
-        int64_t last = q0 + AQ - 1;
-        if (last > a.n - 1) last = a.n - 1;
-        nb = (int)(last / AK) + 1;
-    }
+    // key range of this unit: blocks [b0, b1) of the tile's nbt
+    const int nbt = tile_blocks(tile, a.n, a.causal);
+    const int b0 = uc * ACH;
+    if (b0 >= nbt) return;                            // no such chunk (uniform)
+    const int b1 = b0 + ACH < nbt ? b0 + ACH : nbt;
+    const bool split = nbt > ACH;
     const int kcol = (a.nq + g) * AD, vcol = (a.nq + a.nkv + g) * AD;
 
     // staging: K items (key, chunk) = tid + 256 i; V items (key pair, chunk) = tid + 256 i
@@ -143,11 +161,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         for (int q = 0; q < 16; ++q) oacc[t][q] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    load_block(0);
-    for (int kb = 0; kb < nb; ++kb) {
+    load_block(b0);
+    for (int kb = b0; kb < b1; ++kb) {
         store_block();
         __syncthreads();
-        if (kb + 1 < nb) load_block(kb + 1);
+        if (kb + 1 < b1) load_block(kb + 1);
         if (active) {
             // S^T = K Q^T for the block's two 32-key tiles
             f32x16 sacc[2];
@@ -230,6 +248,23 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         __syncthreads();
     }
 
+    if (split) {
+        // this chunk's unnormalised O, running max and sum for the combine
+        float* pp = a.part + (((((int64_t)ut * a.cmax + uc) * gridDim.y + g) * gridDim.z + blockIdx.z) * 4 + wid) * APART;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 32 * dt + 8 * j + 4 * hh;
+                *reinterpret_cast<float4*>(pp + r * AD + d) =
+                    make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
+            }
+        if (hh == 0) {
+            pp[AQ * AD + r] = m;
+            pp[AQ * AD + AQ + r] = lsum;
+        }
+        return;
+    }
     // out[qi, head, d]: lane holds d = 32 dt + 8 j + 4 hh + i
     if (active && qi < a.n) {
         const float inv = 1.0f / lsum;
@@ -247,15 +282,62 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
 }
 
-}  // namespace
+// Merges the chunks of the split tiles: for query i of head h,
+// m* = max_c m_c, out = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c,
+// chunks in order.  Block (tile, KV group, quad x 4 + wave): 256 threads,
+// thread = (query tid / 8, 16 consecutive d).
+__global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, int nz) {
+    const int ut = blockIdx.x;
+    const int tile = a.causal ? a.ntiles - 1 - ut : ut;
+    const int nbt = tile_blocks(tile, a.n, a.causal);
+    if (nbt <= ACH) return;                              // written directly
+    const int nch = (nbt + ACH - 1) / ACH;
+    const int g = blockIdx.y;
+    const int z = blockIdx.z >> 2, wv = blockIdx.z & 3;
+    const int hsub = z * 4 + wv;
+    if (hsub >= a.rep) return;
+    const int head = g * a.rep + hsub;
+    const int qq = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
+    const int64_t qi = (int64_t)tile * AQ + qq;
+    if (qi >= a.n) return;
+    auto chunk = [&](int c) -> const float* {
+        return a.part + (((((int64_t)ut * a.cmax + c) * gridDim.y + g) * nz + z) * 4 + wv) * APART;
+    };
+    float mx = -INFINITY;
+    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, chunk(c)[AQ * AD + qq]);
+    float acc[16], den = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+        const float* pp = chunk(c);
+        const float w = __builtin_amdgcn_exp2f(pp[AQ * AD + qq] - mx);
+        den = den + w * pp[AQ * AD + AQ + qq];
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+            const float4 o = *reinterpret_cast<const float4*>(pp + qq * AD + d0 + e);
+            acc[e] = acc[e] + w * o.x;
+            acc[e + 1] = acc[e + 1] + w * o.y;
+            acc[e + 2] = acc[e + 2] + w * o.z;
+            acc[e + 3] = acc[e + 3] + w * o.w;
+        }
+    }
+    const float inv = 1.0f / den;
+    uint16_t* o = a.out + qi * (int64_t)a.nq * AD + (int64_t)head * AD + d0;
+    u32x4 w0, w1;
+    w0.x = cvt_bf16x2(acc[0] * inv, acc[1] * inv);
+    w0.y = cvt_bf16x2(acc[2] * inv, acc[3] * inv);
+    w0.z = cvt_bf16x2(acc[4] * inv, acc[5] * inv);
+    w0.w = cvt_bf16x2(acc[6] * inv, acc[7] * inv);
+    w1.x = cvt_bf16x2(acc[8] * inv, acc[9] * inv);
+    w1.y = cvt_bf16x2(acc[10] * inv, acc[11] * inv);
+    w1.z = cvt_bf16x2(acc[12] * inv, acc[13] * inv);
+    w1.w = cvt_bf16x2(acc[14] * inv, acc[15] * inv);
+    reinterpret_cast<u32x4*>(o)[0] = w0;
+    reinterpret_cast<u32x4*>(o)[1] = w1;
+}
 
-hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int head_dim, int causal, void* out,
-                            hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    if (head_dim != AD) return hipErrorInvalidValue;
-    AttnArgs a;
-    a.qkv = static_cast<const uint16_t*>(qkv);
-    a.out = static_cast<uint16_t*>(out);
+AttnArgs attn_args(int64_t n, int nq, int nkv, int causal) {
+    AttnArgs a{};
     a.n = n;
     a.ld = (int64_t)(nq + 2 * nkv) * AD;
     a.nq = nq;
@@ -263,9 +345,38 @@ hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int hea
     a.rep = nq / nkv;
     a.causal = causal ? 1 : 0;
     a.ntiles = (int)((n + AQ - 1) / AQ);
+    const int nbmax = tile_blocks(a.ntiles - 1, n, a.causal);
+    a.cmax = (nbmax + ACH - 1) / ACH;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)AD);
-    const dim3 grid((unsigned)a.ntiles, (unsigned)nkv, (unsigned)((a.rep + 3) / 4));
-    hipLaunchKernelGGL(attention_kernel, grid, dim3(256), 0, s, a);
+    return a;
+}
+
+}  // namespace
+
+size_t attention_ws_bytes(int64_t n, int nq, int nkv, int causal) {
+    if (n <= 0) return 0;
+    const AttnArgs a = attn_args(n, nq, nkv, causal);
+    if (a.cmax <= 1) return 0;
+    const int nz = (a.rep + 3) / 4;
+    return (size_t)a.ntiles * a.cmax * nkv * nz * 4 * APART * sizeof(float);
+}
+
+hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int head_dim, int causal, void* out,
+                            void* ws, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (head_dim != AD) return hipErrorInvalidValue;
+    AttnArgs a = attn_args(n, nq, nkv, causal);
+    a.qkv = static_cast<const uint16_t*>(qkv);
+    a.out = static_cast<uint16_t*>(out);
+    a.part = static_cast<float*>(ws);
+    if (a.cmax > 1 && !ws) return hipErrorInvalidValue;
+    const int nz = (a.rep + 3) / 4;
+    hipLaunchKernelGGL(attention_kernel, dim3((unsigned)(a.ntiles * a.cmax), (unsigned)nkv, (unsigned)nz), dim3(256),
+                       0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.cmax <= 1) return e;
+    hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)a.ntiles, (unsigned)nkv, (unsigned)(nz * 4)),
+                       dim3(256), 0, s, a, nz);
     return hipGetLastError();
 }
 

@@ -69,8 +69,9 @@ hipError_t launch_rs_add_rmsnorm(const void* const* partials, int t, int tp_rank
 hipError_t launch_logits_gather_argmax(const void* const* shards, int t, int64_t n, int64_t vocab, void* full,
                                        int64_t* argmax, hipStream_t s);
 
+size_t attention_ws_bytes(int64_t n, int nq, int nkv, int causal);
 hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int head_dim, int causal, void* out,
-                            hipStream_t s);
+                            void* ws, hipStream_t s);
 
 hipError_t launch_vocab_embed(const int64_t* ids, int64_t n, const void* table, int64_t start,
                               int64_t end, int64_t h, int esize, void* out, hipStream_t s);

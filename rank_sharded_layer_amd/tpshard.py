@@ -58,7 +58,8 @@ _SIGS = {
     "tp_partial_reduce": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _vp, _int, _int, _vp]),
     "tp_ring_schedule": (_int, [_int, _i64, ctypes.POINTER(RingStep), _int, ctypes.POINTER(_int)]),
     "tp_sp_rows": (_int, [_i64, _int, _int, _i64p, _i64p]),
-    "tp_attention_rank": (_int, [_vp, _i64, _int, _int, _int, _int, _int, _vp, _vp]),
+    "tp_attention_workspace_bytes": (_int, [_i64, _int, _int, _int, _int, _int, _szp]),
+    "tp_attention_rank": (_int, [_vp, _i64, _int, _int, _int, _int, _int, _vp, _vp, _sz, _vp]),
     "tp_logits_gather_argmax": (_int, [ctypes.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _vp]),
     "tp_rs_add_rmsnorm": (_int, [ctypes.POINTER(_vp), _int, _int, _i64, _i64, _int, _vp, _vp, ctypes.c_float,
                                  _vp, _vp, _vp]),
@@ -292,7 +293,14 @@ def tp_ring_schedule(t, K):
                  len=s.len) for s in arr[:got.value]]
 
 
-def tp_attention_rank(qkv, nq, nkv, head_dim=128, causal=True, out=None, stream=None):
+def tp_attention_workspace_bytes(n, nq, nkv, head_dim=128, causal=True) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().tp_attention_workspace_bytes(n, nq, nkv, head_dim, _dt(torch.bfloat16), 1 if causal else 0,
+                                              ctypes.byref(b)))
+    return b.value
+
+
+def tp_attention_rank(qkv, nq, nkv, head_dim=128, causal=True, out=None, workspace=None, stream=None):
     """softmax(q k^T / sqrt(d)) v for the rank's nq query heads over its nkv KV
     heads, from the packed QKV projection output [n, (nq + 2 nkv) d]."""
     n = qkv.shape[0]
@@ -300,7 +308,8 @@ def tp_attention_rank(qkv, nq, nkv, head_dim=128, causal=True, out=None, stream=
     if out is None:
         out = torch.empty((n, nq * head_dim), dtype=torch.bfloat16, device=qkv.device)
     po = _dev(out, "out", torch.bfloat16, (n, nq * head_dim))
-    _check(lib().tp_attention_rank(pq, n, nq, nkv, head_dim, _dt(torch.bfloat16), 1 if causal else 0, po,
+    ws, wsb = _workspace(tp_attention_workspace_bytes(n, nq, nkv, head_dim, causal), qkv.device, workspace)
+    _check(lib().tp_attention_rank(pq, n, nq, nkv, head_dim, _dt(torch.bfloat16), 1 if causal else 0, po, ws, wsb,
                                    _stream(stream)))
     return out
 

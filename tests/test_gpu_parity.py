@@ -744,3 +744,24 @@ def test_attention_rank_peaked_and_flat_scores():
     out = T.tp_attention_rank(flat, nq, nkv, causal=False)
     torch.cuda.synchronize()
     attn_check(flat, nq, nkv, False, out)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_rank_split_key_chunks(causal):
+    """n = 4100: 65 key blocks, so tiles are cut into chunks of 32 blocks
+    (non-causal: every tile; causal: the late ones) that a second kernel
+    merges; sampled rows around chunk and tile edges."""
+    n, nq, nkv = 4100, 8, 2
+    assert T.tp_attention_workspace_bytes(n, nq, nkv, causal=causal) > 0
+    qkv = rnd((n, (nq + 2 * nkv) * 128), 1.0, 960 + causal, torch.bfloat16)
+    out = T.tp_attention_rank(qkv, nq, nkv, causal=causal)
+    torch.cuda.synchronize()
+    rows = [0, 31, 2047, 2048, 2049, 2079, 2080, 4064, 4095, 4096, 4099]
+    attn_check(qkv, nq, nkv, causal, out, rows=rows)
+    assert torch.equal(out, T.tp_attention_rank(qkv, nq, nkv, causal=causal))
+
+
+def test_attention_workspace_is_zero_for_short_sequences():
+    assert T.tp_attention_workspace_bytes(2048, 4, 1, causal=True) == 0
+    assert T.tp_attention_workspace_bytes(2048, 4, 1, causal=False) == 0
+    assert T.tp_attention_workspace_bytes(2049, 4, 1, causal=False) > 0
