@@ -252,9 +252,11 @@ TP_API tp_status tp_rs_add_rmsnorm(const void* const* partials /*HOST array*/, i
  *   head_dim must be 128; nkv divides nq; dt must be TP_BF16; qkv under
  *   2 GiB.
  * workspace: at least tp_attention_workspace_bytes(...) bytes, 16-byte
- *   aligned (zero bytes, and NULL allowed, when every query tile's keys fit
- *   one chunk of 2048 keys); it holds fp32 partial results of tiles whose
- *   keys are cut into several chunks, merged by a second launch. */
+ *   aligned.  The work is cut into about 512 equal pieces (pairs of a
+ *   light and a heavy 32-query tile, each pair's key blocks in equal
+ *   chunks); a tile spread over several pieces leaves fp32 partial results
+ *   there, merged by a second launch.  Zero bytes (NULL allowed) for short
+ *   sequences, where every piece holds whole tiles. */
 TP_API tp_status tp_attention_workspace_bytes(int64_t n, int nq, int nkv, int head_dim, tp_dtype dt, int causal,
                                               size_t* bytes /*HOST*/);
 TP_API tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int head_dim, tp_dtype dt,

@@ -11,8 +11,9 @@
 //
 // Design (flash-attention order, one pass over the keys):
 //   * workgroup = 4 waves = up to 4 query heads of one KV group on the same
-//     32 queries; the 64-key K and V blocks are staged once in LDS and read
-//     by all four;
+//     32 queries; each 64-key block of K and V goes from global memory
+//     straight into LDS (buffer_load ... lds, double-buffered, one barrier
+//     per block) and is read by all four;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
 //     keys as rows, queries as columns), so a lane owns one query and 32 of
 //     the block's 64 scores: the running max and sum need one exchange with
@@ -20,26 +21,27 @@
 //   * O^T = V^T P^T: the probabilities are the B operand straight from the
 //     score accumulators -- the 16 keys of a K step are taken in the order
 //     the accumulator holds them (keys 4h..4h+3 and 8+4h..8+4h+3 of each 16
-//     for lane half h), and V^T is read in the same order;
-//   * K in LDS is row-major with 16-byte chunk c of key r at c ^ (r & 15)
-//     (conflict-free fragment reads); V is stored transposed [d][key] with
-//     136-byte rows (conflict-free 8-byte fragment reads);
-//   * the next block's K and V are loaded into registers while the current
-//     one is multiplied;
-//   * causal: a tile stops at its last query's block, the diagonal block is
-//     masked, and tiles are dispatched heaviest first;
-//   * a tile's keys are cut into chunks of at most 32 blocks, one workgroup
-//     each, so that long (causal: late) tiles do not set the kernel's
-//     length; a tile with more than one chunk writes fp32 partials (O, the
-//     running max and sum) to the workspace, and a second kernel merges its
-//     chunks in order.
+//     for lane half h) -- and the V^T fragments come from row-major V in LDS
+//     through the transposing read ds_read_b64_tr_b16;
+//   * the running max moves only when a block raises it by more than 2^8
+//     (in probability), so the 64 accumulator rescales are mostly skipped;
+//   * causal work balance: query tiles are paired heavy with light (tile p
+//     with tile nt-1-p, a near-constant number of key blocks per pair), each
+//     pair's concatenated key blocks are cut into k equal chunks, and one
+//     workgroup takes one chunk, so every workgroup has the same work.  A
+//     tile that spans several chunks writes fp32 partials (unnormalised O,
+//     running max and sum) per chunk to the workspace, and a second kernel
+//     merges them in key order.
 #include "common.hpp"
+
+#include <type_traits>
 
 namespace tpk {
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -54,12 +56,20 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+__device__ __forceinline__ void wg_barrier() {
+    // s_barrier alone: the waits it needs are issued explicitly before it
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 constexpr int AD = 128;          // head_dim
 constexpr int AQ = 32;           // queries per tile
 constexpr int AK = 64;           // keys per block
-constexpr int VT_LD = AK + 4;    // V^T row: 64 keys + 4 pad (136 bytes)
-constexpr int ACH = 32;          // key blocks per chunk (a workgroup's share of a long tile)
 constexpr int APART = AQ * AD + 2 * AQ;   // floats of one wave's partial: O, m, l
+constexpr int AUNITS = 512;      // target workgroups: two per CU
+constexpr int AMINCH = 8;        // fewest key blocks per chunk
+constexpr float ATAU = 8.0f;     // running-max slack before a rescale (base-2 units)
 
 struct AttnArgs {
     const uint16_t* qkv;
@@ -67,10 +77,11 @@ struct AttnArgs {
     int64_t n;
     int64_t ld;                  // qkv row length (elements)
     int nq, nkv, rep, causal;
-    int ntiles;
-    int cmax;                    // chunks of the longest tile
+    int ntiles;                  // query tiles of AQ
+    int npairs;                  // (ntiles + 1) / 2
+    int kch;                     // chunks per pair
     float scale_log2;            // log2(e) / sqrt(d)
-    float* part;                 // [ntiles][cmax][heads/4 quads][4 waves][APART] fp32
+    float* part;                 // [npairs][kch][2][nkv][quads][4 waves][APART] fp32
 };
 
 // key blocks of query tile `tile`
@@ -81,217 +92,316 @@ __host__ __device__ __forceinline__ int tile_blocks(int tile, int64_t n, int cau
     return (int)(last / AK) + 1;
 }
 
+// Pair p = (tile p, tile ntiles-1-p; one tile when they coincide).  Its key
+// blocks in order: tile p's, then the other tile's; chunk c of the pair is
+// [c T / k, (c+1) T / k) of that list, T its length.
+struct PairPlan {
+    int ta, tb;                  // tiles (tb = -1: none)
+    int na, total;               // blocks of ta, of the pair
+};
+
+__host__ __device__ __forceinline__ PairPlan pair_plan(int p, const AttnArgs& a) {
+    PairPlan pp;
+    pp.ta = p;
+    pp.tb = a.ntiles - 1 - p;
+    pp.na = tile_blocks(pp.ta, a.n, a.causal);
+    if (pp.tb == pp.ta) pp.tb = -1;
+    pp.total = pp.na + (pp.tb >= 0 ? tile_blocks(pp.tb, a.n, a.causal) : 0);
+    return pp;
+}
+
+__host__ __device__ __forceinline__ int chunk_lo(int c, int total, int k) {
+    return (int)(((int64_t)c * total) / k);
+}
+
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[AK * AD];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[AD * VT_LD];
+    __shared__ __attribute__((aligned(1024))) uint16_t ks0[AK * AD];
+    __shared__ __attribute__((aligned(1024))) uint16_t ks1[AK * AD];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs0[AK * AD];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs1[AK * AD];
     const int lane = threadIdx.x & 63;
-    const int wid = threadIdx.x >> 6;
-    const int tid = threadIdx.x;
-    // unit = (tile, chunk of at most ACH key blocks); heaviest tiles first
-    const int ut = (int)blockIdx.x / a.cmax, uc = (int)blockIdx.x - ut * a.cmax;
-    const int tile = a.causal ? a.ntiles - 1 - ut : ut;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = (int)blockIdx.x / a.kch, c = (int)blockIdx.x - p * a.kch;
     const int g = blockIdx.y;
     const int hsub = blockIdx.z * 4 + wid;            // head within the group
     const bool active = hsub < a.rep;
     const int head = g * a.rep + (active ? hsub : 0);
-    const int64_t q0 = (int64_t)tile * AQ;
     const int r = lane & 31, hh = lane >> 5;
-    const int64_t qi = q0 + r;                        // this lane's query
-
-    // every load is a buffer load over [n, ld]: rows past n read as zero
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)a.qkv, (short)0, (int)(a.n * a.ld * 2), 0x00020000);
-    auto ld16 = [&](int64_t row, int col) -> u32x4 {
-        return __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((row * a.ld + col) * 2), 0, 0);
-    };
-    // Q fragments (B operand): query qi, d = 16 s + 8 hh .. + 8
-    bf16x8 qf[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qi, head * AD + 16 * s + 8 * hh));
-
-    // key range of this unit: blocks [b0, b1) of the tile's nbt
-    const int nbt = tile_blocks(tile, a.n, a.causal);
-    const int b0 = uc * ACH;
-    if (b0 >= nbt) return;                            // no such chunk (uniform)
-    const int b1 = b0 + ACH < nbt ? b0 + ACH : nbt;
-    const bool split = nbt > ACH;
     const int kcol = (a.nq + g) * AD, vcol = (a.nq + a.nkv + g) * AD;
 
-    // staging: K items (key, chunk) = tid + 256 i; V items (key pair, chunk) = tid + 256 i
-    u32x4 kreg[4], vreg[2][2];
-    auto load_block = [&](int kb) {
-        const int64_t k0 = (int64_t)kb * AK;
+    // every load is a buffer load over [n, ld]: rows past n, and blocks past
+    // the segment (base offset 2^31), read as zero
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.qkv, (short)0, (int)(a.n * a.ld * 2), 0x00020000);
+    const uint32_t row_b = (uint32_t)(a.ld * 2);
+
+    // K and V blocks go from global memory straight into LDS (a wave
+    // instruction fills 64 consecutive 16-byte slots, lane l slot l, so each
+    // lane fetches the chunk that belongs in its slot).  LDS layouts, chosen
+    // so that every fragment read is conflict-free and its address is one
+    // per-lane base plus immediate offsets:
+    //   K: the 32-byte piece d = 16 s .. 16 s + 15 of key k at byte
+    //      2048 s + 32 k, its two 16-byte halves swapped when bit 3 of k is
+    //      set (16 consecutive keys of one half then cover all 16 bank
+    //      groups);
+    //   V: the 64-byte piece d = 32 t .. 32 t + 31 of key k at byte
+    //      4096 t + 64 k (4 consecutive keys of one piece = 256 contiguous
+    //      bytes, what a half-wave transposing read takes).
+    // This wave's instruction q fills slots 64 (4 wid + q) .. + 63:
+    //   K: s = 2 wid + (q >> 1), key 32 (q & 1) + (lane >> 1), half
+    //      (lane & 1) ^ ((lane >> 4) & 1);
+    //   V: t = wid, key 16 q + (lane >> 2), chunk (lane & 3) of the piece.
+    uint32_t koff[4], voff[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, key = idx >> 4, c = idx & 15;
-            kreg[i] = ld16(k0 + key, kcol + 8 * c);
-        }
+    for (int q = 0; q < 4; ++q) {
+        const int kk = 32 * (q & 1) + (lane >> 1);
+        const int kc = 2 * (2 * wid + (q >> 1)) + ((lane & 1) ^ ((lane >> 4) & 1));
+        koff[q] = (uint32_t)kk * row_b + (uint32_t)(kcol + 8 * kc) * 2;
+        const int vk = 16 * q + (lane >> 2);
+        voff[q] = (uint32_t)vk * row_b + (uint32_t)(vcol + 32 * wid + 8 * (lane & 3)) * 2;
+    }
+    auto issue = [&](uint32_t base, uint16_t* buf, const uint32_t (&off)[4]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, kp = idx & 31, c = idx >> 5;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) vreg[i][e] = ld16(k0 + 2 * kp + e, vcol + 8 * c);
+        for (int q = 0; q < 4; ++q) {
+            auto* dst = (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(buf) + (4 * wid + q) * 1024);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, base + off[q], 0, 0, 0);
         }
     };
-    auto store_block = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, key = idx >> 4, c = idx & 15;
-            *reinterpret_cast<u32x4*>(ks + key * AD + ((c ^ (key & 15)) * 8)) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, kp = idx & 31, c = idx >> 5;
-            const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-            const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // d = 8 c + e: (V[2kp][d], V[2kp+1][d]) as one 32-bit word
-                const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
-                const uint32_t hi = (e & 1) ? (w1[e >> 1] & 0xffff0000u) : (w1[e >> 1] << 16);
-                *reinterpret_cast<uint32_t*>(vt + (8 * c + e) * VT_LD + 2 * kp) = lo | hi;
-            }
-        }
+    // K fragment (A operand) of key 32 tt + r, d = 16 s + 8 hh .. + 8
+    const int kfrag_b = r * 32 + 16 * (hh ^ ((r >> 3) & 1));
+    auto kfrag = [&](const uint16_t* kbuf, int s, int tt) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(kbuf) + kfrag_b + 2048 * s + 1024 * tt);
+    };
+    // V^T fragment (A operand, rows d = 32 dt + (lane & 31)) for keys
+    // kb0 + 4 hh + 0..3 and kb0 + 8 + 4 hh + 0..3 (kb0 = 32 tt + 16 q2):
+    // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i & 3 of
+    // lanes 4 k + (i >> 2), k = 0..3, so lane j of the group addresses key
+    // row (j >> 2) at columns 4 (j & 3) .. + 3 of the group's 16 columns
+    const int vfrag_b = (4 * hh + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+    auto vfrag = [&](const uint16_t* vbuf, int kb0, int dt) -> bf16x8 {
+        const uint8_t* pv = reinterpret_cast<const uint8_t*>(vbuf) + vfrag_b + 4096 * dt + 64 * kb0;
+        const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(pv));
+        const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(pv + 512));
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
-    f32x16 oacc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) oacc[t][q] = 0.0f;
-    float m = -INFINITY, lsum = 0.0f;
+    const PairPlan pp = pair_plan(p, a);
+    const int lo = chunk_lo(c, pp.total, a.kch), hi = chunk_lo(c + 1, pp.total, a.kch);
+    // at most two segments: a piece of tile ta, then a piece of tile tb
+#pragma unroll 1
+    for (int sg = 0; sg < 2; ++sg) {
+        int tile, b0, b1;
+        if (sg == 0) {
+            tile = pp.ta;
+            b0 = lo;
+            b1 = hi < pp.na ? hi : pp.na;
+        } else {
+            tile = pp.tb;
+            b0 = (lo > pp.na ? lo : pp.na) - pp.na;
+            b1 = hi - pp.na;
+        }
+        if (tile < 0 || b0 >= b1) continue;          // uniform
+        if (sg == 1) wg_barrier();                    // the first segment's buffers are free
+        const int nbt = tile_blocks(tile, a.n, a.causal);
+        const bool whole = b0 == 0 && b1 == nbt;
+        const int64_t q0 = (int64_t)tile * AQ;
+        const int64_t qi = q0 + r;                    // this lane's query
+        const int qi32 = (int)qi, n32 = (int)a.n;
+        // the tile's last block holds its diagonal (causal) or the end of
+        // the keys (ragged n): masked
+        const bool mask_end = b1 == nbt && (a.causal || (int64_t)nbt * AK > a.n);
+        auto blk_base = [&](int kb) -> uint32_t {
+            return kb < b1 ? (uint32_t)kb * (uint32_t)AK * row_b : 0x80000000u;
+        };
 
-    load_block(b0);
-    for (int kb = b0; kb < b1; ++kb) {
-        store_block();
-        __syncthreads();
-        if (kb + 1 < b1) load_block(kb + 1);
+        f32x16 oacc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) oacc[t][q] = 0.0f;
+        float m = -INFINITY, lsum = 0.0f;            // running max (base-2 units) and sum
+
+        issue(blk_base(b0), ks0, koff);
+        issue(blk_base(b0), vs0, voff);
         if (active) {
-            // S^T = K Q^T for the block's two 32-key tiles
-            f32x16 sacc[2];
+            // Q fragments (B operand): query qi, d = 16 s + 8 hh .. + 8
+            bf16x8 qf[8];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
+            for (int s = 0; s < 8; ++s)
+                qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rs, (uint32_t)(qi * row_b + (head * AD + 16 * s + 8 * hh) * 2), 0, 0));
+            // one key block kb; buffers alternate with its parity
+            auto step = [&](int kb, auto P) {
+                constexpr bool odd = decltype(P)::value != 0;
+                const uint16_t* kcur = odd ? ks1 : ks0;
+                const uint16_t* vcur = odd ? vs1 : vs0;
+                // K(kb), V(kb) landed (own DMA), then everyone's; all waves
+                // are done with block kb-1, whose buffers take block kb+1
+                __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0)
+                wg_barrier();
+                issue(blk_base(kb + 1), odd ? ks0 : ks1, koff);
+                issue(blk_base(kb + 1), odd ? vs0 : vs1, voff);
+                // S^T = K Q^T for the block's two 32-key tiles
+                f32x16 sc[2];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) sacc[tt][q] = 0.0f;
-                const int key = 32 * tt + r;
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + key * AD + (((2 * s + hh) ^ (key & 15)) * 8));
-                    sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[tt], 0, 0, 0);
+                    for (int q = 0; q < 16; ++q) sc[tt][q] = 0.0f;
+                // fragment reads run 8 ahead of the MFMAs that use them
+                bf16x8 kf[16];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kf[i] = kfrag(kcur, i >> 1, i & 1);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i + 8 < 16) kf[i + 8] = kfrag(kcur, (i + 8) >> 1, (i + 8) & 1);
+                    sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], sc[i & 1], 0, 0, 0);
                 }
-            }
-            // scale (base-2 units), mask, running max and sum for query qi;
-            // lane half hh holds keys 8 j + 4 hh + i of each tile
-            const int kbase_i = kb * AK;
-            const int qi32 = (int)qi, n32 = (int)a.n;
-            const bool diag = a.causal ? (kbase_i + AK - 1 > (int)q0) : (kbase_i + AK > n32);
-            float mloc = -INFINITY;
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                // lane half hh holds keys 8 j + 4 hh + i of each 32-key tile
+                if (mask_end && kb == b1 - 1) {
+                    // keys past min(qi, n - 1) (causal) or past n - 1: key
+                    // kb AK + off with off = 32 tt + 8 (q >> 2) + 4 hh + (q & 3)
+                    int lim = (a.causal && qi32 < n32 ? qi32 : n32 - 1) - kb * AK - 4 * hh;
+                    asm volatile("" : "+v"(lim));          // computed here, not hoisted
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    float v = sacc[tt][q] * a.scale_log2;
-                    if (diag) {
-                        const int key = kbase_i + 32 * tt + 8 * (q >> 2) + 4 * hh + (q & 3);
-                        if ((a.causal && key > qi32) || key >= n32) v = -INFINITY;
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q)
+                            if (32 * tt + 8 * (q >> 2) + (q & 3) > lim) sc[tt][q] = -INFINITY;
+                }
+                float mloc = -INFINITY;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) mloc = fmaxf(mloc, sc[tt][q]);
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+                const float ms = mloc * a.scale_log2;
+                // the running max moves only when some query's block max
+                // passes it by more than ATAU (probabilities stay below
+                // 2^ATAU); the first block always sets it (m = -inf)
+                const bool grow = __any(ms > m + ATAU);
+                const float mn = grow ? fmaxf(m, ms) : m;
+                const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 1 if unchanged, 0 on the first block
+                const float nmn = -mn;
+                float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const float pr = __builtin_amdgcn_exp2f(fmaf(sc[tt][q], a.scale_log2, nmn));
+                        sc[tt][q] = pr;
+                        ps[q & 3] += pr;
                     }
-                    sacc[tt][q] = v;
-                    mloc = fmaxf(mloc, v);
-                }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            const float mnew = fmaxf(m, mloc);
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // 0 on the first block (m = -inf)
-            float psum = 0.0f;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[tt][q] - mnew);
-                    sacc[tt][q] = p;
-                    psum += p;
-                }
-            psum += __shfl_xor(psum, 32, 64);
-            lsum = lsum * alpha + psum;
-            m = mnew;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) oacc[t][q] *= alpha;
-            // P^T fragments: K step (tt, q2) = accumulator values 8 q2 .. 8 q2 + 7
-            bf16x8 pf[2][2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(sacc[tt][8 * q2 + 2 * e], sacc[tt][8 * q2 + 2 * e + 1]);
-                    pf[tt][q2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
-                }
-            // O^T += V^T P^T: lane (d row, hh) reads keys 16 q2 + 4 hh + 0..3
-            // and 16 q2 + 8 + 4 hh + 0..3 of tile tt
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const uint16_t* vrow = vt + (32 * dt + r) * VT_LD;
+                float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                psum += __shfl_xor(psum, 32, 64);
+                lsum = lsum * alpha + psum;
+                m = mn;
+                // P^T fragments: K step (tt, q2) = accumulator values 8 q2 .. 8 q2 + 7
+                bf16x8 pf[2][2];
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int q2 = 0; q2 < 2; ++q2) {
-                        const int kk = 32 * tt + 16 * q2 + 4 * hh;
-                        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + kk);
-                        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + kk + 8);
-                        const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4){x0.x, x0.y, x1.x, x1.y});
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[tt][q2], oacc[dt], 0, 0, 0);
+                        uint32_t w[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(sc[tt][8 * q2 + 2 * e], sc[tt][8 * q2 + 2 * e + 1]);
+                        pf[tt][q2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
                     }
+                if (grow) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) oacc[t][q] *= alpha;
+                }
+                // O^T += V^T P^T: the A fragment of (tt, q2) holds keys
+                // 32 tt + 16 q2 + {4 hh + 0..3, 8 + 4 hh + 0..3}, the order in
+                // which the score accumulators hold them
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt)
+                            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vcur, 32 * tt + 16 * q2, dt),
+                                                                              pf[tt][q2], oacc[dt], 0, 0, 0);
+            };
+            for (int kb = b0; kb < b1; kb += 2) {
+                step(kb, std::integral_constant<int, 0>());
+                if (kb + 1 < b1) step(kb + 1, std::integral_constant<int, 1>());
+            }
+        } else {
+            // a wave without a head still moves its share of every block
+            for (int kb = b0; kb < b1; ++kb) {
+                __builtin_amdgcn_s_waitcnt(0x0f70);
+                wg_barrier();
+                const bool odd = ((kb - b0) & 1) != 0;
+                issue(blk_base(kb + 1), odd ? ks0 : ks1, koff);
+                issue(blk_base(kb + 1), odd ? vs0 : vs1, voff);
             }
         }
-        __syncthreads();
-    }
+        // the last step issued only zero-fill loads past the segment
+        __builtin_amdgcn_s_waitcnt(0x0f70);
 
-    if (split) {
-        // this chunk's unnormalised O, running max and sum for the combine
-        float* pp = a.part + (((((int64_t)ut * a.cmax + uc) * gridDim.y + g) * gridDim.z + blockIdx.z) * 4 + wid) * APART;
+        if (!active) continue;
+        if (!whole) {
+            // this segment's unnormalised O, running max and sum for the combine
+            const int64_t slot = ((int64_t)p * a.kch + c) * 2 + sg;
+            float* pw = a.part + (((slot * gridDim.y + g) * gridDim.z + blockIdx.z) * 4 + wid) * APART;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = 32 * dt + 8 * j + 4 * hh;
-                *reinterpret_cast<float4*>(pp + r * AD + d) =
-                    make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
+                for (int j = 0; j < 4; ++j) {
+                    const int d = 32 * dt + 8 * j + 4 * hh;
+                    *reinterpret_cast<float4*>(pw + r * AD + d) =
+                        make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
+                }
+            if (hh == 0) {
+                pw[AQ * AD + r] = m;
+                pw[AQ * AD + AQ + r] = lsum;
             }
-        if (hh == 0) {
-            pp[AQ * AD + r] = m;
-            pp[AQ * AD + AQ + r] = lsum;
+        } else if (qi < a.n) {
+            // out[qi, head, d]: lane holds d = 32 dt + 8 j + 4 hh + i
+            const float inv = 1.0f / lsum;
+            uint16_t* o = a.out + qi * (int64_t)a.nq * AD + (int64_t)head * AD;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = 32 * dt + 8 * j + 4 * hh;
+                    const float v0 = oacc[dt][4 * j], v1 = oacc[dt][4 * j + 1];
+                    const float v2 = oacc[dt][4 * j + 2], v3 = oacc[dt][4 * j + 3];
+                    *reinterpret_cast<u32x2*>(o + d) =
+                        (u32x2){cvt_bf16x2(v0 * inv, v1 * inv), cvt_bf16x2(v2 * inv, v3 * inv)};
+                }
         }
-        return;
-    }
-    // out[qi, head, d]: lane holds d = 32 dt + 8 j + 4 hh + i
-    if (active && qi < a.n) {
-        const float inv = 1.0f / lsum;
-        uint16_t* o = a.out + qi * (int64_t)a.nq * AD + (int64_t)head * AD;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = 32 * dt + 8 * j + 4 * hh;
-                const float v0 = oacc[dt][4 * j], v1 = oacc[dt][4 * j + 1];
-                const float v2 = oacc[dt][4 * j + 2], v3 = oacc[dt][4 * j + 3];
-                *reinterpret_cast<u32x2*>(o + d) =
-                    (u32x2){cvt_bf16x2(v0 * inv, v1 * inv), cvt_bf16x2(v2 * inv, v3 * inv)};
-            }
     }
 }
 
-// Merges the chunks of the split tiles: for query i of head h,
+// Merges the pieces of a split tile: for query i of head h,
 // m* = max_c m_c, out = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c,
-// chunks in order.  Block (tile, KV group, quad x 4 + wave): 256 threads,
+// pieces in key order.  Block (tile, KV group, quad x 4 + wave): 256 threads,
 // thread = (query tid / 8, 16 consecutive d).
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, int nz) {
-    const int ut = blockIdx.x;
-    const int tile = a.causal ? a.ntiles - 1 - ut : ut;
-    const int nbt = tile_blocks(tile, a.n, a.causal);
-    if (nbt <= ACH) return;                              // written directly
-    const int nch = (nbt + ACH - 1) / ACH;
+    const int tile = blockIdx.x;
+    const int p = tile < a.ntiles - 1 - tile ? tile : a.ntiles - 1 - tile;
+    const int sg = tile == p ? 0 : 1;
+    const PairPlan pp = pair_plan(p, a);
+    const int s0 = sg == 0 ? 0 : pp.na;
+    const int s1 = sg == 0 ? pp.na : pp.total;
+    // the pieces: chunks of the pair whose block range meets [s0, s1)
+    auto meets = [&](int cc) {
+        const int l = chunk_lo(cc, pp.total, a.kch), h = chunk_lo(cc + 1, pp.total, a.kch);
+        return (l > s0 ? l : s0) < (h < s1 ? h : s1);
+    };
+    int npc = 0;
+    for (int cc = 0; cc < a.kch; ++cc) npc += meets(cc) ? 1 : 0;
+    if (npc <= 1) return;                                // one piece: written directly
     const int g = blockIdx.y;
     const int z = blockIdx.z >> 2, wv = blockIdx.z & 3;
     const int hsub = z * 4 + wv;
@@ -300,21 +410,24 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, int 
     const int qq = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
     const int64_t qi = (int64_t)tile * AQ + qq;
     if (qi >= a.n) return;
-    auto chunk = [&](int c) -> const float* {
-        return a.part + (((((int64_t)ut * a.cmax + c) * gridDim.y + g) * nz + z) * 4 + wv) * APART;
+    auto piece = [&](int cc) -> const float* {
+        const int64_t slot = ((int64_t)p * a.kch + cc) * 2 + sg;
+        return a.part + (((slot * gridDim.y + g) * nz + z) * 4 + wv) * APART;
     };
     float mx = -INFINITY;
-    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, chunk(c)[AQ * AD + qq]);
+    for (int cc = 0; cc < a.kch; ++cc)
+        if (meets(cc)) mx = fmaxf(mx, piece(cc)[AQ * AD + qq]);
     float acc[16], den = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-    for (int c = 0; c < nch; ++c) {
-        const float* pp = chunk(c);
-        const float w = __builtin_amdgcn_exp2f(pp[AQ * AD + qq] - mx);
-        den = den + w * pp[AQ * AD + AQ + qq];
+    for (int cc = 0; cc < a.kch; ++cc) {
+        if (!meets(cc)) continue;
+        const float* pw = piece(cc);
+        const float w = __builtin_amdgcn_exp2f(pw[AQ * AD + qq] - mx);
+        den = den + w * pw[AQ * AD + AQ + qq];
 #pragma unroll
         for (int e = 0; e < 16; e += 4) {
-            const float4 o = *reinterpret_cast<const float4*>(pp + qq * AD + d0 + e);
+            const float4 o = *reinterpret_cast<const float4*>(pw + qq * AD + d0 + e);
             acc[e] = acc[e] + w * o.x;
             acc[e + 1] = acc[e + 1] + w * o.y;
             acc[e + 2] = acc[e + 2] + w * o.z;
@@ -345,8 +458,15 @@ AttnArgs attn_args(int64_t n, int nq, int nkv, int causal) {
     a.rep = nq / nkv;
     a.causal = causal ? 1 : 0;
     a.ntiles = (int)((n + AQ - 1) / AQ);
-    const int nbmax = tile_blocks(a.ntiles - 1, n, a.causal);
-    a.cmax = (nbmax + ACH - 1) / ACH;
+    a.npairs = (a.ntiles + 1) / 2;
+    // chunks per pair: about AUNITS workgroups in all, chunks of at least
+    // AMINCH blocks
+    const int nz = (a.rep + 3) / 4;
+    const int64_t per = (int64_t)a.npairs * nkv * nz;
+    const int k = (int)((AUNITS + per - 1) / per);
+    const int t0 = pair_plan(0, a).total;             // the longest pair (causal: all about equal)
+    const int kmax = t0 / AMINCH > 1 ? t0 / AMINCH : 1;
+    a.kch = k < kmax ? k : kmax;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)AD);
     return a;
 }
@@ -356,9 +476,9 @@ AttnArgs attn_args(int64_t n, int nq, int nkv, int causal) {
 size_t attention_ws_bytes(int64_t n, int nq, int nkv, int causal) {
     if (n <= 0) return 0;
     const AttnArgs a = attn_args(n, nq, nkv, causal);
-    if (a.cmax <= 1) return 0;
+    if (a.kch <= 1) return 0;                        // every pair in one workgroup: no split tiles
     const int nz = (a.rep + 3) / 4;
-    return (size_t)a.ntiles * a.cmax * nkv * nz * 4 * APART * sizeof(float);
+    return (size_t)a.npairs * a.kch * 2 * nkv * nz * 4 * APART * sizeof(float);
 }
 
 hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int head_dim, int causal, void* out,
@@ -369,12 +489,12 @@ hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int hea
     a.qkv = static_cast<const uint16_t*>(qkv);
     a.out = static_cast<uint16_t*>(out);
     a.part = static_cast<float*>(ws);
-    if (a.cmax > 1 && !ws) return hipErrorInvalidValue;
+    if (a.kch > 1 && !ws) return hipErrorInvalidValue;
     const int nz = (a.rep + 3) / 4;
-    hipLaunchKernelGGL(attention_kernel, dim3((unsigned)(a.ntiles * a.cmax), (unsigned)nkv, (unsigned)nz), dim3(256),
+    hipLaunchKernelGGL(attention_kernel, dim3((unsigned)(a.npairs * a.kch), (unsigned)nkv, (unsigned)nz), dim3(256),
                        0, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.cmax <= 1) return e;
+    if (e != hipSuccess || a.kch <= 1) return e;
     hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)a.ntiles, (unsigned)nkv, (unsigned)(nz * 4)),
                        dim3(256), 0, s, a, nz);
     return hipGetLastError();

@@ -748,9 +748,9 @@ def test_attention_rank_peaked_and_flat_scores():
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_attention_rank_split_key_chunks(causal):
-    """n = 4100: 65 key blocks, so tiles are cut into chunks of 32 blocks
-    (non-causal: every tile; causal: the late ones) that a second kernel
-    merges; sampled rows around chunk and tile edges."""
+    """n = 4100: 129 query tiles in 65 (light, heavy) pairs, each pair's key
+    blocks cut into chunks of about 16 that a second kernel merges; sampled
+    rows around tile edges and the pair of the middle tile."""
     n, nq, nkv = 4100, 8, 2
     assert T.tp_attention_workspace_bytes(n, nq, nkv, causal=causal) > 0
     qkv = rnd((n, (nq + 2 * nkv) * 128), 1.0, 960 + causal, torch.bfloat16)
@@ -762,6 +762,9 @@ def test_attention_rank_split_key_chunks(causal):
 
 
 def test_attention_workspace_is_zero_for_short_sequences():
-    assert T.tp_attention_workspace_bytes(2048, 4, 1, causal=True) == 0
-    assert T.tp_attention_workspace_bytes(2048, 4, 1, causal=False) == 0
-    assert T.tp_attention_workspace_bytes(2049, 4, 1, causal=False) > 0
+    """Short sequences: every workgroup takes whole query tiles (a light and
+    a heavy one), so nothing is merged and no workspace is needed."""
+    assert T.tp_attention_workspace_bytes(512, 4, 1, causal=True) == 0
+    assert T.tp_attention_workspace_bytes(256, 4, 1, causal=False) == 0
+    assert T.tp_attention_workspace_bytes(8192, 4, 1, causal=True) > 0
+    assert T.tp_attention_workspace_bytes(4100, 8, 2, causal=False) > 0
