@@ -23,8 +23,10 @@
 //     the accumulator holds them (keys 4h..4h+3 and 8+4h..8+4h+3 of each 16
 //     for lane half h) -- and the V^T fragments come from row-major V in LDS
 //     through the transposing read ds_read_b64_tr_b16;
-//   * the running max moves only when a block raises it by more than 2^8
-//     (in probability), so the 64 accumulator rescales are mostly skipped;
+//   * a block's probabilities are first taken against the running max; only
+//     when one of them would exceed 2^13 (and on the first block) is the
+//     block's maximum computed, the max moved and the accumulators rescaled,
+//     so most blocks need neither the maximum nor the 64 rescales;
 //   * causal work balance: query tiles are paired heavy with light (tile p
 //     with tile nt-1-p, a near-constant number of key blocks per pair), each
 //     pair's concatenated key blocks are cut into k equal chunks, and one
@@ -69,7 +71,7 @@ constexpr int AK = 64;           // keys per block
 constexpr int APART = AQ * AD + 2 * AQ;   // floats of one wave's partial: O, m, l
 constexpr int AUNITS = 512;      // target workgroups: two per CU
 constexpr int AMINCH = 8;        // fewest key blocks per chunk
-constexpr float ATAU = 8.0f;     // running-max slack before a rescale (base-2 units)
+constexpr float ATAU_SUM = 8192.0f;   // largest accepted sum of a lane's 32 probabilities
 
 struct AttnArgs {
     const uint16_t* qkv;
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int q = 0; q < 16; ++q) oacc[t][q] = 0.0f;
-        float m = -INFINITY, lsum = 0.0f;            // running max (base-2 units) and sum
+        float m = -INFINITY, lsum = 0.0f;            // running max (base-2 units) and this lane's sum
 
         issue(blk_base(b0), ks0, koff);
         issue(blk_base(b0), vs0, voff);
@@ -230,39 +232,22 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
             for (int s = 0; s < 8; ++s)
                 qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                        rs, (uint32_t)(qi * row_b + (head * AD + 16 * s + 8 * hh) * 2), 0, 0));
-            // one key block kb; buffers alternate with its parity
-            auto step = [&](int kb, auto P) {
-                constexpr bool odd = decltype(P)::value != 0;
-                const uint16_t* kcur = odd ? ks1 : ks0;
-                const uint16_t* vcur = odd ? vs1 : vs0;
-                // K(kb), V(kb) landed (own DMA), then everyone's; all waves
-                // are done with block kb-1, whose buffers take block kb+1
-                __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0)
-                wg_barrier();
-                issue(blk_base(kb + 1), odd ? ks0 : ks1, koff);
-                issue(blk_base(kb + 1), odd ? vs0 : vs1, voff);
-                // S^T = K Q^T for the block's two 32-key tiles
-                f32x16 sc[2];
+            // S^T = K Q^T for a block's two 32-key tiles; all 16 fragment
+            // reads are issued before the first MFMA
+            auto scores = [&](const uint16_t* kbuf, f32x16 (&sc)[2]) {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int q = 0; q < 16; ++q) sc[tt][q] = 0.0f;
-                // fragment reads run 8 ahead of the MFMAs that use them
                 bf16x8 kf[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) kf[i] = kfrag(kcur, i >> 1, i & 1);
+                for (int i = 0; i < 16; ++i) kf[i] = kfrag(kbuf, i >> 1, i & 1);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + 8 < 16) kf[i + 8] = kfrag(kcur, (i + 8) >> 1, (i + 8) & 1);
+                for (int i = 0; i < 16; ++i)
                     sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], sc[i & 1], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            };
+            // softmax of block kb's scores sc, then O += V^T P^T from vbuf
+            auto softmax_pv = [&](int kb, f32x16 (&sc)[2], const uint16_t* vbuf) {
                 // lane half hh holds keys 8 j + 4 hh + i of each 32-key tile
                 if (mask_end && kb == b1 - 1) {
                     // keys past min(qi, n - 1) (causal) or past n - 1: key
@@ -275,33 +260,49 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
                         for (int q = 0; q < 16; ++q)
                             if (32 * tt + 8 * (q >> 2) + (q & 3) > lim) sc[tt][q] = -INFINITY;
                 }
-                float mloc = -INFINITY;
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) mloc = fmaxf(mloc, sc[tt][q]);
-                mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-                const float ms = mloc * a.scale_log2;
-                // the running max moves only when some query's block max
-                // passes it by more than ATAU (probabilities stay below
-                // 2^ATAU); the first block always sets it (m = -inf)
-                const bool grow = __any(ms > m + ATAU);
-                const float mn = grow ? fmaxf(m, ms) : m;
-                const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 1 if unchanged, 0 on the first block
-                const float nmn = -mn;
+                // probabilities against the running max m, kept while their
+                // sum over the lane's 32 keys (which bounds each) stays within
+                // ATAU_SUM; otherwise -- and on the first block, m = -inf --
+                // m moves to the block's maximum and the block is redone
+                f32x16 pr[2];
                 float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                const float nm = -m;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int q = 0; q < 16; ++q) {
-                        const float pr = __builtin_amdgcn_exp2f(fmaf(sc[tt][q], a.scale_log2, nmn));
-                        sc[tt][q] = pr;
-                        ps[q & 3] += pr;
+                        pr[tt][q] = __builtin_amdgcn_exp2f(fmaf(sc[tt][q], a.scale_log2, nm));
+                        ps[q & 3] += pr[tt][q];
                     }
                 float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                psum += __shfl_xor(psum, 32, 64);
-                lsum = lsum * alpha + psum;
-                m = mn;
+                if (__any(!(psum <= ATAU_SUM))) {           // also catches inf and NaN (m = -inf)
+                    float mloc = -INFINITY;
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) mloc = fmaxf(mloc, sc[tt][q]);
+                    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+                    const float mn = fmaxf(m, mloc * a.scale_log2);
+                    const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block
+                    const float nmn = -mn;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ps[e] = 0.0f;
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            pr[tt][q] = __builtin_amdgcn_exp2f(fmaf(sc[tt][q], a.scale_log2, nmn));
+                            ps[q & 3] += pr[tt][q];
+                        }
+                    psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                    lsum = lsum * alpha;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) oacc[t][q] *= alpha;
+                    m = mn;
+                }
+                lsum += psum;                               // this lane's 32 keys; halves meet at the end
                 // P^T fragments: K step (tt, q2) = accumulator values 8 q2 .. 8 q2 + 7
                 bf16x8 pf[2][2];
 #pragma unroll
@@ -310,15 +311,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
                     for (int q2 = 0; q2 < 2; ++q2) {
                         uint32_t w[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(sc[tt][8 * q2 + 2 * e], sc[tt][8 * q2 + 2 * e + 1]);
+                        for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(pr[tt][8 * q2 + 2 * e], pr[tt][8 * q2 + 2 * e + 1]);
                         pf[tt][q2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
                     }
-                if (grow) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-#pragma unroll
-                        for (int q = 0; q < 16; ++q) oacc[t][q] *= alpha;
-                }
                 // O^T += V^T P^T: the A fragment of (tt, q2) holds keys
                 // 32 tt + 16 q2 + {4 hh + 0..3, 8 + 4 hh + 0..3}, the order in
                 // which the score accumulators hold them
@@ -328,8 +323,21 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
                     for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
                         for (int dt = 0; dt < 4; ++dt)
-                            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vcur, 32 * tt + 16 * q2, dt),
+                            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vbuf, 32 * tt + 16 * q2, dt),
                                                                               pf[tt][q2], oacc[dt], 0, 0, 0);
+            };
+            // one key block kb; buffers alternate with its parity
+            auto step = [&](int kb, auto P) {
+                constexpr bool odd = decltype(P)::value != 0;
+                // K(kb), V(kb) landed (own DMA), then everyone's; all waves
+                // are done with block kb-1, whose buffers take block kb+1
+                __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0)
+                wg_barrier();
+                issue(blk_base(kb + 1), odd ? ks0 : ks1, koff);
+                issue(blk_base(kb + 1), odd ? vs0 : vs1, voff);
+                f32x16 sc[2];
+                scores(odd ? ks1 : ks0, sc);
+                softmax_pv(kb, sc, odd ? vs1 : vs0);
             };
             for (int kb = b0; kb < b1; kb += 2) {
                 step(kb, std::integral_constant<int, 0>());
@@ -349,6 +357,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0f70);
 
         if (!active) continue;
+        lsum += __shfl_xor(lsum, 32, 64);
         if (!whole) {
             // this segment's unnormalised O, running max and sum for the combine
             const int64_t slot = ((int64_t)p * a.kch + c) * 2 + sg;
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
 // Merges the pieces of a split tile: for query i of head h,
 // m* = max_c m_c, out = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c,
-// pieces in key order.  Block (tile, KV group, quad x 4 + wave): 256 threads,
+// pieces in key order, four at a time with the maximum carried over.  Block (tile, KV group, quad x 4 + wave): 256 threads,
 // thread = (query tid / 8, 16 consecutive d).
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, int nz) {
     const int tile = blockIdx.x;
@@ -414,25 +423,52 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, int 
         const int64_t slot = ((int64_t)p * a.kch + cc) * 2 + sg;
         return a.part + (((slot * gridDim.y + g) * nz + z) * 4 + wv) * APART;
     };
-    float mx = -INFINITY;
-    for (int cc = 0; cc < a.kch; ++cc)
-        if (meets(cc)) mx = fmaxf(mx, piece(cc)[AQ * AD + qq]);
-    float acc[16], den = 0.0f;
+    // pieces in groups of 4, all of a group's loads in flight together;
+    // the running max and sum carry across groups (online, in key order)
+    int cf = 0;
+    while (!meets(cf)) ++cf;
+    int cl = a.kch - 1;
+    while (!meets(cl)) --cl;
+    float mx = -INFINITY, den = 0.0f, acc[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-    for (int cc = 0; cc < a.kch; ++cc) {
-        if (!meets(cc)) continue;
-        const float* pw = piece(cc);
-        const float w = __builtin_amdgcn_exp2f(pw[AQ * AD + qq] - mx);
-        den = den + w * pw[AQ * AD + AQ + qq];
+    for (int g0 = cf; g0 <= cl; g0 += 4) {
+        float mg[4], lg[4];
+        float4 og[4][4];
 #pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-            const float4 o = *reinterpret_cast<const float4*>(pw + qq * AD + d0 + e);
-            acc[e] = acc[e] + w * o.x;
-            acc[e + 1] = acc[e + 1] + w * o.y;
-            acc[e + 2] = acc[e + 2] + w * o.z;
-            acc[e + 3] = acc[e + 3] + w * o.w;
+        for (int i = 0; i < 4; ++i) {
+            const int cc = g0 + i;
+            if (cc <= cl && meets(cc)) {
+                const float* pw = piece(cc);
+                mg[i] = pw[AQ * AD + qq];
+                lg[i] = pw[AQ * AD + AQ + qq];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) og[i][e] = *reinterpret_cast<const float4*>(pw + qq * AD + d0 + 4 * e);
+            } else {
+                mg[i] = -INFINITY;
+                lg[i] = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) og[i][e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
         }
+        const float gm = fmaxf(fmaxf(mx, fmaxf(mg[0], mg[1])), fmaxf(mg[2], mg[3]));
+        const float f = __builtin_amdgcn_exp2f(mx - gm);           // 0 before the first piece
+        den = den * f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = acc[e] * f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float w = __builtin_amdgcn_exp2f(mg[i] - gm);      // 0 for a missing piece
+            den = den + w * lg[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[4 * e] = acc[4 * e] + w * og[i][e].x;
+                acc[4 * e + 1] = acc[4 * e + 1] + w * og[i][e].y;
+                acc[4 * e + 2] = acc[4 * e + 2] + w * og[i][e].z;
+                acc[4 * e + 3] = acc[4 * e + 3] + w * og[i][e].w;
+            }
+        }
+        mx = gm;
     }
     const float inv = 1.0f / den;
     uint16_t* o = a.out + qi * (int64_t)a.nq * AD + (int64_t)head * AD + d0;
