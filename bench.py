@@ -406,6 +406,66 @@ def leg_qwen_fp32(reps):
             "note": "latency bound at this size (19 MB of fp32 weights per rank)"}
 
 
+def leg_load(reps):
+    """Checkpoint-style loading of one rank's MLP weights: rank 5 of TP=8
+    takes its gate and up rows and its down columns from fp32 tensors in host
+    memory into bf16 tables (only the shard crosses the host link)."""
+    w = synth.get("llama70b_prefill_tp8")
+    r, t = 5, w.tp
+    fl = w.f // t
+    g = torch.Generator().manual_seed(w.seed(synth.T_GATE))
+    full = [torch.empty((w.f, w.h), dtype=torch.float32).uniform_(-0.05, 0.05, generator=g) for _ in range(2)]
+    down = torch.empty((w.h, w.f), dtype=torch.float32).uniform_(-0.05, 0.05, generator=g)
+    gu = torch.empty((2 * fl, w.h), dtype=torch.bfloat16, device=DEV)
+    dn = torch.empty((w.h, fl), dtype=torch.bfloat16, device=DEV)
+    staging = torch.empty(T.tp_load_staging_bytes(fl, w.h, torch.float32, torch.bfloat16), dtype=torch.uint8,
+                          device=DEV)
+    host_bytes = 3 * fl * w.h * 4
+
+    def load(srcs):
+        T.tp_load_gate_up(srcs[0], 0, r, t, out=gu, staging=staging)
+        T.tp_load_gate_up(srcs[1], 1, r, t, out=gu, staging=staging)
+        T.tp_load_shard(srcs[2], 1, r, t, out=dn, staging=staging)
+
+    def timed(srcs):
+        load(srcs)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            load(srcs)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+
+    ms_pageable = timed((full[0], full[1], down))
+    pinned = [a.pin_memory() for a in (full[0], full[1], down)]
+    ms_pinned = timed(pinned)
+    # context: one plain contiguous pinned host -> device copy of the same bytes
+    chunk = pinned[0][r * fl:(r + 1) * fl]
+    buf = torch.empty(chunk.shape, dtype=torch.float32, device=DEV)
+    buf.copy_(chunk, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        buf.copy_(chunk, non_blocking=True)
+    torch.cuda.synchronize()
+    ms_copy = (time.perf_counter() - t0) / reps * 1e3
+    copy_gbps = chunk.numel() * 4 / ms_copy / 1e6
+    chunk_pg = full[0][r * fl:(r + 1) * fl]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        buf.copy_(chunk_pg)
+    torch.cuda.synchronize()
+    pageable_copy_gbps = chunk_pg.numel() * 4 / ((time.perf_counter() - t0) / reps * 1e3) / 1e6
+    return {"workload": w.name, "host_bytes": host_bytes,
+            "pageable_ms": ms_pageable, "pageable_GBps": host_bytes / ms_pageable / 1e6,
+            "pinned_ms": ms_pinned, "pinned_GBps": host_bytes / ms_pinned / 1e6,
+            "plain_pinned_copy_GBps": copy_gbps, "plain_pageable_copy_GBps": pageable_copy_gbps,
+            "pinned_frac_of_plain_copy": host_bytes / ms_pinned / 1e6 / copy_gbps,
+            "what": "gate + up rows and down columns of rank 5/8 from fp32 host tensors to bf16 device tables "
+                    "(wall clock, host link bound)"}
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
@@ -492,7 +552,7 @@ def main():
         f"down {dn_ms:.3f} reduce {rd_ms:.3f} -> {value:.1f} TFLOP/s")
 
     legs = {}
-    names = ["decode", "reduce8", "reduce16", "spnorm", "vocab", "attnproj", "qwen_fp32"] if a.legs == "all" else \
+    names = ["decode", "reduce8", "reduce16", "spnorm", "vocab", "attnproj", "qwen_fp32", "load"] if a.legs == "all" else \
         ([] if a.legs == "none" else a.legs.split(","))
     for nm in names:
         log(f"bench: leg {nm}")
@@ -510,6 +570,8 @@ def main():
             legs[nm] = leg_attnproj(10)
         elif nm == "qwen_fp32":
             legs[nm] = leg_qwen_fp32(50)
+        elif nm == "load":
+            legs[nm] = leg_load(3)
         torch.cuda.empty_cache()
 
     if a.copy_calib:

@@ -117,6 +117,58 @@ TP_API tp_status tp_shard_qkv(const void* wq, const void* wk, const void* wv,
                        int64_t n_q, int64_t n_kv, int64_t head_dim, int64_t h,
                        tp_dtype dt, int tp_rank, int tp_size, void* out, void* stream);
 
+/* ---- checkpoint-style loaders (load time) -------------------------------- */
+
+/* The weight loaders of [NANO22] §3-§5 straight from a checkpoint tensor in
+ * HOST memory, in the order [MINISGL] §8 (weight loading and sharding) gives
+ * to keep device memory at the shard's size: select the rank's shard, convert
+ * the dtype, copy it into the local parameter.  Only the shard crosses the
+ * host link (one strided 2-D copy on `stream`); the conversion runs on the
+ * GPU: fp32 -> bf16 rounds to nearest even (a NaN stays a NaN), bf16 -> fp32
+ * is exact, equal dtypes copy the bits.
+ *   src: HOST pointer (pageable or pinned) to the full tensor, row-major,
+ *        in src_dt; it must stay valid and unchanged until the stream has
+ *        passed the call (pageable sources are copied before the call
+ *        returns).
+ *   dst: DEVICE table in dst_dt; staging: DEVICE buffer, 16-byte aligned, of
+ *        at least tp_load_staging_bytes(chunk rows, chunk cols, src_dt,
+ *        dst_dt) bytes (0 bytes, NULL allowed, when the dtypes match); it
+ *        must not be reused until the stream has passed the call.
+ *   src_dt, dst_dt: TP_F32 or TP_BF16.
+ * Errors as for the shard selection above; TP_EWORKSPACE for a short
+ * staging buffer.  Bit-exact to the rule above. */
+TP_API tp_status tp_load_staging_bytes(int64_t rows, int64_t cols, tp_dtype src_dt, tp_dtype dst_dt,
+                                       size_t* bytes /*HOST*/);
+
+/* Column (dim 0) or row (dim 1) parallel loader ([NANO22] §3, §4):
+ * dst = src.narrow(dim, tp_rank S/t, S/t) in dst_dt.  src [rows, cols];
+ * dst [rows/t, cols] (dim 0) or [rows, cols/t] (dim 1); chunk = dst's shape. */
+TP_API tp_status tp_load_shard(const void* src /*HOST*/, tp_dtype src_dt, int64_t rows, int64_t cols, int dim,
+                               int tp_rank, int tp_size, void* dst, tp_dtype dst_dt, void* staging,
+                               size_t staging_bytes, void* stream);
+
+/* One projection of the fused gate_up table ([NANO22] §5, the merged
+ * column-parallel loader): shard_id 0 = gate, 1 = up.  The projection's
+ * segment of the rank's table is rows [shard_id f/t, (shard_id+1) f/t) (the
+ * first cut) and it receives rows [tp_rank f/t, (tp_rank+1) f/t) of src
+ * (the second cut, chunk(t)[tp_rank]).  src [f, h]; dst the rank's
+ * [2 f/t, h] table (other rows untouched); chunk [f/t, h].  Loading both
+ * projections gives tp_shard_gate_up's table. */
+TP_API tp_status tp_load_gate_up(const void* src /*HOST*/, tp_dtype src_dt, int shard_id, int64_t f, int64_t h,
+                                 int tp_rank, int tp_size, void* dst, tp_dtype dst_dt, void* staging,
+                                 size_t staging_bytes, void* stream);
+
+/* One projection of the merged QKV table ([NANO22] §5, the QKV loader, with
+ * the GQA replication of tp_kv_heads_for_rank): shard_id 0 = q (src
+ * [n_q hd, h]; segment rows [0, n_q/t hd) <- heads [r n_q/t, (r+1) n_q/t)),
+ * 1 = k and 2 = v (src [n_kv hd, h]; segments after q, then after k, each
+ * kv_count hd rows <- the rank's KV heads).  dst the rank's
+ * [(n_q/t + 2 kv_count) hd, h] table (other rows untouched); chunk = the
+ * segment.  Loading q, k and v gives tp_shard_qkv's table. */
+TP_API tp_status tp_load_qkv(const void* src /*HOST*/, tp_dtype src_dt, int shard_id, int64_t n_q, int64_t n_kv,
+                             int64_t head_dim, int64_t h, int tp_rank, int tp_size, void* dst, tp_dtype dst_dt,
+                             void* staging, size_t staging_bytes, void* stream);
+
 /* ---- column-parallel gate_up with the local SiLU(gate)*up ---------------- */
 
 /* act = SiLU(x . G^T) * (x . U^T), G = w_gate_up rows [0, f_local),

@@ -229,6 +229,71 @@ def shard_qkv(wq, wk, wv, n_q, n_kv, head_dim, tp_rank, tp_size) -> np.ndarray:
     return out
 
 
+# --- checkpoint-style loaders ----------------------------------------------
+# [NANO22] §3-§5 weight_loader applied to a full checkpoint tensor, in the
+# order of [MINISGL] §8 (weight loading and sharding): select the rank's
+# shard, convert the dtype, copy it into the local parameter.  Tensors are
+# float32 arrays or bfloat16 as uint16 bit arrays.
+
+def convert(a, to_bf16):
+    """The dtype conversion of copying into the parameter: fp32 -> bf16
+    rounds to nearest even (f32_to_bf16_bits), bf16 -> fp32 is exact, equal
+    dtypes copy."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return f32_to_bf16_bits(a) if to_bf16 else a.copy()
+    if a.dtype == np.uint16:
+        return a.copy() if to_bf16 else (a.astype(np.uint32) << 16).view(np.float32)
+    raise OracleError("convert: float32 or bf16 bits (uint16) expected")
+
+
+def load_shard(src, dim, tp_rank, tp_size, to_bf16) -> np.ndarray:
+    """Column (dim 0, [NANO22] §3) or row (dim 1, §4) parallel loader: the
+    rank's narrow(dim, r S/t, S/t) of the full tensor, then converted."""
+    if src.shape[dim] % tp_size:
+        raise OracleError("load_shard: size not divisible by tp_size")
+    sh = src.shape[dim] // tp_size
+    part = src[tp_rank * sh:(tp_rank + 1) * sh, :] if dim == 0 else src[:, tp_rank * sh:(tp_rank + 1) * sh]
+    return convert(part, to_bf16)
+
+
+def load_gate_up(table, src, shard_id, tp_rank, tp_size) -> None:
+    """[NANO22] §5 merged column-parallel loader, in place on the rank's
+    table: output_sizes = [f, f] (gate, up); the projection's segment starts
+    at sum(output_sizes[:shard_id]) / t and is output_sizes[shard_id] / t
+    rows long (first cut); it receives src.chunk(t, 0)[tp_rank] (second
+    cut), converted to the table's dtype."""
+    f = src.shape[0]
+    if f % tp_size:
+        raise OracleError("load_gate_up: f not divisible by tp_size")
+    output_sizes = [f, f]
+    off = sum(output_sizes[:shard_id]) // tp_size
+    size = output_sizes[shard_id] // tp_size
+    chunk = np.split(src, tp_size, axis=0)[tp_rank]
+    table[off:off + size] = convert(chunk, table.dtype == np.uint16)
+
+
+def load_qkv(table, src, shard_id, n_q, n_kv, head_dim, tp_rank, tp_size) -> None:
+    """[NANO22] §5 QKV loader, in place on the rank's table: segments q
+    (n_q/t heads), k and v (the rank's KV heads each) in that order; q takes
+    chunk(t)[tp_rank] of its heads, k and v take the heads
+    kv_heads_for_rank gives (the same chunk when t <= n_kv, the replicated
+    head r / (t / n_kv) otherwise, [GUIDE62] §2.2)."""
+    if n_q % tp_size:
+        raise OracleError("load_qkv: n_q not divisible by tp_size")
+    nq_r = n_q // tp_size
+    first, kvc = kv_heads_for_rank(n_kv, tp_rank, tp_size)
+    if shard_id == 0:
+        off, heads = 0, src[tp_rank * nq_r * head_dim:(tp_rank + 1) * nq_r * head_dim]
+    elif shard_id == 1:
+        off, heads = nq_r * head_dim, src[first * head_dim:(first + kvc) * head_dim]
+    elif shard_id == 2:
+        off, heads = (nq_r + kvc) * head_dim, src[first * head_dim:(first + kvc) * head_dim]
+    else:
+        raise OracleError("load_qkv: shard_id must be 0 (q), 1 (k) or 2 (v)")
+    table[off:off + heads.shape[0]] = convert(heads, table.dtype == np.uint16)
+
+
 # --- vocab parallel ----------------------------------------------------------
 
 def vocab_range(vocab, tp_rank, tp_size):

@@ -192,6 +192,109 @@ tp_status tp_shard_qkv(const void* wq, const void* wk, const void* wv, int64_t n
     return hip_status(e, "tp_shard_qkv");
 }
 
+// ---- checkpoint-style loaders -----------------------------------------------
+
+namespace {
+
+size_t load_staging(int64_t rows, int64_t cols, tp_dtype src_dt, tp_dtype dst_dt) {
+    if (src_dt == dst_dt) return 0;
+    return align256((size_t)rows * (size_t)cols * tpk::dtype_size(src_dt));
+}
+
+// common checks, then block [r0, r0 + rows) x [c0, c0 + cols) of the host
+// tensor (row length src_ld) into the table at (dr0, dc0), row length dst_ld
+tp_status load_block(const char* fn, const void* src, tp_dtype src_dt, int64_t src_ld, int64_t r0, int64_t c0,
+                     int64_t rows, int64_t cols, void* dst, tp_dtype dst_dt, int64_t dst_ld, int64_t dr0,
+                     int64_t dc0, void* staging, size_t staging_bytes, void* stream) {
+    const size_t need = load_staging(rows, cols, src_dt, dst_dt);
+    if (need > 0) {
+        if (!staging || staging_bytes < need)
+            return fail(TP_EWORKSPACE, "%s: staging buffer of %zu bytes needed, %zu given", fn, need,
+                        staging ? staging_bytes : (size_t)0);
+        if (((uintptr_t)staging & 15u) != 0) return fail(TP_EALIGN, "%s: staging must be 16-byte aligned", fn);
+    }
+    hipError_t e = tpk::launch_load_block(src, src_dt, src_ld, r0, c0, rows, cols, dst, dst_dt, dst_ld, dr0, dc0,
+                                          staging, as_stream(stream));
+    return hip_status(e, fn);
+}
+
+tp_status load_common(const char* fn, const void* src, tp_dtype src_dt, void* dst, tp_dtype dst_dt, int tp_rank,
+                      int tp_size) {
+    if (!src || !dst) return fail(TP_EINVAL, "%s: null pointer", fn);
+    if (!valid_dt(src_dt) || !valid_dt(dst_dt))
+        return fail(TP_EDTYPE, "%s: bad dtype pair %d -> %d", fn, (int)src_dt, (int)dst_dt);
+    return check_rank(tp_rank, tp_size);
+}
+
+}  // namespace
+
+tp_status tp_load_staging_bytes(int64_t rows, int64_t cols, tp_dtype src_dt, tp_dtype dst_dt, size_t* bytes) {
+    if (!bytes) return fail(TP_EINVAL, "tp_load_staging_bytes: null pointer");
+    if (!valid_dt(src_dt) || !valid_dt(dst_dt)) return fail(TP_EDTYPE, "tp_load_staging_bytes: bad dtype");
+    if (rows < 0 || cols < 0 || (cols > 0 && rows > kMaxElems / cols))
+        return fail(TP_EINVAL, "tp_load_staging_bytes: bad shape");
+    *bytes = load_staging(rows, cols, src_dt, dst_dt);
+    return ok();
+}
+
+tp_status tp_load_shard(const void* src, tp_dtype src_dt, int64_t rows, int64_t cols, int dim, int tp_rank,
+                        int tp_size, void* dst, tp_dtype dst_dt, void* staging, size_t staging_bytes, void* stream) {
+    if (tp_status st = load_common("tp_load_shard", src, src_dt, dst, dst_dt, tp_rank, tp_size)) return st;
+    if (dim != 0 && dim != 1) return fail(TP_EINVAL, "tp_load_shard: dim %d not 0 or 1", dim);
+    if (rows < 1 || cols < 1 || rows > kMaxElems / cols)
+        return fail(TP_EINVAL, "tp_load_shard: bad shape [%lld, %lld]", (long long)rows, (long long)cols);
+    const int64_t S = dim == 0 ? rows : cols;
+    if (S % tp_size)
+        return fail(TP_ESHAPE, "tp_load_shard: size %lld of dim %d not divisible by tp_size %d", (long long)S, dim,
+                    tp_size);
+    const int64_t sh = S / tp_size;
+    if (dim == 0)
+        return load_block("tp_load_shard", src, src_dt, cols, tp_rank * sh, 0, sh, cols, dst, dst_dt, cols, 0, 0,
+                          staging, staging_bytes, stream);
+    return load_block("tp_load_shard", src, src_dt, cols, 0, tp_rank * sh, rows, sh, dst, dst_dt, sh, 0, 0, staging,
+                      staging_bytes, stream);
+}
+
+tp_status tp_load_gate_up(const void* src, tp_dtype src_dt, int shard_id, int64_t f, int64_t h, int tp_rank,
+                          int tp_size, void* dst, tp_dtype dst_dt, void* staging, size_t staging_bytes, void* stream) {
+    if (tp_status st = load_common("tp_load_gate_up", src, src_dt, dst, dst_dt, tp_rank, tp_size)) return st;
+    if (shard_id != 0 && shard_id != 1) return fail(TP_EINVAL, "tp_load_gate_up: shard_id %d not 0 (gate) or 1 (up)", shard_id);
+    if (f < 1 || h < 1 || f > kMaxElems / h) return fail(TP_EINVAL, "tp_load_gate_up: bad shape");
+    if (f % tp_size)
+        return fail(TP_ESHAPE, "tp_load_gate_up: f %lld not divisible by tp_size %d", (long long)f, tp_size);
+    const int64_t fc = f / tp_size;
+    return load_block("tp_load_gate_up", src, src_dt, h, tp_rank * fc, 0, fc, h, dst, dst_dt, h, shard_id * fc, 0,
+                      staging, staging_bytes, stream);
+}
+
+tp_status tp_load_qkv(const void* src, tp_dtype src_dt, int shard_id, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                      int64_t h, int tp_rank, int tp_size, void* dst, tp_dtype dst_dt, void* staging,
+                      size_t staging_bytes, void* stream) {
+    if (tp_status st = load_common("tp_load_qkv", src, src_dt, dst, dst_dt, tp_rank, tp_size)) return st;
+    if (shard_id < 0 || shard_id > 2) return fail(TP_EINVAL, "tp_load_qkv: shard_id %d not 0 (q), 1 (k) or 2 (v)", shard_id);
+    if (n_q < 1 || n_kv < 1 || head_dim < 1 || h < 1 || n_q * head_dim > kMaxElems / h)
+        return fail(TP_EINVAL, "tp_load_qkv: bad shape");
+    if (n_q % tp_size)
+        return fail(TP_ESHAPE, "tp_load_qkv: n_q %lld not divisible by tp_size %d", (long long)n_q, tp_size);
+    int64_t kv0, kvc;
+    if (tp_status st = tp_kv_heads_for_rank(n_kv, tp_rank, tp_size, &kv0, &kvc)) return st;
+    const int64_t qc = n_q / tp_size;
+    // segment of the projection in the rank's table, and the rows of the
+    // full projection it takes (whole heads of head_dim rows)
+    int64_t seg, first, count;
+    if (shard_id == 0) {
+        seg = 0;
+        first = tp_rank * qc;
+        count = qc;
+    } else {
+        seg = shard_id == 1 ? qc : qc + kvc;
+        first = kv0;
+        count = kvc;
+    }
+    return load_block("tp_load_qkv", src, src_dt, h, first * head_dim, 0, count * head_dim, h, dst, dst_dt, h,
+                      seg * head_dim, 0, staging, staging_bytes, stream);
+}
+
 // ---- GEMMs --------------------------------------------------------------------
 
 tp_status tp_gate_up_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_dtype dt, size_t* bytes) {

@@ -59,6 +59,9 @@ namespace tpk {
 hipError_t launch_copy2d(const void* src, int64_t src_ld_bytes, void* dst, int64_t dst_ld_bytes,
                          int64_t rows, int64_t row_bytes, hipStream_t s);
 
+hipError_t launch_load_block(const void* src_host, tp_dtype src_dt, int64_t src_ld, int64_t r0, int64_t c0,
+                             int64_t rows, int64_t cols, void* dst, tp_dtype dst_dt, int64_t dst_ld, int64_t dr0,
+                             int64_t dc0, void* staging, hipStream_t s);
 hipError_t launch_ring_reduce(const void* const* parts, int t, int64_t K, tp_dtype in_dt,
                               void* out, tp_dtype out_dt, tp_order order, hipStream_t s);
 

@@ -49,6 +49,10 @@ _SIGS = {
     "tp_shard_gate_up": (_int, [_vp, _vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
     "tp_kv_heads_for_rank": (_int, [_i64, _int, _int, _i64p, _i64p]),
     "tp_shard_qkv": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp]),
+    "tp_load_staging_bytes": (_int, [_i64, _i64, _int, _int, _szp]),
+    "tp_load_shard": (_int, [_vp, _int, _i64, _i64, _int, _int, _int, _vp, _int, _vp, _sz, _vp]),
+    "tp_load_gate_up": (_int, [_vp, _int, _int, _i64, _i64, _int, _int, _vp, _int, _vp, _sz, _vp]),
+    "tp_load_qkv": (_int, [_vp, _int, _int, _i64, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _sz, _vp]),
     "tp_gate_up_workspace_bytes": (_int, [_i64, _i64, _i64, _int, _szp]),
     "tp_gate_up_act_rank": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp, _sz, _vp]),
     "tp_linear_workspace_bytes": (_int, [_i64, _i64, _i64, _int, _szp]),
@@ -169,6 +173,66 @@ def tp_shard_gate_up(gate, up, tp_rank, tp_size, out=None, stream=None):
     po = _dev(out, "out", gate.dtype, shape)
     _check(lib().tp_shard_gate_up(pg, pu, f, h, _dt(gate.dtype), tp_rank, tp_size, po,
                                   _stream(stream)))
+    return out
+
+
+# ---- checkpoint-style loaders ------------------------------------------------
+
+def _host(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.is_cuda:
+        raise ValueError(f"{name} must be a host (CPU) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def tp_load_staging_bytes(rows, cols, src_dtype, dst_dtype) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().tp_load_staging_bytes(rows, cols, _dt(src_dtype), _dt(dst_dtype), ctypes.byref(b)))
+    return b.value
+
+
+def _staging(rows, cols, src_dtype, out, staging):
+    return _workspace(tp_load_staging_bytes(rows, cols, src_dtype, out.dtype), out.device, staging)
+
+
+def tp_load_shard(src, dim, tp_rank, tp_size, dtype=torch.bfloat16, out=None, staging=None, stream=None):
+    rows, cols = src.shape
+    shape = (rows // max(tp_size, 1), cols) if dim == 0 else (rows, cols // max(tp_size, 1))
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device="cuda")
+    ps = _host(src, "src")
+    po = _dev(out, "out", None, shape)
+    pw, nw = _staging(shape[0], shape[1], src.dtype, out, staging)
+    _check(lib().tp_load_shard(ps, _dt(src.dtype), rows, cols, dim, tp_rank, tp_size, po, _dt(out.dtype), pw, nw,
+                               _stream(stream)))
+    return out
+
+
+def tp_load_gate_up(src, shard_id, tp_rank, tp_size, out, staging=None, stream=None):
+    f, h = src.shape
+    ps = _host(src, "src")
+    po = _dev(out, "out", None, (2 * (f // max(tp_size, 1)), h))
+    pw, nw = _staging(f // max(tp_size, 1), h, src.dtype, out, staging)
+    _check(lib().tp_load_gate_up(ps, _dt(src.dtype), shard_id, f, h, tp_rank, tp_size, po, _dt(out.dtype), pw, nw,
+                                 _stream(stream)))
+    return out
+
+
+def tp_load_qkv(src, shard_id, n_q, n_kv, head_dim, tp_rank, tp_size, out, staging=None, stream=None):
+    h = src.shape[1]
+    _, kvc = tp_kv_heads_for_rank(n_kv, tp_rank, tp_size)
+    nq_r = n_q // max(tp_size, 1)
+    ps = _host(src, "src")
+    po = _dev(out, "out", None, ((nq_r + 2 * kvc) * head_dim, h))
+    rows = (nq_r if shard_id == 0 else kvc) * head_dim
+    pw, nw = _staging(rows, h, src.dtype, out, staging)
+    _check(lib().tp_load_qkv(ps, _dt(src.dtype), shard_id, n_q, n_kv, head_dim, h, tp_rank, tp_size, po,
+                             _dt(out.dtype), pw, nw, _stream(stream)))
     return out
 
 

@@ -227,3 +227,42 @@ def test_rs_add_rmsnorm_errors():
     assert st == 1 and "partials[1]" in msg
     lo, hi = ctypes.c_int64(), ctypes.c_int64()
     assert L.tp_sp_rows(8, 3, 2, ctypes.byref(lo), ctypes.byref(hi)) == 1
+
+
+@no_gpu
+def test_load_errors():
+    L = T.lib()
+    sz = ctypes.c_size_t()
+    assert L.tp_load_staging_bytes(4, 6, 0, 1, ctypes.byref(sz)) == 0 and sz.value == 256   # 4*6 fp32, 256-aligned
+    assert L.tp_load_staging_bytes(4, 6, 1, 1, ctypes.byref(sz)) == 0 and sz.value == 0     # same dtype: none
+    st, _ = _status(L.tp_load_staging_bytes, 4, 6, 9, 1, ctypes.byref(sz))
+    assert st == 3
+    # tp_load_shard(src, src_dt, rows, cols, dim, rank, t, dst, dst_dt, staging, bytes, stream)
+    st, msg = _status(L.tp_load_shard, NULL, 0, 4, 4, 0, 0, 2, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 1 and "null" in msg
+    st, _ = _status(L.tp_load_shard, DUMMY, 0, 4, 4, 2, 0, 2, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 1                    # dim
+    st, msg = _status(L.tp_load_shard, DUMMY, 0, 5, 4, 0, 0, 2, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 2 and "divisible" in msg
+    st, _ = _status(L.tp_load_shard, DUMMY, 5, 4, 4, 0, 0, 2, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 3                    # source dtype
+    st, _ = _status(L.tp_load_shard, DUMMY, 0, 4, 4, 0, 3, 2, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 1                    # rank
+    st, msg = _status(L.tp_load_shard, DUMMY, 0, 64, 64, 0, 0, 2, DUMMY, 1, DUMMY, 1024, NULL)
+    assert st == 6 and "staging" in msg   # 32 x 64 fp32 = 8 KiB needed
+    st, msg = _status(L.tp_load_shard, DUMMY, 0, 64, 64, 0, 0, 2, DUMMY, 1, NULL, 0, NULL)
+    assert st == 6
+    st, msg = _status(L.tp_load_shard, DUMMY, 0, 64, 64, 0, 0, 2, DUMMY, 1, ctypes.c_void_p(0x1008), 1 << 20, NULL)
+    assert st == 4 and "aligned" in msg
+    # tp_load_gate_up(src, src_dt, shard_id, f, h, rank, t, dst, dst_dt, staging, bytes, stream)
+    st, _ = _status(L.tp_load_gate_up, DUMMY, 0, 2, 8, 4, 0, 2, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 1                    # shard id
+    st, _ = _status(L.tp_load_gate_up, DUMMY, 0, 0, 6, 4, 0, 4, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 2                    # 6 rows over 4 ranks
+    # tp_load_qkv(src, src_dt, shard_id, n_q, n_kv, hd, h, rank, t, dst, dst_dt, staging, bytes, stream)
+    st, _ = _status(L.tp_load_qkv, DUMMY, 0, 3, 8, 2, 4, 8, 0, 2, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 1                    # shard id
+    st, _ = _status(L.tp_load_qkv, DUMMY, 0, 1, 12, 8, 4, 8, 0, 3, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 2                    # 8 kv heads over 3 ranks
+    st, _ = _status(L.tp_load_qkv, DUMMY, 0, 0, 6, 2, 4, 8, 0, 4, DUMMY, 1, DUMMY, 4096, NULL)
+    assert st == 2                    # n_q 6 over 4 ranks

@@ -272,3 +272,28 @@ def test_llama70b_attnproj_tp16_attention_core_sampled():
     got = f64_bits(bits(out[rows]), torch.bfloat16)
     for h in range(nq):
         assert relf(got[:, h * 128:(h + 1) * 128], ref[:, h * 128:(h + 1) * 128]) <= 1e-2
+
+
+def test_llama70b_prefill_tp8_checkpoint_load():
+    """The loaders at the benchmarked shapes: rank 5 of TP=8 takes its gate
+    and up rows and its down columns straight from fp32 checkpoint tensors in
+    host memory ([28672, 8192] and [8192, 28672]) into bf16 tables; compared
+    in full with the oracle's loaders."""
+    w = synth.get("llama70b_prefill_tp8")
+    r, t = 5, w.tp
+    fl = w.f // t
+    gate = synth.normal((w.f, w.h), 0.02, w.seed(synth.T_GATE), torch.float32)
+    up = synth.normal((w.f, w.h), 0.02, w.seed(synth.T_UP), torch.float32)
+    gu = torch.empty((2 * fl, w.h), dtype=torch.bfloat16, device=DEV)
+    T.tp_load_gate_up(gate, 0, r, t, out=gu)
+    T.tp_load_gate_up(up, 1, r, t, out=gu)
+    torch.cuda.synchronize()
+    ref = np.empty((2 * fl, w.h), dtype=np.uint16)
+    oracle.load_gate_up(ref, gate.numpy(), 0, r, t)
+    oracle.load_gate_up(ref, up.numpy(), 1, r, t)
+    assert np.array_equal(bits(gu), ref)
+    del gate, up, gu
+    down = synth.normal((w.h, w.f), 0.02, w.seed(synth.T_DOWN), torch.float32)
+    dn = T.tp_load_shard(down, 1, r, t, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(dn), oracle.load_shard(down.numpy(), 1, r, t, True))

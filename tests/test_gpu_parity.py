@@ -768,3 +768,77 @@ def test_attention_workspace_is_zero_for_short_sequences():
     assert T.tp_attention_workspace_bytes(256, 4, 1, causal=False) == 0
     assert T.tp_attention_workspace_bytes(8192, 4, 1, causal=True) > 0
     assert T.tp_attention_workspace_bytes(4100, 8, 2, causal=False) > 0
+
+# --------------------------------------------------------------------------
+# checkpoint-style loaders: host checkpoint tensor -> the rank's device
+# table, bit-exact against the oracle's loaders
+# --------------------------------------------------------------------------
+
+def host_np(t):
+    """numpy view of a host tensor in the oracle's convention (bf16 as bits)."""
+    return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def host_tensor(shape, seed, dtype, pinned=False):
+    a = synth.normal(shape, 1.0, seed, torch.float32)
+    a[0, :4] = torch.tensor([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130])   # ties, subnormal
+    a = a.to(dtype)
+    return a.pin_memory() if pinned else a
+
+
+@pytest.mark.parametrize("src_dt,dst_dt", [(torch.float32, torch.bfloat16), (torch.bfloat16, torch.bfloat16),
+                                           (torch.bfloat16, torch.float32), (torch.float32, torch.float32)])
+@pytest.mark.parametrize("rows,cols,t", [(96, 160, 4), (48, 150, 2), (64, 64, 1), (40, 24, 8)])
+@pytest.mark.parametrize("dim", [0, 1])
+def test_load_shard_matches_oracle(src_dt, dst_dt, rows, cols, t, dim):
+    """Column and row cuts, with and without conversion; 150 columns (and 75
+    after a row cut) take the element-wise conversion."""
+    if (rows if dim == 0 else cols) % t:
+        pytest.skip("not divisible")
+    src = host_tensor((rows, cols), 1300 + rows + cols + t, src_dt)
+    for r in range(t):
+        out = T.tp_load_shard(src, dim, r, t, dtype=dst_dt)
+        torch.cuda.synchronize()
+        ref = oracle.load_shard(host_np(src), dim, r, t, dst_dt == torch.bfloat16)
+        assert np.array_equal(bits(out), ref.view(np.uint16 if dst_dt == torch.bfloat16 else np.uint32))
+
+
+def test_load_shard_from_pinned_memory_and_caller_staging():
+    src = host_tensor((64, 256), 1400, torch.float32, pinned=True)
+    staging = torch.empty(T.tp_load_staging_bytes(16, 256, torch.float32, torch.bfloat16), dtype=torch.uint8,
+                          device=DEV)
+    out = torch.full((16, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
+    T.tp_load_shard(src, 0, 3, 4, out=out, staging=staging)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), oracle.load_shard(host_np(src), 0, 3, 4, True))
+
+
+@pytest.mark.parametrize("n_q,n_kv,t", [(8, 2, 2), (8, 2, 8), (16, 4, 4), (4, 4, 2)])
+def test_load_qkv_and_gate_up_tables(n_q, n_kv, t):
+    """One projection per call into the rank's merged table (other rows
+    untouched until their call), fp32 checkpoint -> bf16 table; equal to the
+    oracle's loaders and to tp_shard_qkv / tp_shard_gate_up of the converted
+    full tensors (GQA replication when t > n_kv)."""
+    hd, h, f = 16, 72, 24 * t
+    wq = host_tensor((n_q * hd, h), 1500 + t, torch.float32)
+    wk = host_tensor((n_kv * hd, h), 1501 + t, torch.float32)
+    wv = host_tensor((n_kv * hd, h), 1502 + t, torch.float32)
+    gate = host_tensor((f, h), 1503 + t, torch.float32)
+    up = host_tensor((f, h), 1504 + t, torch.float32)
+    dev = [a.to(DEV).to(torch.bfloat16) for a in (wq, wk, wv, gate, up)]
+    for r in range(t):
+        _, kvc = T.tp_kv_heads_for_rank(n_kv, r, t)
+        table = torch.full(((n_q // t + 2 * kvc) * hd, h), float("nan"), dtype=torch.bfloat16, device=DEV)
+        ref = np.full(table.shape, 0x7FC0, dtype=np.uint16)
+        for sid in (1, 2, 0):
+            T.tp_load_qkv((wq, wk, wv)[sid], sid, n_q, n_kv, hd, r, t, out=table)
+            oracle.load_qkv(ref, host_np((wq, wk, wv)[sid]), sid, n_q, n_kv, hd, r, t)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(table), ref)
+        assert torch.equal(table.view(torch.int16),
+                           T.tp_shard_qkv(dev[0], dev[1], dev[2], n_q, n_kv, hd, r, t).view(torch.int16))
+        gu = torch.full((2 * f // t, h), float("nan"), dtype=torch.bfloat16, device=DEV)
+        T.tp_load_gate_up(up, 1, r, t, out=gu)
+        T.tp_load_gate_up(gate, 0, r, t, out=gu)
+        torch.cuda.synchronize()
+        assert torch.equal(gu.view(torch.int16), T.tp_shard_gate_up(dev[3], dev[4], r, t).view(torch.int16))

@@ -779,3 +779,123 @@ def test_attention_rows_are_independent():
     full = oracle.attention_rank(qkv, nq, nkv, d, True)
     rows = [18, 0, 7]
     assert np.array_equal(oracle.attention_rank(qkv, nq, nkv, d, True, rows=rows), full[rows])
+
+
+# --------------------------------------------------------------------------
+# Checkpoint-style loaders: [NANO22] §3-§5 weight_loader on the full tensor,
+# shard selected before the dtype conversion ([MINISGL] §8)
+# --------------------------------------------------------------------------
+
+def _bits_to_f64(b):
+    return oracle.bf16_bits_to_f64(b)
+
+
+def test_loader_worked_examples():
+    """The printed runs of [NANO22] §3 (column cut), §4 (row cut) and §5
+    (merged q/k/v and gate/up, one projection per call), through the loaders
+    with a float32 -> bfloat16 conversion (all values are exact in bf16)."""
+    g = gold("nano22_column_parallel.json")
+    full = np.array([[v] * g["in_features"] for v in g["full_row_labels"]], dtype=np.float32)
+    for r, rows in g["rank_rows"].items():
+        got = _bits_to_f64(oracle.load_shard(full, 0, int(r), g["tp_size"], True))
+        assert got.shape == tuple(g["rank_weight_shape"]) and got[:, 0].tolist() == rows
+    g = gold("nano22_row_parallel.json")
+    w = np.array(g["weight"], dtype=np.float32)
+    for r, cols in g["rank_cols"].items():
+        assert _bits_to_f64(oracle.load_shard(w, 1, int(r), g["tp_size"], True)).tolist() == cols
+    g = gold("nano22_merged_double_cut.json")
+    q = g["qkv"]
+    hd, hid, t = q["head_size"], q["hidden"], q["tp_size"]
+    srcs = [_by_head(q["num_q_heads"], q["q_base"], hd, hid), _by_head(q["num_kv_heads"], q["k_base"], hd, hid),
+            _by_head(q["num_kv_heads"], q["v_base"], hd, hid)]
+    for r in range(t):
+        table = np.zeros(((q["num_q_heads"] // t + 2 * (q["num_kv_heads"] // t)) * hd, hid), dtype=np.uint16)
+        for sid in (2, 0, 1):                          # any order of the three calls
+            oracle.load_qkv(table, srcs[sid], sid, q["num_q_heads"], q["num_kv_heads"], hd, r, t)
+        c = _bits_to_f64(table)[:, 0].tolist()
+        exp = q[f"rank{r}"]
+        nq, nk = len(exp["q"]), len(exp["k"])
+        assert c[:nq] == exp["q"] and c[nq:nq + nk] == exp["k"] and c[nq + nk:] == exp["v"]
+    gu = g["gate_up"]
+    table = np.zeros((2 * gu["intermediate"] // gu["tp_size"], gu["hidden"]), dtype=np.float32)
+    oracle.load_gate_up(table, np.full((gu["intermediate"], gu["hidden"]), gu["gate_fill"], np.float32), 0, 0,
+                        gu["tp_size"])
+    oracle.load_gate_up(table, np.full((gu["intermediate"], gu["hidden"]), gu["up_fill"], np.float32), 1, 0,
+                        gu["tp_size"])
+    half = gu["intermediate"] // gu["tp_size"]
+    assert table[:half, 0].tolist() == gu["rank0"]["gate_segment"]
+    assert table[half:, 0].tolist() == gu["rank0"]["up_segment"]
+
+
+def test_loader_conversion_is_torch_copy_into_bf16_param():
+    """The pages' loaders end in param.data.copy_(loaded_weight): copying a
+    float32 chunk into a bfloat16 parameter is torch's round to nearest even
+    (ties, subnormals and infinities included; a NaN stays a NaN); bf16 ->
+    fp32 is exact."""
+    rng = np.random.default_rng(21)
+    src = rng.standard_normal((16, 64)).astype(np.float32)
+    src[0, :8] = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, np.inf, -np.inf, np.nan, 0.0],
+                          dtype=np.float32)
+    src[1, :4] = np.array([3.0e38, -3.0e38, 1e-40, -0.0], dtype=np.float32)
+    for dim in (0, 1):
+        for r in range(4):
+            got = oracle.load_shard(src, dim, r, 4, True)
+            chunk = torch.from_numpy(src).chunk(4, dim)[r]
+            param = torch.empty(chunk.shape, dtype=torch.bfloat16)
+            param.copy_(chunk)
+            ref = param.view(torch.int16).numpy().view(np.uint16)
+            # a NaN stays a NaN (its payload bits are not fixed)
+            nan_got = (got & 0x7F80) == 0x7F80
+            nan_got &= (got & 0x007F) != 0
+            assert np.array_equal(nan_got, torch.isnan(param).numpy())
+            assert np.array_equal(got[~nan_got], ref[~nan_got])
+    b = oracle.f32_to_bf16_bits(src)
+    back = oracle.load_shard(b, 0, 1, 2, False)
+    ref = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).chunk(2, 0)[1].float().numpy()
+    assert np.array_equal(back.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("n_q,n_kv,t", [(8, 2, 2), (8, 2, 8), (64, 8, 16), (4, 4, 4)])
+def test_loader_tables_equal_shard_then_convert(n_q, n_kv, t):
+    """Loading the projections one at a time gives the merged table of the
+    full tensors' shard selection ([NANO22] §5 / [GUIDE62] §2.2 replication),
+    converted; the segment order is q, k, v and gate, up."""
+    rng = np.random.default_rng(n_q * 100 + t)
+    hd, h, f = 4, 6, 8 * t
+    wq = rng.standard_normal((n_q * hd, h)).astype(np.float32)
+    wk = rng.standard_normal((n_kv * hd, h)).astype(np.float32)
+    wv = rng.standard_normal((n_kv * hd, h)).astype(np.float32)
+    gate = rng.standard_normal((f, h)).astype(np.float32)
+    up = rng.standard_normal((f, h)).astype(np.float32)
+    for r in range(t):
+        ref = oracle.shard_qkv(oracle.f32_to_bf16_bits(wq), oracle.f32_to_bf16_bits(wk), oracle.f32_to_bf16_bits(wv),
+                               n_q, n_kv, hd, r, t)
+        table = np.full(ref.shape, 0xFFFF, dtype=np.uint16)
+        for sid, src in enumerate((wq, wk, wv)):
+            oracle.load_qkv(table, src, sid, n_q, n_kv, hd, r, t)
+        assert np.array_equal(table, ref)
+        ref = oracle.shard_gate_up(oracle.f32_to_bf16_bits(gate), oracle.f32_to_bf16_bits(up), r, t)
+        table = np.full(ref.shape, 0xFFFF, dtype=np.uint16)
+        oracle.load_gate_up(table, up, 1, r, t)
+        oracle.load_gate_up(table, gate, 0, r, t)
+        assert np.array_equal(table, ref)
+
+
+def test_loader_wrong_segment_or_chunk_is_caught():
+    """Putting k where v belongs, or taking the chunk of the wrong rank, fails
+    the comparison with the shard selection of the full tensors."""
+    rng = np.random.default_rng(3)
+    n_q, n_kv, hd, h, t = 4, 2, 2, 3, 2
+    wq = rng.standard_normal((n_q * hd, h)).astype(np.float32)
+    wk = rng.standard_normal((n_kv * hd, h)).astype(np.float32)
+    wv = rng.standard_normal((n_kv * hd, h)).astype(np.float32)
+    ref = oracle.shard_qkv(wq, wk, wv, n_q, n_kv, hd, 1, t)
+    table = np.zeros_like(ref)
+    oracle.load_qkv(table, wq, 0, n_q, n_kv, hd, 1, t)
+    oracle.load_qkv(table, wv, 1, n_q, n_kv, hd, 1, t)      # v into k's segment
+    oracle.load_qkv(table, wk, 2, n_q, n_kv, hd, 1, t)
+    assert not np.array_equal(table, ref)
+    other = np.zeros_like(ref)
+    for sid, src in enumerate((wq, wk, wv)):
+        oracle.load_qkv(other, src, sid, n_q, n_kv, hd, 0, t)   # rank 0's chunks
+    assert not np.array_equal(other, ref)
