@@ -137,7 +137,12 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int64_t gm, int64_t gn
     if (EPI == EPI_STORE_F32) {
         float* dst = static_cast<float*>(p.C) + gm * p.N + gn;
         if (p.vec_out && gn + 3 < p.N) {
-            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            // a final fp32 output (the LM head's logits) is not read back
+            // here: non-temporal stores (135 -> 116 us at the Qwen3 vocab
+            // shard; the same hint on 8-byte bf16 stores made o_proj 2.5x
+            // slower)
+            typedef float f32x4v __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store((f32x4v){v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4v*>(dst));
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -809,6 +814,72 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dl_kernel(GemmArgs p) 
     gemm_epilogue<BM, BN, WM, WN, EPI>(p, acc, m0, n0, wm, wn, lane);
 }
 
+// fp32 plain-store epilogue of the 16x16x32 kernels through LDS (the LM
+// head's logits): the results are written to LDS in the MFMA's lane layout
+// (4 consecutive output columns of one token) and read back as whole 1 KiB
+// output rows, so each wave store is 1 KiB of contiguous output instead of
+// 16 rows x 64 bytes; they go out with non-temporal stores (the logits are
+// not read back here).  Two passes of 128 token rows (the waves with wm = 0,
+// then wm = 1); the 16-byte slot s of token row t sits at s ^ (t & 15), so
+// writes and reads are conflict-free.  Same-box A/B at the Qwen3 vocab
+// shard: 105 vs 118 us on one machine, equal (118 us) on another; the same
+// staging for bf16 outputs (o_proj, down) measured no gain, so they store
+// directly.  The caller's LDS ring is free: no DMA is in
+// flight after the last K step, and a barrier waits for the last fragment
+// reads.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void staged_store_f32(const GemmArgs& p, f32x4 (&acc)[BN / WN / 16][BM / WM / 16],
+                                                 uint8_t* lds, int64_t m0, int64_t n0, int wm, int wn, int lane) {
+    constexpr int WTM = BM / WM;
+    constexpr int TM = WTM / 16, TN = BN / WN / 16;
+    constexpr int NT = WM * WN * 64;
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const int tl = lane & 15, cl = 4 * (lane >> 4);
+    float* C = static_cast<float*>(p.C);
+    __builtin_amdgcn_s_waitcnt(0x0070);                 // vmcnt(0) lgkmcnt(0)
+    bare_barrier();
+#pragma unroll
+    for (int h = 0; h < WM; ++h) {
+        if (h > 0) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);         // lgkmcnt(0): last pass's reads done
+            bare_barrier();
+        }
+        if (wm == h) {
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+                    const int t = j * 16 + tl;
+                    const int col = b_tile_row_of<BN, WN, false, 16>(i, wn) + cl;
+                    float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                    if (p.bias) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (n0 + col + q < p.N) v[q] = v[q] + bf16_to_f32(p.bias[n0 + col + q]);
+                    }
+                    const int slot = (col >> 2) ^ (t & 15);
+                    *reinterpret_cast<f32x4v*>(lds + t * (BN * 4) + slot * 16) = (f32x4v){v[0], v[1], v[2], v[3]};
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): this pass's writes done
+        bare_barrier();
+        constexpr int PIECES = WTM * BN / 4;                // 16-byte pieces of the pass
+#pragma unroll 4
+        for (int pc = threadIdx.x; pc < PIECES; pc += NT) {
+            const int t = pc / (BN / 4), k = pc % (BN / 4);
+            const int64_t gm = m0 + h * WTM + t, gn = n0 + 4 * k;
+            if (gm >= p.M || gn >= p.N) continue;
+            const f32x4v x = *reinterpret_cast<const f32x4v*>(lds + t * (BN * 4) + 16 * (k ^ (t & 15)));
+            float* dst = C + gm * p.N + gn;
+            if (gn + 3 < p.N) {
+                __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(dst));
+            } else {
+                for (int e = 0; gn + e < p.N; ++e) dst[e] = x[e];
+            }
+        }
+    }
+}
+
 // Deep-pipelined direct-to-LDS kernel with 16x16x32 MFMAs (16-byte-aligned
 // operands, K a multiple of 8), for the 256 x 256 tiles.
 //   * MFMA shape: v_mfma_f32_16x16x32_bf16 moves half the accumulator data
@@ -1016,6 +1087,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
                     make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             }
         return;
+    }
+    if constexpr (EPI == EPI_STORE_F32) {
+        if (p.vec_out) {
+            staged_store_f32<BM, BN, WM, WN>(p, acc, lds, m0, n0, wm, wn, lane);
+            return;
+        }
     }
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
