@@ -260,21 +260,35 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
                         for (int q = 0; q < 16; ++q)
                             if (32 * tt + 8 * (q >> 2) + (q & 3) > lim) sc[tt][q] = -INFINITY;
                 }
-                // probabilities against the running max m, kept while their
-                // sum over the lane's 32 keys (which bounds each) stays within
-                // ATAU_SUM; otherwise -- and on the first block, m = -inf --
-                // m moves to the block's maximum and the block is redone
-                f32x16 pr[2];
-                float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                const float nm = -m;
+                // probabilities against the running max m, packed to bf16 as
+                // the P^T fragments (K step (tt, q2) = accumulator values
+                // 8 q2 .. 8 q2 + 7) and summed as packed (one bf16 dot
+                // product with (1, 1) per pair: the sum of exactly the
+                // weights the P.V product uses).  Kept while the sum over the
+                // lane's 32 keys (which bounds each) stays within ATAU_SUM;
+                // otherwise -- and on the first block, m = -inf -- m moves to
+                // the block's maximum and the block is redone.
+                bf16x8 pf[2][2];
+                auto probs = [&](float nmx) -> float {
+                    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+                    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        pr[tt][q] = __builtin_amdgcn_exp2f(fmaf(sc[tt][q], a.scale_log2, nm));
-                        ps[q & 3] += pr[tt][q];
-                    }
-                float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                        for (int q2 = 0; q2 < 2; ++q2) {
+                            uint32_t w[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[tt][8 * q2 + 2 * e], a.scale_log2, nmx));
+                                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[tt][8 * q2 + 2 * e + 1], a.scale_log2, nmx));
+                                w[e] = cvt_bf16x2(p0, p1);
+                                ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one2, ps[e], false);
+                            }
+                            pf[tt][q2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+                        }
+                    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                };
+                float psum = probs(-m);
                 if (__any(!(psum <= ATAU_SUM))) {           // also catches inf and NaN (m = -inf)
                     float mloc = -INFINITY;
 #pragma unroll
@@ -284,17 +298,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
                     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
                     const float mn = fmaxf(m, mloc * a.scale_log2);
                     const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block
-                    const float nmn = -mn;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ps[e] = 0.0f;
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int q = 0; q < 16; ++q) {
-                            pr[tt][q] = __builtin_amdgcn_exp2f(fmaf(sc[tt][q], a.scale_log2, nmn));
-                            ps[q & 3] += pr[tt][q];
-                        }
-                    psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                    psum = probs(-mn);
                     lsum = lsum * alpha;
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
@@ -303,17 +307,6 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
                     m = mn;
                 }
                 lsum += psum;                               // this lane's 32 keys; halves meet at the end
-                // P^T fragments: K step (tt, q2) = accumulator values 8 q2 .. 8 q2 + 7
-                bf16x8 pf[2][2];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int q2 = 0; q2 < 2; ++q2) {
-                        uint32_t w[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(pr[tt][8 * q2 + 2 * e], pr[tt][8 * q2 + 2 * e + 1]);
-                        pf[tt][q2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
-                    }
                 // O^T += V^T P^T: the A fragment of (tt, q2) holds keys
                 // 32 tt + 16 q2 + {4 hh + 0..3, 8 + 4 hh + 0..3}, the order in
                 // which the score accumulators hold them
