@@ -761,6 +761,20 @@ def test_attention_rank_split_key_chunks(causal):
     assert torch.equal(out, T.tp_attention_rank(qkv, nq, nkv, causal=causal))
 
 
+@pytest.mark.parametrize("n,nq,nkv,causal", [(2600, 16, 2, True), (2600, 16, 2, False), (3000, 2, 2, True)])
+def test_attention_rank_split_with_head_quads_and_idle_waves(n, nq, nkv, causal):
+    """Split tiles (partials and the combine) with two KV groups of 8 heads
+    (two head quads per group: partial slots over groups and quads), and MHA
+    (one head per group: three idle waves per workgroup)."""
+    assert T.tp_attention_workspace_bytes(n, nq, nkv, causal=causal) > 0
+    qkv = rnd((n, (nq + 2 * nkv) * 128), 1.0, 970 + n + nq + causal, torch.bfloat16)
+    out = T.tp_attention_rank(qkv, nq, nkv, causal=causal)
+    torch.cuda.synchronize()
+    rows = [0, 1, 31, 32, 1023, 1024, 1300, 1301, n // 2, n - 33, n - 32, n - 1]
+    attn_check(qkv, nq, nkv, causal, out, rows=rows)
+    assert torch.equal(out, T.tp_attention_rank(qkv, nq, nkv, causal=causal))
+
+
 def test_attention_workspace_is_zero_for_short_sequences():
     """Short sequences: every workgroup takes whole query tiles (a light and
     a heavy one), so nothing is merged and no workspace is needed."""
