@@ -129,8 +129,9 @@ TP_API tp_status tp_shard_qkv(const void* wq, const void* wk, const void* wv,
  *   src: HOST pointer (pageable or pinned) to the full tensor, row-major,
  *        in src_dt; it must stay valid and unchanged until the stream has
  *        passed the call (pageable sources are copied before the call
- *        returns; a column cut (dim 1) of pageable memory is gathered on the
- *        host in 16 MiB blocks and synchronises the stream).
+ *        returns; a dim-1 cut (row-parallel: a segment of every row) of
+ *        pageable memory is gathered on the host in 16 MiB blocks and
+ *        synchronises the stream).
  *   dst: DEVICE table in dst_dt; staging: DEVICE buffer, 16-byte aligned, of
  *        at least tp_load_staging_bytes(chunk rows, chunk cols, src_dt,
  *        dst_dt) bytes (0 bytes, NULL allowed, when the dtypes match); it

@@ -10,9 +10,10 @@
 // and columns cross the host link, into a device staging buffer in the
 // checkpoint's dtype; a kernel then converts it into its place in the table
 // (fp32 -> bf16 round to nearest even, bf16 -> fp32 exact).  When the dtypes
-// match, the copy lands in the table directly.  A row cut of pageable host
-// memory is gathered on the host in 16 MiB blocks first: the runtime's
-// strided copy from pageable memory runs at a fraction of a plain copy.
+// match, the copy lands in the table directly.  A dim-1 cut (row-parallel:
+// a segment of every row) of pageable host memory is gathered on the host in
+// 16 MiB blocks first: the runtime's strided copy from pageable memory runs
+// at a fraction of a plain copy.
 #include <string.h>
 
 #include <vector>
