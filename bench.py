@@ -5,7 +5,11 @@ shape, one rank of TP=8 (n=8192 tokens, h=8192, f_local=3584, bf16):
   fused column-parallel gate_up GEMM with the SiLU(gate)*up epilogue,
   row-parallel down GEMM -> full-shape [8192, 8192] bf16 partial,
   ring-order reduce of that partial with the 7 other ranks' partials.
-Inputs are resident in HBM before timing starts.  `value` is the MLP's
+Inputs are resident in HBM before timing starts.  Before the W warmup
+steps, the step runs untimed for --settle-ms of wall time: under sustained
+MFMA load the GPU's power management takes tens of milliseconds to reach its
+steady state (back-to-back gate_up launches fall from ~1.17 ms to ~0.71 ms
+over the first ~70 ms), and the figure reported is the steady state.  `value` is the MLP's
 TFLOP/s over its two launches (algorithmic FLOP / measured time);
 `ms_per_step` covers the whole step, reduce included.
 
@@ -16,7 +20,7 @@ ranks, the vocab-parallel embedding + LM head (TP=2), the attention
 projections at TP=16 and the fp32 Qwen3 MLP.  A bounded sample of the fp64
 CPU oracle is timed on the host as a baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none|a,b]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--legs all|none|a,b]
 """
 import argparse
 import json
@@ -509,6 +513,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps before the warmup, for this much wall time (clock settling)")
     ap.add_argument("--legs", default="all")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
@@ -527,6 +533,15 @@ def main():
     log("bench: setup prefill workload")
     S = prefill_setup()
     w = S["w"]
+    log(f"bench: settle {a.settle_ms:.0f} ms")
+    n_settle = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < a.settle_ms:
+        for _ in range(8):
+            prefill_step(S)
+        n_settle += 8
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(a.warmup):
         prefill_step(S)
     torch.cuda.synchronize()
@@ -593,6 +608,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "settle": {"steps": n_settle, "ms": round(settle_ms, 1)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "n": w.n, "h": w.h, "f_local": fl, "tp": w.tp,
