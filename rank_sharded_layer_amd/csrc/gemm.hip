@@ -881,7 +881,10 @@ __device__ __forceinline__ void staged_store_f32(const GemmArgs& p, f32x4 (&acc)
 }
 
 // Deep-pipelined direct-to-LDS kernel with 16x16x32 MFMAs (16-byte-aligned
-// operands, K a multiple of 8), for the 256 x 256 tiles.
+// operands, K a multiple of 8), for the 256 x 256 tiles.  PAIR (every K
+// range a multiple of 64) replaces the four single stages below by two
+// stages of K = 64, so that each DMA request is a whole 128-byte line (see
+// the PAIR branch); the rest of this comment describes single stages.
 //   * MFMA shape: v_mfma_f32_16x16x32_bf16 moves half the accumulator data
 //     per flop of the 32x32x16 form; on this power-limited part that buys
 //     clock (measured ~15% more MFMA throughput on random operands).  Lane
@@ -902,7 +905,7 @@ __device__ __forceinline__ void staged_store_f32(const GemmArgs& p, f32x4 (&acc)
 // c ^ ((r >> 2) & 3) of its row and 16 consecutive rows hit 16 distinct
 // groups.  The DMA applies the permutation on the global side (lane l of an
 // instruction fills slot l and fetches the chunk that belongs there).
-template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
+template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL, bool PAIR>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p) {
     constexpr int BK = 32;
     constexpr int NST = 4;
@@ -930,147 +933,298 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
     const int64_t n0 = GATED ? (int64_t)u.tile_n * (BN / 2) : (int64_t)u.tile_n * BN;
     const int64_t k_begin = u.k_begin, k_end = u.k_end;
 
-    // DMA: instruction j of a stage fills slots 64 j .. 64 j + 63, i.e. tile
-    // rows 16 j + (lane >> 2), position lane & 3, which holds chunk cl
-    const int cl = (lane & 3) ^ ((lane >> 4) & 3);
-    uint32_t off[PW];
-#pragma unroll
-    for (int q = 0; q < PW; ++q) {
-        const int j = wid * PW + q;
-        const int r = j * 16 + (lane >> 2);
-        off[q] = SENT;
-        if (j < A_INSTR) {
-            if (m0 + r < p.M) off[q] = (uint32_t)(((int64_t)r * p.K + cl * 8) * 2);
-        } else {
-            const int lr = r - BM;
-            int64_t gb;
-            bool ok;
-            if (GATED) {
-                const int half = BN / 2;
-                const int64_t c = n0 + (lr < half ? lr : lr - half);
-                ok = c < p.N;
-                gb = lr < half ? c : p.N + c;
-            } else {
-                gb = n0 + lr;
-                ok = gb < p.Nb;
-            }
-            if (ok) off[q] = (uint32_t)(((gb - n0) * p.K + cl * 8) * 2);
-        }
-    }
-    const uint16_t* a_tile = p.A + m0 * p.K;
-    const uint16_t* b_tile = p.B + n0 * p.K;
-    auto issue_stage = [&](int64_t k0, int st) {
-        __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
-        __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
-        const bool tail = KTAIL && k0 + BK > k_end;
-#pragma unroll
-        for (int q = 0; q < PW; ++q) {
-            const int j = wid * PW + q;
-            uint32_t o = off[q];
-            if (KTAIL && tail && k0 + cl * 8 >= k_end) o = SENT;
-            auto* dst = (__attribute__((address_space(3))) void*)(lds + st * STAGE + j * 1024);
-            if (j < A_INSTR)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, o, 0, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, o, 0, 0, 0);
-        }
-    };
-
-    // fragment reads: lane l reads row l & 15 of a 16-row block, chunk
-    // l >> 4, at its swizzled position
-    const int lo = (lane & 15) * ROWB + (((lane >> 4) ^ (((lane & 15) >> 2) & 3)) * 16);
-    const int xbase = wm * WTM * ROWB + lo;
-    const int wbase = A_BYTES + lo;
-
-    bf16x8 wf[2][TN], xf[2][TM];
-    auto read_frags = [&](int st, auto slot_c) {
-        constexpr int SL = decltype(slot_c)::value;
-        const uint8_t* b = lds + st * STAGE;
-#pragma unroll
-        for (int i = 0; i < TN; ++i)
-            wf[SL][i] = *reinterpret_cast<const bf16x8*>(b + wbase + b_tile_row_of<BN, WN, GATED, 16>(i, wn) * ROWB);
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-            xf[SL][j] = *reinterpret_cast<const bf16x8*>(b + xbase + j * 16 * ROWB);
-    };
-
     f32x4 acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-    constexpr int MF = TN * TM;
-    constexpr int NR = TN + TM;
-    auto mfma_slot = [&](auto slot_c) {
-        constexpr int SL = decltype(slot_c)::value;
+    if constexpr (PAIR) {
+        // Paired stages: two LDS buffers of K = 64 (tile rows of 128 bytes),
+        // each multiplied as two K steps of 32 (h = 0, 1).  A DMA instruction
+        // then fetches 8 rows x 128 contiguous bytes: whole 128-byte lines,
+        // half the L1 -> L2 requests of the 64-byte rows of single stages.
+        //   * chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16
+        //     rows of one fragment read fall in 16 distinct 16-byte bank
+        //     groups (rows alternate between the two 128-byte halves of the
+        //     256 bytes the 64 banks cover);
+        //   * pair q + 1 is DMA'd into the other buffer from the middle of
+        //     step 2q - 1 (once every wave holds pair q - 1's last
+        //     fragments) and certified in the middle of step 2q + 1, two K
+        //     steps later; one barrier per pair;
+        //   * fragments of step s + 1 are read under the MFMAs of step s.
+        constexpr int ROW2 = 2 * ROWB;                       // 128 bytes
+        constexpr int STAGE2 = (BM + BN) * ROW2;
+        static_assert(2 * STAGE2 <= NST * STAGE, "two pair buffers fit the ring");
+        constexpr int N2 = STAGE2 / 1024, A2 = BM * ROW2 / 1024;
+        static_assert(N2 % NW == 0, "each wave issues the same number of DMA instructions");
+        constexpr int PW2 = N2 / NW;
+        uint32_t off2[PW2];
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
+        for (int q = 0; q < PW2; ++q) {
+            const int j = wid * PW2 + q;
+            const int r = j * 8 + (lane >> 3);                // tile row; (r >> 1) & 7 = (4 (j & 1) + (lane >> 4)) & 7
+            const int c = (lane & 7) ^ ((4 * (j & 1) + (lane >> 4)) & 7);
+            off2[q] = SENT;
+            if (j < A2) {
+                if (m0 + r < p.M) off2[q] = (uint32_t)(((int64_t)r * p.K + c * 8) * 2);
+            } else {
+                const int lr = r - BM;
+                int64_t gb;
+                bool ok;
+                if (GATED) {
+                    const int half = BN / 2;
+                    const int64_t cc = n0 + (lr < half ? lr : lr - half);
+                    ok = cc < p.N;
+                    gb = lr < half ? cc : p.N + cc;
+                } else {
+                    gb = n0 + lr;
+                    ok = gb < p.Nb;
+                }
+                if (ok) off2[q] = (uint32_t)(((gb - n0) * p.K + c * 8) * 2);
+            }
+        }
+        const uint16_t* a_tile = p.A + m0 * p.K;
+        const uint16_t* b_tile = p.B + n0 * p.K;
+        auto issue_pair = [&](int64_t k0, int buf) {
+            __amdgpu_buffer_rsrc_t rsa =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+            __amdgpu_buffer_rsrc_t rsb =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+            for (int q = 0; q < PW2; ++q) {
+                const int j = wid * PW2 + q;
+                const uint32_t o = off2[q];
+                auto* dst = (__attribute__((address_space(3))) void*)(lds + buf * STAGE2 + j * 1024);
+                if (j < A2)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, o, 0, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, o, 0, 0, 0);
+            }
+        };
+        // fragment reads: lane l reads row l & 15 of a 16-row block, chunk
+        // 4 h + (l >> 4), at its swizzled position
+        const int lrow = lane & 15;
+        const int lo0 = lrow * ROW2 + ((((lane >> 4)) ^ (lrow >> 1)) * 16);
+        const int lo1 = lrow * ROW2 + (((4 + (lane >> 4)) ^ (lrow >> 1)) * 16);
+        bf16x8 wf[2][TN], xf[2][TM];
+        auto read_one = [&](int buf, int lo, auto slot_c, int r) {
+            constexpr int SL = decltype(slot_c)::value;
+            const uint8_t* b = lds + buf * STAGE2 + lo;
+            if (r < TN)
+                wf[SL][r] = *reinterpret_cast<const bf16x8*>(b + (BM + b_tile_row_of<BN, WN, GATED, 16>(r, wn)) * ROW2);
+            else
+                xf[SL][r - TN] = *reinterpret_cast<const bf16x8*>(b + (wm * WTM + (r - TN) * 16) * ROW2);
+        };
+        auto mfma_block = [&](auto slot_c, int i) {
+            constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
             for (int j = 0; j < TM; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[SL][i], xf[SL][j], acc[i][j], 0, 0, 0);
-    };
-
-    const int nk = (int)ceil_div(k_end - k_begin, BK);
-    auto kof = [&](int s) { return k_begin + (int64_t)s * BK; };
-    auto vm_wait = [&](bool one_stage_in_flight) {
-        // this wave's DMA of older stages has landed; the newest (PW
-        // instructions) may still be in flight
-        if (one_stage_in_flight)
-            __builtin_amdgcn_s_waitcnt(0x0f70 | (PW & 15) | ((PW >> 4) << 14));
-        else
-            __builtin_amdgcn_s_waitcnt(0x0f70);
-    };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-
-    if (nk > 0) {
-        for (int s = 0; s < 3; ++s)
-            if (s < nk) issue_stage(kof(s), s);
-        vm_wait(nk > 2);
-        bare_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(0, S0{});
-        // K step s multiplies slot s mod 2 and reads step s + 1 into the
-        // other slot.  It first refills the stage of step s - 1 with step
-        // s + 3, and ends by certifying step s + 2.  FULL: all of this is
-        // known to apply (steady state, no branches between the MFMAs and
-        // the reads they hide); otherwise each part is checked.
-        auto step = [&](int s, auto sa, auto sb, auto full_c) {
-            constexpr bool FULL = decltype(full_c)::value;
-            const bool dma = FULL || s + 3 < nk;
-            const bool more = FULL || s + 1 < nk;
-            const bool bar = FULL || s + 2 < nk;
-            if (dma) issue_stage(kof(s + 3), (s + 3) & 3);
-            __builtin_amdgcn_sched_barrier(0);
-            if (more) read_frags((s + 1) & 3, sb);
-            mfma_slot(sa);
-#pragma unroll
-            for (int q = 0; q < MF; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (FULL && (q % (MF / 4)) < NR / 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (bar) {
-                vm_wait(dma);
-                bare_barrier();
-            }
-            __builtin_amdgcn_sched_barrier(0);
         };
-        using T_ = std::true_type;
-        using F_ = std::false_type;
-        int s = 0;
-        for (; s + 4 < nk; s += 2) {
-            step(s, S0{}, S1{}, T_{});
-            step(s + 1, S1{}, S0{}, T_{});
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        constexpr int NR = TN + TM;
+        constexpr int MF = TN * TM;
+        const int np = (int)((k_end - k_begin) / 64);
+        if (np > 0) {
+            issue_pair(k_begin, 0);
+            if (np > 1) issue_pair(k_begin + 64, 1);
+            if (np > 1)
+                __builtin_amdgcn_s_waitcnt(0x0f70 | (PW2 & 15) | ((PW2 >> 4) << 14));
+            else
+                __builtin_amdgcn_s_waitcnt(0x0f70);
+            bare_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read_one(0, lo0, S0{}, r);
+            // pair q, buffer q & 1.  Step 2q (h = 0): read step 2q + 1's
+            // fragments (same buffer, h = 1) under its MFMAs.  Step 2q + 1
+            // (h = 1): half its MFMAs; certify pair q + 1 (DMA landed, every
+            // wave's reads done); refill buffer q & 1 with pair q + 2; read
+            // step 2q + 2's fragments (pair q + 1, h = 0) under the other half.
+            auto pair_steps = [&](int q, auto full_c) {
+                constexpr bool FULL = decltype(full_c)::value;
+                const int buf = q & 1;
+                const bool next = FULL || q + 1 < np;
+                const bool dma = FULL || q + 2 < np;
+#pragma unroll
+                for (int r = 0; r < NR; ++r) read_one(buf, lo1, S1{}, r);
+#pragma unroll
+                for (int i = 0; i < TN; ++i) mfma_block(S0{}, i);
+#pragma unroll
+                for (int qq = 0; qq < MF; ++qq) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if ((qq % (MF / 4)) < NR / 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TN / 2; ++i) mfma_block(S1{}, i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (next) {
+                    __builtin_amdgcn_s_waitcnt(0x0070);          // vmcnt(0) lgkmcnt(0)
+                    bare_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (dma) issue_pair(k_begin + (int64_t)(q + 2) * 64, buf);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) read_one(buf ^ 1, lo0, S0{}, r);
+                }
+#pragma unroll
+                for (int i = TN / 2; i < TN; ++i) mfma_block(S1{}, i);
+                if (FULL) {
+#pragma unroll
+                    for (int qq = 0; qq < MF / 2; ++qq) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (qq < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            int q = 0;
+            for (; q + 2 < np; ++q) pair_steps(q, std::true_type{});
+            for (; q < np; ++q) pair_steps(q, std::false_type{});
         }
-        // at most 4 steps remain (s is even here): unrolled, so that the
-        // register slots stay compile-time
-        if (s < nk) step(s, S0{}, S1{}, F_{});
-        if (s + 1 < nk) step(s + 1, S1{}, S0{}, F_{});
-        if (s + 2 < nk) step(s + 2, S0{}, S1{}, F_{});
-        if (s + 3 < nk) step(s + 3, S1{}, S0{}, F_{});
-    }
+    } else {
+        // DMA: instruction j of a stage fills slots 64 j .. 64 j + 63, i.e. tile
+        // rows 16 j + (lane >> 2), position lane & 3, which holds chunk cl
+        const int cl = (lane & 3) ^ ((lane >> 4) & 3);
+        uint32_t off[PW];
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            const int j = wid * PW + q;
+            const int r = j * 16 + (lane >> 2);
+            off[q] = SENT;
+            if (j < A_INSTR) {
+                if (m0 + r < p.M) off[q] = (uint32_t)(((int64_t)r * p.K + cl * 8) * 2);
+            } else {
+                const int lr = r - BM;
+                int64_t gb;
+                bool ok;
+                if (GATED) {
+                    const int half = BN / 2;
+                    const int64_t c = n0 + (lr < half ? lr : lr - half);
+                    ok = c < p.N;
+                    gb = lr < half ? c : p.N + c;
+                } else {
+                    gb = n0 + lr;
+                    ok = gb < p.Nb;
+                }
+                if (ok) off[q] = (uint32_t)(((gb - n0) * p.K + cl * 8) * 2);
+            }
+        }
+        const uint16_t* a_tile = p.A + m0 * p.K;
+        const uint16_t* b_tile = p.B + n0 * p.K;
+        auto issue_stage = [&](int64_t k0, int st) {
+            __amdgpu_buffer_rsrc_t rsa =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+            __amdgpu_buffer_rsrc_t rsb =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+            const bool tail = KTAIL && k0 + BK > k_end;
+#pragma unroll
+            for (int q = 0; q < PW; ++q) {
+                const int j = wid * PW + q;
+                uint32_t o = off[q];
+                if (KTAIL && tail && k0 + cl * 8 >= k_end) o = SENT;
+                auto* dst = (__attribute__((address_space(3))) void*)(lds + st * STAGE + j * 1024);
+                if (j < A_INSTR)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, o, 0, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, o, 0, 0, 0);
+            }
+        };
+
+        // fragment reads: lane l reads row l & 15 of a 16-row block, chunk
+        // l >> 4, at its swizzled position
+        const int lo = (lane & 15) * ROWB + (((lane >> 4) ^ (((lane & 15) >> 2) & 3)) * 16);
+        const int xbase = wm * WTM * ROWB + lo;
+        const int wbase = A_BYTES + lo;
+
+        bf16x8 wf[2][TN], xf[2][TM];
+        auto read_frags = [&](int st, auto slot_c) {
+            constexpr int SL = decltype(slot_c)::value;
+            const uint8_t* b = lds + st * STAGE;
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+                wf[SL][i] = *reinterpret_cast<const bf16x8*>(b + wbase + b_tile_row_of<BN, WN, GATED, 16>(i, wn) * ROWB);
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+                xf[SL][j] = *reinterpret_cast<const bf16x8*>(b + xbase + j * 16 * ROWB);
+        };
+
+        constexpr int MF = TN * TM;
+        constexpr int NR = TN + TM;
+        auto mfma_slot = [&](auto slot_c) {
+            constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[SL][i], xf[SL][j], acc[i][j], 0, 0, 0);
+        };
+
+        const int nk = (int)ceil_div(k_end - k_begin, BK);
+        auto kof = [&](int s) { return k_begin + (int64_t)s * BK; };
+        auto vm_wait = [&](bool one_stage_in_flight) {
+            // this wave's DMA of older stages has landed; the newest (PW
+            // instructions) may still be in flight
+            if (one_stage_in_flight)
+                __builtin_amdgcn_s_waitcnt(0x0f70 | (PW & 15) | ((PW >> 4) << 14));
+            else
+                __builtin_amdgcn_s_waitcnt(0x0f70);
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+
+        if (nk > 0) {
+            for (int s = 0; s < 3; ++s)
+                if (s < nk) issue_stage(kof(s), s);
+            vm_wait(nk > 2);
+            bare_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(0, S0{});
+            // K step s multiplies slot s mod 2 and reads step s + 1 into the
+            // other slot.  It first refills the stage of step s - 1 with step
+            // s + 3, and ends by certifying step s + 2.  FULL: all of this is
+            // known to apply (steady state, no branches between the MFMAs and
+            // the reads they hide); otherwise each part is checked.
+            auto step = [&](int s, auto sa, auto sb, auto full_c) {
+                constexpr bool FULL = decltype(full_c)::value;
+                const bool dma = FULL || s + 3 < nk;
+                const bool more = FULL || s + 1 < nk;
+                const bool bar = FULL || s + 2 < nk;
+                if (dma) issue_stage(kof(s + 3), (s + 3) & 3);
+                __builtin_amdgcn_sched_barrier(0);
+                if (more) read_frags((s + 1) & 3, sb);
+                mfma_slot(sa);
+#pragma unroll
+                for (int q = 0; q < MF; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (FULL && (q % (MF / 4)) < NR / 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (bar) {
+                    vm_wait(dma);
+                    bare_barrier();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            using T_ = std::true_type;
+            using F_ = std::false_type;
+            int s = 0;
+            for (; s + 4 < nk; s += 2) {
+                step(s, S0{}, S1{}, T_{});
+                step(s + 1, S1{}, S0{}, T_{});
+            }
+            // at most 4 steps remain (s is even here): unrolled, so that the
+            // register slots stay compile-time
+            if (s < nk) step(s, S0{}, S1{}, F_{});
+            if (s + 1 < nk) step(s + 1, S1{}, S0{}, F_{});
+            if (s + 2 < nk) step(s + 2, S0{}, S1{}, F_{});
+            if (s + 3 < nk) step(s + 3, S1{}, S0{}, F_{});
+        }
+
+    }  // single stages
 
     // results: block (i, j), lane l: rows (output columns) b_row(i) + 4 (l >> 4)
     // + q, column (token) wm WTM + 16 j + (l & 15)
@@ -2081,6 +2235,16 @@ static bool pipe_enabled() {
     return on == 1;
 }
 
+// paired K = 64 stages in the deep-pipelined kernel (TPSHARD_GEMM_PAIR=0 turns them off)
+static bool pair_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TPSHARD_GEMM_PAIR");
+        on = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    return on == 1;
+}
+
 // weight-streaming decode kernel switch (TPSHARD_GEMM_STREAM=0 turns it off)
 static bool stream_enabled() {
     static int on = -1;
@@ -2280,10 +2444,20 @@ static void launch_pipe_one(const GemmArgs& a, int splits, hipStream_t s) {
     const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
     dim3 grid((unsigned)units, (unsigned)splits);
     const bool kt32 = (a.K % 32) != 0 || (a.k_split % 32) != 0;
+    // paired K = 64 stages: every K range a multiple of 64
+    const bool pair = BM == 256 && pair_enabled() && a.K % 64 == 0 && a.k_split % 64 == 0 &&
+                      (a.tail_split <= 1 || a.tail_k % 64 == 0);
+    if constexpr (BM == 256) {
+        if (pair) {
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false, true>), grid, dim3(WM * WN * 64), 0, s, a);
+            launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
+            return;
+        }
+    }
     if (kt32)
-        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, a);
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, true, false>), grid, dim3(WM * WN * 64), 0, s, a);
     else
-        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, a);
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false, false>), grid, dim3(WM * WN * 64), 0, s, a);
     launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
 }
 
