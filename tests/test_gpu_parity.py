@@ -411,6 +411,47 @@ def test_tail_split_gate_up_matches_oracle(n, h, fl):
     assert torch.equal(act, again)          # fixed piece order: deterministic
 
 
+@pytest.mark.parametrize("n,k,m", [(4100, 1024, 7800), (8192, 3584, 8192)])
+def test_paired_stage_tiles_linear_matches_oracle(n, k, m):
+    """256 x 256 tiles with K a multiple of 64 (paired K = 64 LDS stages):
+    17 x 31 = 527 tiles with a ragged last tile row and column, and the 70B
+    down shape (1024 tiles).  Plain and biased bf16 stores and the staged
+    fp32 store, every 256-column tile of the sampled rows checked."""
+    x = rnd((n, k), 1.0, 190 + n, torch.bfloat16)
+    w = rnd((m, k), 0.02, 191 + m, torch.bfloat16)
+    b = rnd((m,), 0.02, 192, torch.bfloat16)
+    rows = sorted(set(synth.sample_rows(n, 10, 193) + list(range(n - 4, n)) + [255, 256, 4095 % n]))
+    for bias in (None, b):
+        for out_dt in (torch.bfloat16, torch.float32):
+            y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+            ref = oracle.linear(to_f64(x[rows]), to_f64(w), to_f64(bias) if bias is not None else None)
+            got = to_f64(y[rows])
+            assert relf(got, ref) <= 1e-2, (bias is None, out_dt)
+            assert relf(got[:, -300:], ref[:, -300:]) <= 1e-2
+            # every 256-column tile of the sampled rows, on its own
+            for c0 in range(0, m, 256):
+                assert relf(got[:, c0:c0 + 256], ref[:, c0:c0 + 256]) <= 1e-2, (c0, bias is None, out_dt)
+    y1 = T.tp_linear_rank_forward(x, w)
+    assert torch.equal(y1, T.tp_linear_rank_forward(x, w))
+
+
+def test_paired_stage_tiles_gate_up_matches_oracle():
+    """Gated paired-stage tiles: 17 x 31 = 527 tiles of 256 x 128 act
+    columns, ragged last tile row and column."""
+    n, h, fl = 4100, 1024, 3900
+    x = rnd((n, h), 1.0, 195, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.02, 196, torch.bfloat16)
+    act = T.tp_gate_up_act_rank(x, wgu)
+    rows = sorted(set(synth.sample_rows(n, 10, 197) + list(range(n - 4, n)) + [255, 256]))
+    xg, W = to_f64(x[rows]), to_f64(wgu)
+    ref = oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:]))
+    got = to_f64(act[rows])
+    assert relf(got, ref) <= 1e-2
+    for c0 in range(0, fl, 128):
+        assert relf(got[:, c0:c0 + 128], ref[:, c0:c0 + 128]) <= 1e-2, c0
+    assert torch.equal(act, T.tp_gate_up_act_rank(x, wgu))
+
+
 def test_tail_split_not_used_for_short_k_or_one_round():
     # 594 tiles of 256 but K = 1024: pieces would be too short
     assert T.tp_linear_workspace_bytes(512, 1024, 75968, torch.bfloat16) == 0
