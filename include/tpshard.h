@@ -306,8 +306,8 @@ TP_API tp_status tp_rs_add_rmsnorm(const void* const* partials /*HOST array*/, i
  *   head_dim must be 128; nkv divides nq; dt must be TP_BF16; qkv under
  *   2 GiB.
  * workspace: at least tp_attention_workspace_bytes(...) bytes, 16-byte
- *   aligned.  The work is cut into about 512 equal pieces (pairs of a
- *   light and a heavy 32-query tile, each pair's key blocks in equal
+ *   aligned.  The work is cut into about 256 equal pieces (pairs of a
+ *   light and a heavy 64-query tile, each pair's key blocks in equal
  *   chunks); a tile spread over several pieces leaves fp32 partial results
  *   there, merged by a second launch.  Zero bytes (NULL allowed) for short
  *   sequences, where every piece holds whole tiles. */

@@ -10,10 +10,14 @@
 // accumulation, probabilities rounded to bf16 for the P.V product.
 //
 // Design (flash-attention order, one pass over the keys):
-//   * workgroup = 4 waves = up to 4 query heads of one KV group on the same
-//     32 queries; each 64-key block of K and V goes from global memory
-//     straight into LDS (buffer_load ... lds, double-buffered, one barrier
-//     per block) and is read by all four;
+//   * workgroup = 8 waves = two 32-query halves of a 64-query tile x up to
+//     4 query heads of one KV group, one workgroup per CU; each 64-key
+//     block of K and V goes from global memory straight into LDS
+//     (buffer_load ... lds, double-buffered, one barrier per block) and is
+//     read by all eight.  With 64 = the key block size, both halves of a
+//     tile have the same key blocks (causal or ragged), so sharing a block
+//     between two query halves halves the K/V traffic per query against
+//     32-query workgroups of 4 waves at two per CU;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
 //     keys as rows, queries as columns), so a lane owns one query and 32 of
 //     the block's 64 scores: the running max and sum need one exchange with
@@ -66,10 +70,12 @@ __device__ __forceinline__ void wg_barrier() {
 }
 
 constexpr int AD = 128;          // head_dim
-constexpr int AQ = 32;           // queries per tile
+constexpr int AQ = 32;           // queries per wave
+constexpr int AQW = 64;          // queries per tile: two 32-query halves of a workgroup
 constexpr int AK = 64;           // keys per block
+constexpr int AW = 8;            // waves: (query half, head of a quad)
 constexpr int APART = AQ * AD + 2 * AQ;   // floats of one wave's partial: O, m, l
-constexpr int AUNITS = 512;      // target workgroups: two per CU
+constexpr int AUNITS = 256;      // target workgroups: one per CU
 constexpr int AMINCH = 8;        // fewest key blocks per chunk
 constexpr float ATAU_SUM = 8192.0f;   // largest accepted sum of a lane's 32 probabilities
 
@@ -79,17 +85,17 @@ struct AttnArgs {
     int64_t n;
     int64_t ld;                  // qkv row length (elements)
     int nq, nkv, rep, causal;
-    int ntiles;                  // query tiles of AQ
+    int ntiles;                  // query tiles of AQW
     int npairs;                  // (ntiles + 1) / 2
     int kch;                     // chunks per pair
     float scale_log2;            // log2(e) / sqrt(d)
-    float* part;                 // [npairs][kch][2][nkv][quads][4 waves][APART] fp32
+    float* part;                 // [npairs][kch][2][nkv][quads][AW waves][APART] fp32
 };
 
 // key blocks of query tile `tile`
 __host__ __device__ __forceinline__ int tile_blocks(int tile, int64_t n, int causal) {
     if (!causal) return (int)((n + AK - 1) / AK);
-    int64_t last = (int64_t)tile * AQ + AQ - 1;
+    int64_t last = (int64_t)tile * AQW + AQW - 1;
     if (last > n - 1) last = n - 1;
     return (int)(last / AK) + 1;
 }
@@ -116,7 +122,7 @@ __host__ __device__ __forceinline__ int chunk_lo(int c, int total, int k) {
     return (int)(((int64_t)c * total) / k);
 }
 
-__global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(AW * 64, 1) void attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t ks0[AK * AD];
     __shared__ __attribute__((aligned(1024))) uint16_t ks1[AK * AD];
     __shared__ __attribute__((aligned(1024))) uint16_t vs0[AK * AD];
@@ -125,7 +131,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int p = (int)blockIdx.x / a.kch, c = (int)blockIdx.x - p * a.kch;
     const int g = blockIdx.y;
-    const int hsub = blockIdx.z * 4 + wid;            // head within the group
+    const int half = wid >> 2;                        // query half of the tile
+    const int hsub = blockIdx.z * 4 + (wid & 3);      // head within the group
     const bool active = hsub < a.rep;
     const int head = g * a.rep + (active ? hsub : 0);
     const int r = lane & 31, hh = lane >> 5;
@@ -149,23 +156,27 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     //   V: the 64-byte piece d = 32 t .. 32 t + 31 of key k at byte
     //      4096 t + 64 k (4 consecutive keys of one piece = 256 contiguous
     //      bytes, what a half-wave transposing read takes).
-    // This wave's instruction q fills slots 64 (4 wid + q) .. + 63:
-    //   K: s = 2 wid + (q >> 1), key 32 (q & 1) + (lane >> 1), half
+    // A block is 16 instructions of K and 16 of V; this wave's instruction
+    // q fills slots 64 J .. + 63, J = 2 wid + q:
+    //   K: s = J >> 1, key 32 (J & 1) + (lane >> 1), half
     //      (lane & 1) ^ ((lane >> 4) & 1);
-    //   V: t = wid, key 16 q + (lane >> 2), chunk (lane & 3) of the piece.
-    uint32_t koff[4], voff[4];
+    //   V: t = J >> 2, key 16 (J & 3) + (lane >> 2), chunk (lane & 3) of
+    //      the piece.
+    constexpr int PQ = 16 / AW;                       // instructions per wave and operand
+    uint32_t koff[PQ], voff[PQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int kk = 32 * (q & 1) + (lane >> 1);
-        const int kc = 2 * (2 * wid + (q >> 1)) + ((lane & 1) ^ ((lane >> 4) & 1));
+    for (int q = 0; q < PQ; ++q) {
+        const int J = PQ * wid + q;
+        const int kk = 32 * (J & 1) + (lane >> 1);
+        const int kc = 2 * (J >> 1) + ((lane & 1) ^ ((lane >> 4) & 1));
         koff[q] = (uint32_t)kk * row_b + (uint32_t)(kcol + 8 * kc) * 2;
-        const int vk = 16 * q + (lane >> 2);
-        voff[q] = (uint32_t)vk * row_b + (uint32_t)(vcol + 32 * wid + 8 * (lane & 3)) * 2;
+        const int vk = 16 * (J & 3) + (lane >> 2);
+        voff[q] = (uint32_t)vk * row_b + (uint32_t)(vcol + 32 * (J >> 2) + 8 * (lane & 3)) * 2;
     }
-    auto issue = [&](uint32_t base, uint16_t* buf, const uint32_t (&off)[4]) {
+    auto issue = [&](uint32_t base, uint16_t* buf, const uint32_t (&off)[PQ]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            auto* dst = (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(buf) + (4 * wid + q) * 1024);
+        for (int q = 0; q < PQ; ++q) {
+            auto* dst = (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(buf) + (PQ * wid + q) * 1024);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, base + off[q], 0, 0, 0);
         }
     };
@@ -206,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         if (sg == 1) wg_barrier();                    // the first segment's buffers are free
         const int nbt = tile_blocks(tile, a.n, a.causal);
         const bool whole = b0 == 0 && b1 == nbt;
-        const int64_t q0 = (int64_t)tile * AQ;
+        const int64_t q0 = (int64_t)tile * AQW + AQ * half;
         const int64_t qi = q0 + r;                    // this lane's query
         const int qi32 = (int)qi, n32 = (int)a.n;
         // the tile's last block holds its diagonal (causal) or the end of
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         if (!whole) {
             // this segment's unnormalised O, running max and sum for the combine
             const int64_t slot = ((int64_t)p * a.kch + c) * 2 + sg;
-            float* pw = a.part + (((slot * gridDim.y + g) * gridDim.z + blockIdx.z) * 4 + wid) * APART;
+            float* pw = a.part + (((slot * gridDim.y + g) * gridDim.z + blockIdx.z) * AW + wid) * APART;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -387,8 +398,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
 // Merges the pieces of a split tile: for query i of head h,
 // m* = max_c m_c, out = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c,
-// pieces in key order, four at a time with the maximum carried over.  Block (tile, KV group, quad x 4 + wave): 256 threads,
-// thread = (query tid / 8, 16 consecutive d).
+// pieces in key order, four at a time with the maximum carried over.
+// Block (tile, KV group, quad x AW + wave of the producing workgroup): 256
+// threads, thread = (query of the wave's 32: tid / 8, 16 consecutive d).
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, int nz) {
     const int tile = blockIdx.x;
     const int p = tile < a.ntiles - 1 - tile ? tile : a.ntiles - 1 - tile;
@@ -405,16 +417,16 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, int 
     for (int cc = 0; cc < a.kch; ++cc) npc += meets(cc) ? 1 : 0;
     if (npc <= 1) return;                                // one piece: written directly
     const int g = blockIdx.y;
-    const int z = blockIdx.z >> 2, wv = blockIdx.z & 3;
-    const int hsub = z * 4 + wv;
+    const int z = blockIdx.z / AW, wv = blockIdx.z % AW;
+    const int hsub = z * 4 + (wv & 3);
     if (hsub >= a.rep) return;
     const int head = g * a.rep + hsub;
     const int qq = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
-    const int64_t qi = (int64_t)tile * AQ + qq;
+    const int64_t qi = (int64_t)tile * AQW + AQ * (wv >> 2) + qq;
     if (qi >= a.n) return;
     auto piece = [&](int cc) -> const float* {
         const int64_t slot = ((int64_t)p * a.kch + cc) * 2 + sg;
-        return a.part + (((slot * gridDim.y + g) * nz + z) * 4 + wv) * APART;
+        return a.part + (((slot * gridDim.y + g) * nz + z) * AW + wv) * APART;
     };
     // pieces in groups of 4, all of a group's loads in flight together;
     // the running max and sum carry across groups (online, in key order)
@@ -486,7 +498,7 @@ AttnArgs attn_args(int64_t n, int nq, int nkv, int causal) {
     a.nkv = nkv;
     a.rep = nq / nkv;
     a.causal = causal ? 1 : 0;
-    a.ntiles = (int)((n + AQ - 1) / AQ);
+    a.ntiles = (int)((n + AQW - 1) / AQW);
     a.npairs = (a.ntiles + 1) / 2;
     // chunks per pair: about AUNITS workgroups in all, chunks of at least
     // AMINCH blocks
@@ -507,7 +519,7 @@ size_t attention_ws_bytes(int64_t n, int nq, int nkv, int causal) {
     const AttnArgs a = attn_args(n, nq, nkv, causal);
     if (a.kch <= 1) return 0;                        // every pair in one workgroup: no split tiles
     const int nz = (a.rep + 3) / 4;
-    return (size_t)a.npairs * a.kch * 2 * nkv * nz * 4 * APART * sizeof(float);
+    return (size_t)a.npairs * a.kch * 2 * nkv * nz * AW * APART * sizeof(float);
 }
 
 hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int head_dim, int causal, void* out,
@@ -520,11 +532,11 @@ hipError_t launch_attention(const void* qkv, int64_t n, int nq, int nkv, int hea
     a.part = static_cast<float*>(ws);
     if (a.kch > 1 && !ws) return hipErrorInvalidValue;
     const int nz = (a.rep + 3) / 4;
-    hipLaunchKernelGGL(attention_kernel, dim3((unsigned)(a.npairs * a.kch), (unsigned)nkv, (unsigned)nz), dim3(256),
-                       0, s, a);
+    hipLaunchKernelGGL(attention_kernel, dim3((unsigned)(a.npairs * a.kch), (unsigned)nkv, (unsigned)nz),
+                       dim3(AW * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.kch <= 1) return e;
-    hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)a.ntiles, (unsigned)nkv, (unsigned)(nz * 4)),
+    hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)a.ntiles, (unsigned)nkv, (unsigned)(nz * AW)),
                        dim3(256), 0, s, a, nz);
     return hipGetLastError();
 }

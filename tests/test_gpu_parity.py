@@ -806,12 +806,13 @@ def test_attention_rank_split_key_chunks(causal):
 def test_attention_rank_split_with_head_quads_and_idle_waves(n, nq, nkv, causal):
     """Split tiles (partials and the combine) with two KV groups of 8 heads
     (two head quads per group: partial slots over groups and quads), and MHA
-    (one head per group: three idle waves per workgroup)."""
+    (one head per group: three idle waves per query half).  Rows on both
+    sides of the 32-query halves and the 64-query tiles."""
     assert T.tp_attention_workspace_bytes(n, nq, nkv, causal=causal) > 0
     qkv = rnd((n, (nq + 2 * nkv) * 128), 1.0, 970 + n + nq + causal, torch.bfloat16)
     out = T.tp_attention_rank(qkv, nq, nkv, causal=causal)
     torch.cuda.synchronize()
-    rows = [0, 1, 31, 32, 1023, 1024, 1300, 1301, n // 2, n - 33, n - 32, n - 1]
+    rows = [0, 1, 31, 32, 63, 64, 95, 96, 1023, 1024, 1300, 1301, n // 2, n - 33, n - 32, n - 1]
     attn_check(qkv, nq, nkv, causal, out, rows=rows)
     assert torch.equal(out, T.tp_attention_rank(qkv, nq, nkv, causal=causal))
 
