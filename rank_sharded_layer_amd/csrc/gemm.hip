@@ -957,19 +957,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
         constexpr int STAGE2 = (BM + BN) * ROW2;
         static_assert(2 * STAGE2 <= NST * STAGE, "two pair buffers fit the ring");
         constexpr int N2 = STAGE2 / 1024, A2 = BM * ROW2 / 1024;
-        // The DMA is issued by waves 0 .. 3 only, one per SIMD (waves w and
-        // w + 4 share a SIMD): while one wave of a SIMD waits to issue its
-        // loads, the other keeps issuing MFMAs (gate_up 698 -> 686 us
-        // against all eight waves issuing a share).  Not for the staged
-        // fp32 epilogue, whose wave then runs out of registers.
-        constexpr int DW = NW >= 8 && EPI != EPI_STORE_F32 ? NW / 2 : NW;
-        static_assert(N2 % DW == 0, "each issuing wave issues the same number of DMA instructions");
-        constexpr int PW2 = N2 / DW;
-        const bool dma_wave = wid < DW;
+        static_assert(N2 % NW == 0, "each wave issues the same number of DMA instructions");
+        constexpr int PW2 = N2 / NW;
         uint32_t off2[PW2];
 #pragma unroll
         for (int q = 0; q < PW2; ++q) {
-            const int j = (wid % DW) * PW2 + q;
+            const int j = wid * PW2 + q;
             const int r = j * 8 + (lane >> 3);                // tile row; (r >> 1) & 7 = (4 (j & 1) + (lane >> 4)) & 7
             const int c = (lane & 7) ^ ((4 * (j & 1) + (lane >> 4)) & 7);
             off2[q] = SENT;
@@ -998,7 +991,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
                 __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
             __amdgpu_buffer_rsrc_t rsb =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
-            if (DW < NW && !dma_wave) return;
 #pragma unroll
             for (int q = 0; q < PW2; ++q) {
                 const int j = wid * PW2 + q;
