@@ -75,6 +75,9 @@ def _load():
         "orc_reduce_rank_f32": (None, [ctypes.POINTER(_f32p), _int, _i64, _f32p]),
         "orc_attention_rank": (_int, [_f64p, _i64, _int, _int, _int, _int, _i64p, _i64, _f64p]),
         "orc_logits_gather_argmax": (_int, [ctypes.POINTER(_f64p), _int, _i64, _i64, _f64p, _i64p]),
+        "orc_load_shard": (_int, [_vp, _int, _i64, _i64, _int, _int, _int, _vp, _int]),
+        "orc_load_gate_up": (_int, [_vp, _int, _vp, _int, _int, _i64, _i64, _int, _int]),
+        "orc_load_qkv": (_int, [_vp, _int, _vp, _int, _int, _i64, _i64, _i64, _i64, _int, _int]),
         "orc_rs_add_rmsnorm": (_int, [ctypes.POINTER(_f32p), _int, _int, _i64, _i64, _f32p, _f64p,
                                       ctypes.c_double, _int, _f32p, _f64p]),
     }
@@ -232,66 +235,65 @@ def shard_qkv(wq, wk, wv, n_q, n_kv, head_dim, tp_rank, tp_size) -> np.ndarray:
 # --- checkpoint-style loaders ----------------------------------------------
 # [NANO22] §3-§5 weight_loader applied to a full checkpoint tensor, in the
 # order of [MINISGL] §8 (weight loading and sharding): select the rank's
-# shard, convert the dtype, copy it into the local parameter.  Tensors are
-# float32 arrays or bfloat16 as uint16 bit arrays.
+# shard, convert the dtype, copy it into the local parameter (tp_oracle.c:
+# orc_load_shard, orc_load_gate_up, orc_load_qkv).  Tensors are float32
+# arrays or bfloat16 as uint16 bit arrays.
 
-def convert(a, to_bf16):
-    """The dtype conversion of copying into the parameter: fp32 -> bf16
-    rounds to nearest even (f32_to_bf16_bits), bf16 -> fp32 is exact, equal
-    dtypes copy."""
-    a = np.ascontiguousarray(a)
+def _ldt(a):
     if a.dtype == np.float32:
-        return f32_to_bf16_bits(a) if to_bf16 else a.copy()
+        return 0
     if a.dtype == np.uint16:
-        return a.copy() if to_bf16 else (a.astype(np.uint32) << 16).view(np.float32)
-    raise OracleError("convert: float32 or bf16 bits (uint16) expected")
+        return 1
+    raise OracleError("loader: float32 or bf16 bits (uint16) expected")
 
 
 def load_shard(src, dim, tp_rank, tp_size, to_bf16) -> np.ndarray:
     """Column (dim 0, [NANO22] §3) or row (dim 1, §4) parallel loader: the
     rank's narrow(dim, r S/t, S/t) of the full tensor, then converted."""
-    if src.shape[dim] % tp_size:
+    src = np.ascontiguousarray(src)
+    rows, cols = src.shape
+    s = rows if dim == 0 else cols
+    if s % tp_size:
         raise OracleError("load_shard: size not divisible by tp_size")
-    sh = src.shape[dim] // tp_size
-    part = src[tp_rank * sh:(tp_rank + 1) * sh, :] if dim == 0 else src[:, tp_rank * sh:(tp_rank + 1) * sh]
-    return convert(part, to_bf16)
+    shape = (rows // tp_size, cols) if dim == 0 else (rows, cols // tp_size)
+    out = np.empty(shape, dtype=np.uint16 if to_bf16 else np.float32)
+    _check(_load().orc_load_shard(src.ctypes.data, _ldt(src), rows, cols, dim, tp_rank, tp_size,
+                                  out.ctypes.data, _ldt(out)), "load_shard")
+    return out
 
 
 def load_gate_up(table, src, shard_id, tp_rank, tp_size) -> None:
     """[NANO22] §5 merged column-parallel loader, in place on the rank's
-    table: output_sizes = [f, f] (gate, up); the projection's segment starts
-    at sum(output_sizes[:shard_id]) / t and is output_sizes[shard_id] / t
-    rows long (first cut); it receives src.chunk(t, 0)[tp_rank] (second
-    cut), converted to the table's dtype."""
-    f = src.shape[0]
+    [2 f/t, h] table: the projection's segment (first cut) receives
+    src.chunk(t, 0)[tp_rank] (second cut), converted to the table's dtype."""
+    src = np.ascontiguousarray(src)
+    f, h = src.shape
     if f % tp_size:
         raise OracleError("load_gate_up: f not divisible by tp_size")
-    output_sizes = [f, f]
-    off = sum(output_sizes[:shard_id]) // tp_size
-    size = output_sizes[shard_id] // tp_size
-    chunk = np.split(src, tp_size, axis=0)[tp_rank]
-    table[off:off + size] = convert(chunk, table.dtype == np.uint16)
+    if not table.flags["C_CONTIGUOUS"] or table.shape != (2 * (f // tp_size), h):
+        raise OracleError("load_gate_up: table must be a contiguous [2 f/t, h] array")
+    _check(_load().orc_load_gate_up(table.ctypes.data, _ldt(table), src.ctypes.data, _ldt(src), shard_id, f, h,
+                                    tp_rank, tp_size), "load_gate_up")
 
 
 def load_qkv(table, src, shard_id, n_q, n_kv, head_dim, tp_rank, tp_size) -> None:
     """[NANO22] §5 QKV loader, in place on the rank's table: segments q
-    (n_q/t heads), k and v (the rank's KV heads each) in that order; q takes
-    chunk(t)[tp_rank] of its heads, k and v take the heads
-    kv_heads_for_rank gives (the same chunk when t <= n_kv, the replicated
-    head r / (t / n_kv) otherwise, [GUIDE62] §2.2)."""
+    (n_q/t heads), k and v (the rank's KV heads each) in that order, with the
+    KV replication of kv_heads_for_rank ([GUIDE62] §2.2)."""
+    src = np.ascontiguousarray(src)
     if n_q % tp_size:
         raise OracleError("load_qkv: n_q not divisible by tp_size")
-    nq_r = n_q // tp_size
-    first, kvc = kv_heads_for_rank(n_kv, tp_rank, tp_size)
-    if shard_id == 0:
-        off, heads = 0, src[tp_rank * nq_r * head_dim:(tp_rank + 1) * nq_r * head_dim]
-    elif shard_id == 1:
-        off, heads = nq_r * head_dim, src[first * head_dim:(first + kvc) * head_dim]
-    elif shard_id == 2:
-        off, heads = (nq_r + kvc) * head_dim, src[first * head_dim:(first + kvc) * head_dim]
-    else:
+    if shard_id not in (0, 1, 2):
         raise OracleError("load_qkv: shard_id must be 0 (q), 1 (k) or 2 (v)")
-    table[off:off + heads.shape[0]] = convert(heads, table.dtype == np.uint16)
+    h = src.shape[1]
+    _, kvc = kv_heads_for_rank(n_kv, tp_rank, tp_size)
+    rows = (n_q // tp_size + 2 * kvc) * head_dim
+    if not table.flags["C_CONTIGUOUS"] or table.shape != (rows, h):
+        raise OracleError("load_qkv: table must be a contiguous [(n_q/t + 2 kvc) hd, h] array")
+    if src.shape[0] != (n_q if shard_id == 0 else n_kv) * head_dim:
+        raise OracleError("load_qkv: src has the wrong number of rows")
+    _check(_load().orc_load_qkv(table.ctypes.data, _ldt(table), src.ctypes.data, _ldt(src), shard_id, n_q, n_kv,
+                                head_dim, h, tp_rank, tp_size), "load_qkv")
 
 
 # --- vocab parallel ----------------------------------------------------------

@@ -300,6 +300,108 @@ ORC_API int orc_shard_qkv(const void* wq, const void* wk, const void* wv,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Checkpoint-style loaders                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* The loaders of [NANO22] §3-§5 applied to a full checkpoint tensor, in the
+ * order [MINISGL] §8 (weight loading and sharding) gives: select the rank's
+ * shard, convert it to the parameter's dtype, copy it into the parameter.
+ * Element types: 0 = fp32, 1 = bf16 (raw 16-bit patterns).  Copying into a
+ * parameter of the other type is torch's copy_: fp32 -> bf16 rounds to
+ * nearest even (orc_f32_to_bf16), bf16 -> fp32 is exact (the 16 bits become
+ * the top half of the fp32 encoding), equal types copy the bits. */
+static void convert_one(const void* src, int src_dt, int64_t si, void* dst, int dst_dt, int64_t di) {
+    if (src_dt == 0 && dst_dt == 0) {
+        ((float*)dst)[di] = ((const float*)src)[si];
+    } else if (src_dt == 0) {
+        ((uint16_t*)dst)[di] = orc_f32_to_bf16(((const float*)src)[si]);
+    } else if (dst_dt == 1) {
+        ((uint16_t*)dst)[di] = ((const uint16_t*)src)[si];
+    } else {
+        uint32_t u = (uint32_t)((const uint16_t*)src)[si] << 16;
+        memcpy((float*)dst + di, &u, 4);
+    }
+}
+
+/* Rows [r0, r0 + nrows) x columns [c0, c0 + ncols) of src ([*, src_cols] in
+ * src_dt) converted into dst rows [d0, d0 + nrows) ([*, ncols] in dst_dt). */
+static void copy_convert(const void* src, int src_dt, int64_t src_cols, int64_t r0, int64_t c0,
+                         int64_t nrows, int64_t ncols, void* dst, int dst_dt, int64_t d0) {
+    for (int64_t i = 0; i < nrows; ++i)
+        for (int64_t j = 0; j < ncols; ++j)
+            convert_one(src, src_dt, (r0 + i) * src_cols + c0 + j, dst, dst_dt, (d0 + i) * ncols + j);
+}
+
+static int valid_load_dt(int a, int b) { return (a == 0 || a == 1) && (b == 0 || b == 1); }
+
+/* Column (dim 0, [NANO22] §3) or row (dim 1, §4) parallel loader: the
+ * rank's narrow(dim, r S/t, S/t) of src [rows, cols], converted into dst
+ * ([rows/t, cols] or [rows, cols/t]).  Returns 2 when t does not divide S. */
+ORC_API int orc_load_shard(const void* src, int src_dt, int64_t rows, int64_t cols, int dim, int tp_rank,
+                           int tp_size, void* dst, int dst_dt) {
+    if (tp_size < 1 || tp_rank < 0 || tp_rank >= tp_size || (dim != 0 && dim != 1)) return 1;
+    if (!valid_load_dt(src_dt, dst_dt)) return 1;
+    int64_t s = dim == 0 ? rows : cols;
+    if (s % tp_size) return 2;
+    int64_t sh = s / tp_size;
+    if (dim == 0)
+        copy_convert(src, src_dt, cols, (int64_t)tp_rank * sh, 0, sh, cols, dst, dst_dt, 0);
+    else
+        copy_convert(src, src_dt, cols, 0, (int64_t)tp_rank * sh, rows, sh, dst, dst_dt, 0);
+    return 0;
+}
+
+/* [NANO22] §5, the merged column-parallel loader, one projection per call
+ * (shard_id 0 = gate, 1 = up), in place on the rank's [2 f/t, h] table:
+ *   cut 1: output_sizes = [f, f]; the projection's segment starts at
+ *          sum(output_sizes[:shard_id]) / t and is output_sizes[shard_id] / t
+ *          rows long;
+ *   cut 2: src [f, h] is chunked into t pieces along dim 0 and piece
+ *          tp_rank fills the segment, converted to the table's type.
+ * Rows outside the segment are not touched. */
+ORC_API int orc_load_gate_up(void* table, int table_dt, const void* src, int src_dt, int shard_id, int64_t f,
+                             int64_t h, int tp_rank, int tp_size) {
+    if (tp_size < 1 || tp_rank < 0 || tp_rank >= tp_size || shard_id < 0 || shard_id > 1) return 1;
+    if (!valid_load_dt(src_dt, table_dt)) return 1;
+    if (f % tp_size) return 2;
+    int64_t output_sizes[2] = {f, f};
+    int64_t before = 0;
+    for (int p = 0; p < shard_id; ++p) before += output_sizes[p];
+    int64_t seg_off = before / tp_size;
+    int64_t seg_len = output_sizes[shard_id] / tp_size;
+    int64_t chunk = output_sizes[shard_id] / tp_size;
+    copy_convert(src, src_dt, h, (int64_t)tp_rank * chunk, 0, seg_len, h, table, table_dt, seg_off);
+    return 0;
+}
+
+/* [NANO22] §5, the QKV loader, one projection per call, in place on the
+ * rank's [(nq/t + 2 kvc) hd, h] table (segments q, k, v in that order):
+ *   shard_id 0 (q): src [nq hd, h]; the segment at row 0 takes the rank's
+ *                   chunk of the heads, heads [r nq/t, (r+1) nq/t);
+ *   shard_id 1 (k), 2 (v): src [n_kv hd, h]; the segment after q (k) or
+ *                   after q and k (v) takes the rank's KV heads from
+ *                   orc_kv_heads_for_rank (its chunk when t <= n_kv, the
+ *                   replicated head r / (t/n_kv) otherwise, [GUIDE62] §2.2).
+ * Rows outside the segment are not touched. */
+ORC_API int orc_load_qkv(void* table, int table_dt, const void* src, int src_dt, int shard_id, int64_t nq,
+                         int64_t n_kv, int64_t hd, int64_t h, int tp_rank, int tp_size) {
+    if (tp_size < 1 || tp_rank < 0 || tp_rank >= tp_size || shard_id < 0 || shard_id > 2) return 1;
+    if (!valid_load_dt(src_dt, table_dt)) return 1;
+    if (nq % tp_size) return 2;
+    int64_t kv0 = 0, kvc = 0;
+    int rc = orc_kv_heads_for_rank(n_kv, tp_rank, tp_size, &kv0, &kvc);
+    if (rc) return rc;
+    int64_t qc = nq / tp_size;
+    if (shard_id == 0)
+        copy_convert(src, src_dt, h, (int64_t)tp_rank * qc * hd, 0, qc * hd, h, table, table_dt, 0);
+    else if (shard_id == 1)
+        copy_convert(src, src_dt, h, kv0 * hd, 0, kvc * hd, h, table, table_dt, qc * hd);
+    else
+        copy_convert(src, src_dt, h, kv0 * hd, 0, kvc * hd, h, table, table_dt, (qc + kvc) * hd);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Vocab-parallel embedding and LM head                                     */
 /* ------------------------------------------------------------------------ */
 

@@ -82,6 +82,30 @@ def test_silu_closed_forms():
     assert oracle.silu(-800.0) == 0.0 or abs(oracle.silu(-800.0)) < 1e-300
 
 
+def test_silu_mul_matches_torch_silu_of_gate_times_up():
+    """Tensor parallelism: implemented from scratch, "Implementation", class
+    TPMLP: the local activation is F.silu(gate(x)) * up(x), SiLU applied to
+    the gate product only.  Pinned to torch's F.silu in float64 on inputs
+    where gate and up differ in sign and scale, so that SiLU taken of the up
+    product, a dropped factor or a swapped pair fails."""
+    rng = np.random.default_rng(11)
+    g = rng.standard_normal((7, 33)) * 3.0
+    u = rng.standard_normal((7, 33)) * 0.5 + 0.25
+    ref = (F.silu(torch.from_numpy(g)) * torch.from_numpy(u)).numpy()
+    got = oracle.silu_mul(g, u)
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-15)
+    # the swapped-operand form SiLU(u) * g and a plain product are far off
+    swapped = (F.silu(torch.from_numpy(u)) * torch.from_numpy(g)).numpy()
+    assert relf(got, swapped) > 0.5
+    assert relf(got, g * u) > 0.1
+    # closed forms element by element: a zero gate gives 0, SiLU(32) * u is
+    # 32 u up to e^-32, and a negative gate of large size gives (-0) * u
+    z = oracle.silu_mul(np.array([0.0, 32.0, -50.0]), np.array([5.0, 3.0, 2.0]))
+    assert z[0] == 0.0
+    assert z[1] == pytest.approx(96.0, rel=1e-13)
+    assert abs(z[2]) < 1e-19
+
+
 # --------------------------------------------------------------------------
 # Linear layers: the pages' printed worked examples (bit-exact integers)
 # --------------------------------------------------------------------------
