@@ -30,7 +30,14 @@
  *     Divisibility is an error, as the pages' divide() assertion makes it.
  *   - Alignment: 16-byte aligned pointers and reduction sizes that are a
  *     multiple of 8 (bf16) take the vector path; anything else takes a
- *     slower element-wise path with identical results.
+ *     slower element-wise path with identical results.  Workspaces and
+ *     staging buffers must be aligned as each entry point states
+ *     (TP_EALIGN otherwise).
+ *   - bf16 GEMM sizes: the kernels address operand tiles with 32-bit byte
+ *     offsets, so the reduction size K must satisfy 256 K 2 < 2^31
+ *     (K < 4194304), and a fused gate_up table must have its up rows within
+ *     2 GiB of its gate rows: (f_local + 256) K 2 < 2^31.  Larger shapes
+ *     return TP_ESHAPE.
  */
 #ifndef TPSHARD_H
 #define TPSHARD_H
@@ -54,7 +61,8 @@ typedef enum {
     TP_EINVAL = 1,      /* bad argument: null pointer, rank outside [0, t), t outside [1, 64], n <= 0 ... */
     TP_ESHAPE = 2,      /* sizes that do not divide, or buffers whose sizes do not match */
     TP_EDTYPE = 3,      /* unsupported element type or (input, output) pair */
-    TP_EALIGN = 4,      /* reserved: no entry point currently requires alignment */
+    TP_EALIGN = 4,      /* a buffer that must be aligned is not: workspaces (16 bytes; 256 for
+                           tp_mlp_rank_forward), loader staging, attention qkv/out (16 bytes) */
     TP_EHIP = 5,        /* the HIP runtime reported an error on launch */
     TP_EWORKSPACE = 6   /* workspace missing or smaller than the matching *_workspace_bytes query */
 } tp_status;
@@ -179,7 +187,8 @@ TP_API tp_status tp_load_qkv(const void* src /*HOST*/, tp_dtype src_dt, int shar
  * is element-wise, so it needs no communication).  Fused: gate and up
  * products are never written; act is rounded once to dt.
  *   x [n, h] dt; w_gate_up [2 f_local, h] dt; act [n, f_local] dt.
- * workspace: at least tp_gate_up_workspace_bytes(...) bytes (may be 0). */
+ * workspace: at least tp_gate_up_workspace_bytes(...) bytes, 16-byte
+ * aligned (NULL allowed when the query returns 0). */
 TP_API tp_status tp_gate_up_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_dtype dt,
                                      size_t* bytes /*HOST*/);
 TP_API tp_status tp_gate_up_act_rank(const void* x, int64_t n, int64_t h, const void* w_gate_up,
@@ -191,7 +200,8 @@ TP_API tp_status tp_gate_up_act_rank(const void* x, int64_t n, int64_t h, const 
 /* y = x . w^T (+ bias).  Row-parallel layers pass the bias on rank 0 only, so
  * that the sum over ranks adds it once ([NANO22] §4).
  *   x [n, k] dt; w [m, k] dt; bias [m] dt or NULL; y [n, m] out_dt.
- * workspace: at least tp_linear_workspace_bytes(...) bytes (may be 0). */
+ * workspace: at least tp_linear_workspace_bytes(...) bytes, 16-byte
+ * aligned (NULL allowed when the query returns 0). */
 TP_API tp_status tp_linear_workspace_bytes(int64_t n, int64_t k, int64_t m, tp_dtype dt,
                                     size_t* bytes /*HOST*/);
 TP_API tp_status tp_linear_rank_forward(const void* x, int64_t n, int64_t k, const void* w,
@@ -336,7 +346,9 @@ TP_API tp_status tp_vocab_embed_rank(const int64_t* ids, int64_t n, const void* 
 
 /* logits_r = x . T_r^T, the rank's slice of the logits along vocab
  * ([VLLM13] §2.4.2: Y_i = X E_i^T; the full logits are the concatenation).
- *   x [n, h] dt; table_shard [v_local, h] dt; logits [n, v_local] out_dt. */
+ *   x [n, h] dt; table_shard [v_local, h] dt; logits [n, v_local] out_dt.
+ * workspace: at least tp_linear_workspace_bytes(n, h, v_local, dt) bytes,
+ * 16-byte aligned (NULL allowed when that is 0). */
 TP_API tp_status tp_lm_head_rank(const void* x, int64_t n, int64_t h, const void* table_shard,
                           int64_t v_local, tp_dtype dt, void* logits, tp_dtype out_dt,
                           void* workspace, size_t workspace_bytes, void* stream);

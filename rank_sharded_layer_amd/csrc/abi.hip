@@ -75,6 +75,36 @@ tp_status check_gemm_dims(int64_t n, int64_t k, int64_t m, const char* fn) {
     return TP_OK;
 }
 
+// The bf16 GEMM kernels address a tile's operand rows through 32-bit byte
+// offsets from the tile's first row (buffer loads).  A tile spans at most
+// 256 rows of either operand, and a gated tile's up rows sit f_local rows
+// after its gate rows in the fused table, so both spans must stay under
+// 2 GiB: 256 k 2 < 2^31 (k < 2^22) and, gated, (f_local + 256) k 2 < 2^31
+// (the fused table of the rank under about 2 GiB).
+tp_status check_bf16_offsets(int64_t k, int64_t f_local, bool gated, tp_dtype dt, const char* fn) {
+    if (dt != TP_BF16) return TP_OK;
+    const int64_t lim = (int64_t)1 << 31;
+    if (256 * k * 2 >= lim)
+        return fail(TP_ESHAPE, "%s: reduction size %lld too large (bf16 tiles need 256 rows x K under 2 GiB)", fn,
+                    (long long)k);
+    if (gated && (f_local + 256) * k * 2 >= lim)
+        return fail(TP_ESHAPE, "%s: fused gate_up table of %lld x %lld too large (the up rows must lie within 2 GiB "
+                    "of the gate rows)", fn, (long long)(2 * f_local), (long long)k);
+    return TP_OK;
+}
+
+// a caller workspace that is needed must be 16-byte aligned (vector stores
+// of the fp32 partial tiles)
+tp_status check_ws(size_t need, void* workspace, size_t workspace_bytes, size_t align, const char* fn) {
+    if (need == 0) return TP_OK;
+    if (!workspace || workspace_bytes < need)
+        return fail(TP_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) & (align - 1))
+        return fail(TP_EALIGN, "%s: workspace not %zu-byte aligned", fn, align);
+    return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -301,6 +331,7 @@ tp_status tp_gate_up_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_d
     if (!bytes) return fail(TP_EINVAL, "tp_gate_up_workspace_bytes: null pointer");
     if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_gate_up_workspace_bytes: bad dtype %d", (int)dt);
     if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_gate_up_workspace_bytes")) return st;
+    if (tp_status st = check_bf16_offsets(h, f_local, true, dt, "tp_gate_up_workspace_bytes")) return st;
     *bytes = tpk::plan_gemm(n, f_local, h, true, dt).ws_bytes;
     return ok();
 }
@@ -310,10 +341,9 @@ tp_status tp_gate_up_act_rank(const void* x, int64_t n, int64_t h, const void* w
     if (!x || !w_gate_up || !act) return fail(TP_EINVAL, "tp_gate_up_act_rank: null pointer");
     if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_gate_up_act_rank: bad dtype %d", (int)dt);
     if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_gate_up_act_rank")) return st;
+    if (tp_status st = check_bf16_offsets(h, f_local, true, dt, "tp_gate_up_act_rank")) return st;
     tpk::GemmPlan pl = tpk::plan_gemm(n, f_local, h, true, dt);
-    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes))
-        return fail(TP_EWORKSPACE, "tp_gate_up_act_rank: workspace of %zu bytes needed, %zu given", pl.ws_bytes,
-                    workspace ? workspace_bytes : (size_t)0);
+    if (tp_status st = check_ws(pl.ws_bytes, workspace, workspace_bytes, 16, "tp_gate_up_act_rank")) return st;
     return hip_status(tpk::launch_gemm(pl, x, w_gate_up, nullptr, act, n, f_local, h, true, dt, dt, workspace,
                                        as_stream(stream)),
                       "tp_gate_up_act_rank");
@@ -323,6 +353,7 @@ tp_status tp_linear_workspace_bytes(int64_t n, int64_t k, int64_t m, tp_dtype dt
     if (!bytes) return fail(TP_EINVAL, "tp_linear_workspace_bytes: null pointer");
     if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_linear_workspace_bytes: bad dtype %d", (int)dt);
     if (tp_status st = check_gemm_dims(n, k, m, "tp_linear_workspace_bytes")) return st;
+    if (tp_status st = check_bf16_offsets(k, 0, false, dt, "tp_linear_workspace_bytes")) return st;
     *bytes = tpk::plan_gemm(n, m, k, false, dt).ws_bytes;
     return ok();
 }
@@ -334,10 +365,9 @@ tp_status tp_linear_rank_forward(const void* x, int64_t n, int64_t k, const void
     if (!valid_dt(dt) || !valid_dt(out_dt) || !valid_pair(dt, out_dt))
         return fail(TP_EDTYPE, "tp_linear_rank_forward: unsupported dtype pair (%d -> %d)", (int)dt, (int)out_dt);
     if (tp_status st = check_gemm_dims(n, k, m, "tp_linear_rank_forward")) return st;
+    if (tp_status st = check_bf16_offsets(k, 0, false, dt, "tp_linear_rank_forward")) return st;
     tpk::GemmPlan pl = tpk::plan_gemm(n, m, k, false, dt);
-    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes))
-        return fail(TP_EWORKSPACE, "tp_linear_rank_forward: workspace of %zu bytes needed, %zu given", pl.ws_bytes,
-                    workspace ? workspace_bytes : (size_t)0);
+    if (tp_status st = check_ws(pl.ws_bytes, workspace, workspace_bytes, 16, "tp_linear_rank_forward")) return st;
     return hip_status(tpk::launch_gemm(pl, x, w, bias, y, n, m, k, false, dt, out_dt, workspace, as_stream(stream)),
                       "tp_linear_rank_forward");
 }
@@ -346,6 +376,8 @@ tp_status tp_mlp_workspace_bytes(int64_t n, int64_t h, int64_t f_local, tp_dtype
     if (!bytes) return fail(TP_EINVAL, "tp_mlp_workspace_bytes: null pointer");
     if (!valid_dt(dt)) return fail(TP_EDTYPE, "tp_mlp_workspace_bytes: bad dtype %d", (int)dt);
     if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_mlp_workspace_bytes")) return st;
+    if (tp_status st = check_bf16_offsets(h, f_local, true, dt, "tp_mlp_workspace_bytes")) return st;
+    if (tp_status st = check_bf16_offsets(f_local, 0, false, dt, "tp_mlp_workspace_bytes")) return st;
     *bytes = mlp_layout(n, h, f_local, dt).total;
     return ok();
 }
@@ -357,11 +389,10 @@ tp_status tp_mlp_rank_forward(const void* x, int64_t n, int64_t h, const void* w
     if (!valid_dt(dt) || !valid_dt(out_dt) || !valid_pair(dt, out_dt))
         return fail(TP_EDTYPE, "tp_mlp_rank_forward: unsupported dtype pair (%d -> %d)", (int)dt, (int)out_dt);
     if (tp_status st = check_gemm_dims(n, h, 2 * f_local, "tp_mlp_rank_forward")) return st;
+    if (tp_status st = check_bf16_offsets(h, f_local, true, dt, "tp_mlp_rank_forward")) return st;
+    if (tp_status st = check_bf16_offsets(f_local, 0, false, dt, "tp_mlp_rank_forward")) return st;
     MlpLayout L = mlp_layout(n, h, f_local, dt);
-    if (!workspace || workspace_bytes < L.total)
-        return fail(TP_EWORKSPACE, "tp_mlp_rank_forward: workspace of %zu bytes needed, %zu given", L.total,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (((uintptr_t)workspace) & 255u) return fail(TP_EINVAL, "tp_mlp_rank_forward: workspace not 256-byte aligned");
+    if (tp_status st = check_ws(L.total, workspace, workspace_bytes, 256, "tp_mlp_rank_forward")) return st;
     char* ws = static_cast<char*>(workspace);
     void* act = ws;
     void* split = ws + L.act_bytes;
@@ -411,12 +442,9 @@ tp_status tp_attention_rank(const void* qkv, int64_t n, int nq, int nkv, int hea
     if (!qkv || !out) return fail(TP_EINVAL, "tp_attention_rank: null pointer");
     if (tp_status st = check_attention(n, nq, nkv, head_dim, dt, "tp_attention_rank")) return st;
     const size_t need = tpk::attention_ws_bytes(n, nq, nkv, causal);
-    if (need && (!workspace || workspace_bytes < need))
-        return fail(TP_EWORKSPACE, "tp_attention_rank: workspace of %zu bytes needed, %zu given", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (need && (((uintptr_t)workspace) & 15u)) return fail(TP_EINVAL, "tp_attention_rank: workspace not 16-byte aligned");
+    if (tp_status st = check_ws(need, workspace, workspace_bytes, 16, "tp_attention_rank")) return st;
     if ((((uintptr_t)qkv) | ((uintptr_t)out)) & 15u)
-        return fail(TP_EINVAL, "tp_attention_rank: qkv and out must be 16-byte aligned");
+        return fail(TP_EALIGN, "tp_attention_rank: qkv and out must be 16-byte aligned");
     const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)(n * (int64_t)(nq + 2 * nkv) * head_dim * 2);
     const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)(n * (int64_t)nq * head_dim * 2);
     if (n > 0 && o0 < q1 && q0 < o1) return fail(TP_EINVAL, "tp_attention_rank: out overlaps qkv");
@@ -544,10 +572,9 @@ tp_status tp_lm_head_rank(const void* x, int64_t n, int64_t h, const void* table
     if (!valid_dt(dt) || !valid_dt(out_dt) || !valid_pair(dt, out_dt))
         return fail(TP_EDTYPE, "tp_lm_head_rank: unsupported dtype pair (%d -> %d)", (int)dt, (int)out_dt);
     if (tp_status st = check_gemm_dims(n, h, v_local, "tp_lm_head_rank")) return st;
+    if (tp_status st = check_bf16_offsets(h, 0, false, dt, "tp_lm_head_rank")) return st;
     tpk::GemmPlan pl = tpk::plan_gemm(n, v_local, h, false, dt);
-    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes))
-        return fail(TP_EWORKSPACE, "tp_lm_head_rank: workspace of %zu bytes needed, %zu given", pl.ws_bytes,
-                    workspace ? workspace_bytes : (size_t)0);
+    if (tp_status st = check_ws(pl.ws_bytes, workspace, workspace_bytes, 16, "tp_lm_head_rank")) return st;
     return hip_status(tpk::launch_gemm(pl, x, table_shard, nullptr, logits, n, v_local, h, false, dt, out_dt,
                                        workspace, as_stream(stream)),
                       "tp_lm_head_rank");

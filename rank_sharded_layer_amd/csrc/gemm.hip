@@ -264,7 +264,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[B
 // its B operand, so in each 32x32 result lane l holds token row (l & 31) and
 // output columns 8g + 4(l >> 5) + q, q = 0..3: four consecutive columns per
 // group g, written with one 8-byte (bf16) or 16-byte (fp32) store.
-template <int BM, int BN, int WM, int WN, int EPI, bool VEC>
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
     constexpr int BK = 64;
     constexpr int NT = WM * WN * 64;
@@ -278,7 +278,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
     static_assert(BM * KC % NT == 0 && BN * KC % NT == 0, "tile/threads mismatch");
     static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up MFMA tiles");
     constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
-    constexpr uint32_t SENT = 0x80000000u;   // buffer offset past num_records: the load returns 0
 
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -312,52 +311,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs p) {
     };
 
     // ---- global -> register staging ------------------------------------
-    // Vector path: raw buffer loads.  Each thread's chunks keep a fixed byte
-    // offset from a per-tile base that advances by BK per K step; chunks of
-    // rows outside the matrix (or past the K end in the last step) use an
-    // offset beyond num_records, for which the hardware returns zeros, so the
-    // loop has no per-load branches.
+    // Element-wise loads: this kernel serves operands the 16-byte buffer
+    // loads of the other kernels cannot (K not a multiple of 8, or operands
+    // not 16-byte aligned).  Rows outside the matrix and K past the end of
+    // the range read as zero.
     u32x4 ra[A_LD], rb[B_LD];
-    uint32_t offa[A_LD], offb[B_LD];
-    int kca[A_LD], kcb[B_LD];
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int v = tid + i * NT;
-        const int row = v / KC;
-        kca[i] = v % KC;
-        offa[i] = m0 + row < p.M ? (uint32_t)(((int64_t)row * p.K + kca[i] * 8) * 2) : SENT;
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int v = tid + i * NT;
-        const int row = v / KC;
-        kcb[i] = v % KC;
-        bool ok;
-        const int64_t gb = b_row(row, ok);
-        offb[i] = ok ? (uint32_t)(((gb - n0) * p.K + kcb[i] * 8) * 2) : SENT;
-    }
-    const uint16_t* a_tile = A + m0 * p.K;
-    const uint16_t* b_tile = B + n0 * p.K;
 
     auto load_tile = [&](int64_t k0) {
-        if (VEC) {
-            const bool tail = k0 + BK > k_end;
-            __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
-            __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
-#pragma unroll
-            for (int i = 0; i < A_LD; ++i) {
-                const uint32_t o = (tail && k0 + kca[i] * 8 >= k_end) ? SENT : offa[i];
-                ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, o, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i) {
-                const uint32_t o = (tail && k0 + kcb[i] * 8 >= k_end) ? SENT : offb[i];
-                rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rs, o, 0, 0);
-            }
-            return;
-        }
         // element-wise path (K not a multiple of 8 or unaligned operands)
         auto load_chunk = [&](const uint16_t* src, int64_t row, bool ok, int64_t k) -> u32x4 {
             uint32_t w[4];
@@ -1272,156 +1232,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
     }
 }
 
-// Decode-sized GEMM (M <= 64 tokens): weight streaming.  HBM-bound on the
-// weights, so the design keeps many weight bytes in flight per CU and reads
-// every weight byte once:
-//   * a workgroup owns 16 output columns over the FULL K (gated: 16 gate rows
-//     and the same 16 up rows; plain: 16 weight rows) -- f_local/16 or N/16
-//     workgroups, two per CU;
-//   * its KW waves split K; each wave streams its weight slice and the
-//     matching token slice straight from global memory into MFMA operand
-//     registers (v_mfma_f32_16x16x32_bf16: lane l holds row l & 15 and k
-//     offset 8 (l >> 4), so the four lanes of a row read 64 contiguous bytes
-//     per load), two 64-wide K blocks ahead of the MFMAs;
-//   * the waves' partial sums meet in LDS and are added in wave order
-//     0..KW-1 (deterministic), then the gated SiLU(g)*u or plain epilogue.
-template <int EPI, int KW, bool KTAIL>
-__global__ __launch_bounds__(KW * 64) void gemm_bf16_decode_kernel(GemmArgs p) {
-    constexpr bool GATED = EPI == EPI_GATED_BF16;
-    constexpr int WT = GATED ? 2 : 1;     // 16-row weight tiles per wave
-    constexpr int XT = 4;                 // 16-token tiles (64 tokens)
-    constexpr int NS = 3;                 // register stages (blocks in flight + 1)
-    constexpr uint32_t SENT = 0x80000000u;
-    constexpr int PER_WAVE = WT * XT * 4 * 64;
-    __shared__ __attribute__((aligned(16))) float red[KW * PER_WAVE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t n0 = (int64_t)blockIdx.x * 16;   // first output column of the workgroup
-
-    // K range of this wave (multiples of 64 except at the end)
-    const int64_t chunk = ceil_div(ceil_div(p.K, KW), 64) * 64;
-    const int64_t kw0 = (int64_t)wid * chunk;
-    int64_t kw1 = kw0 + chunk;
-    if (kw1 > p.K) kw1 = p.K;
-
-    const int q = lane >> 4;              // k offset 8q within a 32-wide sub-step
-    uint32_t wrow[WT], xrow[XT];
-#pragma unroll
-    for (int t = 0; t < WT; ++t) {
-        const int64_t c = n0 + (lane & 15);
-        int64_t row;
-        bool ok;
-        if (GATED) {
-            ok = c < p.N;
-            row = t == 0 ? c : p.N + c;
-        } else {
-            ok = c < p.Nb;
-            row = c;
-        }
-        wrow[t] = ok ? (uint32_t)((row * p.K + 8 * q) * 2) : SENT;
-    }
-#pragma unroll
-    for (int j = 0; j < XT; ++j) {
-        const int64_t m = 16 * j + (lane & 15);
-        xrow[j] = m < p.M ? (uint32_t)((m * p.K + 8 * q) * 2) : SENT;
-    }
-
-    f32x4 acc[WT][XT];
-#pragma unroll
-    for (int t = 0; t < WT; ++t)
-#pragma unroll
-        for (int j = 0; j < XT; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[t][j][r] = 0.0f;
-
-    // a 64-wide K block = two 32-wide sub-steps
-    bf16x8 wv[NS][WT][2], xv[NS][XT][2];
-    // Offsets past num_records (the sentinel plus up to 64) load zeros.  With
-    // KTAIL (K not a multiple of 64), chunks at or past the wave's k end are
-    // fetched as zeros too.
-    auto load_block = [&](int64_t kb, int slot) {
-        __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + kb), (short)0, 0x7fffffff, 0x00020000);
-        __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + kb), (short)0, 0x7fffffff, 0x00020000);
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            uint32_t kill = 0;
-            if (KTAIL) kill = kb + 32 * s2 + 8 * q >= kw1 ? SENT : 0u;
-#pragma unroll
-            for (int t = 0; t < WT; ++t)
-                wv[slot][t][s2] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, (wrow[t] | kill) + 64 * s2, 0, 0));
-#pragma unroll
-            for (int j = 0; j < XT; ++j)
-                xv[slot][j][s2] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, (xrow[j] | kill) + 64 * s2, 0, 0));
-        }
-    };
-    auto mma_block = [&](int slot) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int t = 0; t < WT; ++t)
-#pragma unroll
-                for (int j = 0; j < XT; ++j)
-                    acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[slot][t][s2], xv[slot][j][s2], acc[t][j], 0, 0, 0);
-    };
-
-    // NS-1 blocks are in flight while a block is multiplied; fences keep the
-    // loads of block b+NS-1 ahead of the MFMAs of block b
-    const int nb = kw1 > kw0 ? (int)ceil_div(kw1 - kw0, 64) : 0;
-    auto kof = [&](int b) { return kw0 + (int64_t)b * 64; };
-#pragma unroll
-    for (int b = 0; b < NS - 1; ++b)
-        if (b < nb) load_block(kof(b), b);
-    int b = 0;
-    for (; b + NS - 1 < nb; b += NS) {
-#pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            if (b + u + NS - 1 < nb) load_block(kof(b + u + NS - 1), (u + NS - 1) % NS);
-            __builtin_amdgcn_sched_barrier(0);
-            if (b + u < nb) mma_block(u);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u)
-        if (b + u < nb) mma_block(u);
-
-    // ---- cross-wave reduction in LDS, in wave order --------------------
-#pragma unroll
-    for (int t = 0; t < WT; ++t)
-#pragma unroll
-        for (int j = 0; j < XT; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[wid * PER_WAVE + ((t * XT + j) * 4 + r) * 64 + lane] = acc[t][j][r];
-    __syncthreads();
-    // element e = (j, r, l): token 16 j + (l & 15), column n0 + 4 (l >> 4) + r
-    for (int e = tid; e < XT * 4 * 64; e += KW * 64) {
-        const int l = e & 63;
-        const int r = (e >> 6) & 3;
-        const int j = e >> 8;
-        const int64_t m = 16 * j + (l & 15);
-        const int64_t n = n0 + 4 * (l >> 4) + r;
-        float v0 = 0.0f, v1 = 0.0f;
-        for (int w = 0; w < KW; ++w) {
-            v0 = v0 + red[w * PER_WAVE + ((0 * XT + j) * 4 + r) * 64 + l];
-            if (GATED) v1 = v1 + red[w * PER_WAVE + ((1 * XT + j) * 4 + r) * 64 + l];
-        }
-        if (m >= p.M || n >= p.N) continue;
-        if (GATED) {
-            static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(silu_mul(v0, v1));
-        } else {
-            if (p.bias) v0 = v0 + bf16_to_f32(p.bias[n]);
-            if (EPI == EPI_STORE_F32)
-                static_cast<float*>(p.C)[m * p.N + n] = v0;
-            else
-                static_cast<uint16_t*>(p.C)[m * p.N + n] = f32_to_bf16(v0);
-        }
-    }
-}
-
 // Adds the split-K partial sums in split order and applies the epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float* __restrict__ ws, int splits,
@@ -2160,7 +1970,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs p, int BM, int
 
 // ---- planning -------------------------------------------------------------
 
-enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DECODE = 5, K_BF16_DEC4 = 6,
+enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DEC4 = 6,
             K_BF16_STREAM = 7, K_BF16_RS = 8 };
 
 // Tile configurations (BM tokens x BN weight rows):
@@ -2213,48 +2023,6 @@ static void tiles_for(int kern, int64_t M, int64_t N, bool gated, int& tm, int& 
 // the 256 architectural VGPRs for the accumulators and spill).
 static int huge_kernel() { return K_BF16_HUGE8; }
 
-// Weight-streaming decode kernel: off by default (the split-K tiled path
-// measures faster: this kernel re-reads the token block once per 16 output
-// columns); TPSHARD_GEMM_DECODE=1 selects it.
-static bool decode_enabled() {
-    static int on = -1;
-    if (on < 0) {
-        const char* e = getenv("TPSHARD_GEMM_DECODE");
-        on = (e && atoi(e) == 1) ? 1 : 0;
-    }
-    return on == 1;
-}
-
-// deep-pipelined large-tile kernel switch (TPSHARD_GEMM_PIPE=0 turns it off)
-static bool pipe_enabled() {
-    static int on = -1;
-    if (on < 0) {
-        const char* e = getenv("TPSHARD_GEMM_PIPE");
-        on = (e && atoi(e) == 0) ? 0 : 1;
-    }
-    return on == 1;
-}
-
-// paired K = 64 stages in the deep-pipelined kernel (TPSHARD_GEMM_PAIR=0 turns them off)
-static bool pair_enabled() {
-    static int on = -1;
-    if (on < 0) {
-        const char* e = getenv("TPSHARD_GEMM_PAIR");
-        on = (e && atoi(e) == 0) ? 0 : 1;
-    }
-    return on == 1;
-}
-
-// weight-streaming decode kernel switch (TPSHARD_GEMM_STREAM=0 turns it off)
-static bool stream_enabled() {
-    static int on = -1;
-    if (on < 0) {
-        const char* e = getenv("TPSHARD_GEMM_STREAM");
-        on = (e && atoi(e) == 0) ? 0 : 1;
-    }
-    return on == 1;
-}
-
 // CUs of an MI355X: the weight-streaming kernel runs one workgroup on each
 constexpr int kStreamWGs = 256;
 
@@ -2267,42 +2035,17 @@ static int64_t stream_units_of(int64_t N, int64_t K, bool gated) {
     return make_stream_op(nullptr, nullptr, 1, N, K, gated, nullptr, kStreamWGs).units;
 }
 
-// register-streaming decode kernel switch (TPSHARD_GEMM_RS=0 turns it off)
-static bool rs_enabled() {
-    static int on = -1;
-    if (on < 0) {
-        const char* e = getenv("TPSHARD_GEMM_RS");
-        on = (e && atoi(e) == 0) ? 0 : 1;
-    }
-    return on == 1;
-}
-
 static size_t rs_ws_bytes(int64_t M, int64_t K, int64_t Nb) {
     const RsOp o = make_rs_op(nullptr, nullptr, nullptr, M, K, Nb);
     return (size_t)o.S * (size_t)o.rbn * 1024 * sizeof(float);
 }
 
-// balanced-last-round switch (TPSHARD_GEMM_TAIL=0 turns it off)
-static bool tail_enabled() {
-    static int on = -1;
-    if (on < 0) {
-        const char* e = getenv("TPSHARD_GEMM_TAIL");
-        on = (e && atoi(e) == 0) ? 0 : 1;
-    }
-    return on == 1;
-}
-
 // Split-K target: about this many workgroups for shapes with fewer output
-// tiles than CUs (TPSHARD_SPLIT_TARGET overrides; tuning knob).
-static int64_t split_target(int64_t dflt) {
-    static int64_t t = -1;
-    if (t < 0) {
-        const char* e = getenv("TPSHARD_SPLIT_TARGET");
-        t = e ? atoll(e) : 0;
-        if (t < 1) t = 0;
-    }
-    return t > 0 ? t : dflt;
-}
+// tiles than CUs.
+constexpr int64_t kSplitTarget = 1024;
+// DEC4 (48 KiB of LDS ring, three workgroups per CU) aims at one full round
+// of 768 workgroups without exceeding it.
+constexpr int64_t kSplitTargetDec4 = 768;
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     GemmPlan pl{};
@@ -2318,14 +2061,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     }
     int tm, tn;
     const int64_t Nb0 = gated ? 2 * N : N;
-    if (M <= 64 && K % 8 == 0 && Nb0 * K * 2 < ((int64_t)1 << 31) && M * K * 2 < ((int64_t)1 << 31) &&
-        decode_enabled()) {
-        pl.kernel = K_BF16_DECODE;     // weight streaming, full K per workgroup, no workspace
-        return pl;
-    }
     // register-streaming kernel: enough 16-row blocks for two per workgroup
-    if (M <= 64 && K % 8 == 0 && K >= 1024 && Nb0 * K * 2 < ((int64_t)1 << 31) && M * K * 2 < ((int64_t)1 << 31) &&
-        rs_enabled()) {
+    if (M <= 64 && K % 8 == 0 && K >= 1024 && Nb0 * K * 2 < ((int64_t)1 << 31) && M * K * 2 < ((int64_t)1 << 31)) {
         const RsOp o = make_rs_op(nullptr, nullptr, nullptr, M, K, Nb0);
         if (o.rbn >= 2 * (256 / o.S)) {
             pl.kernel = K_BF16_RS;
@@ -2333,7 +2070,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
             return pl;
         }
     }
-    if (M <= 64 && K % 8 == 0 && Nb0 * K * 2 < ((int64_t)1 << 31) && stream_enabled()) {
+    if (M <= 64 && K % 8 == 0 && Nb0 * K * 2 < ((int64_t)1 << 31)) {
         if (stream_units_of(N, K, gated) >= 2 * kStreamWGs) {
             pl.kernel = K_BF16_STREAM;
             pl.ws_bytes = stream_ws_bytes(M, N, K, gated);
@@ -2344,16 +2081,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
         tiles_for(K_BF16_HUGE8, M, N, gated, tm, tn);
         pl.kernel = (int64_t)tm * tn >= 512 ? huge_kernel() : K_BF16_LARGE;
     } else {
-        pl.kernel = pipe_enabled() ? K_BF16_DEC4 : K_BF16_SMALL;
+        pl.kernel = K_BF16_DEC4;
     }
     tiles_for(pl.kernel, M, N, gated, tm, tn);
     const int64_t tiles = (int64_t)tm * tn;
     const int64_t Nb = gated ? 2 * N : N;
-    // fewer tiles than CUs: split K so that the launch fills the machine.
-    // DEC4 (48 KiB of LDS ring, three workgroups per CU) aims at one full
-    // round of 768 workgroups without exceeding it.
+    // fewer tiles than CUs: split K so that the launch fills the machine
     if (tiles < 256 && K >= 1024) {
-        int64_t want = pl.kernel == K_BF16_DEC4 ? split_target(768) / tiles : ceil_div(split_target(1024), tiles);
+        int64_t want = pl.kernel == K_BF16_DEC4 ? kSplitTargetDec4 / tiles : ceil_div(kSplitTarget, tiles);
         int64_t maxs = pl.kernel == K_BF16_DEC4 ? K / 256 : K / 512;
         int64_t s = want < maxs ? want : maxs;
         if (s > 1) {
@@ -2374,7 +2109,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     // for long K: each piece costs a 4-byte-per-element partial tile written
     // and read back, which pieces shorter than 1024 do not pay for.
     const int64_t slots = 256 * wgs_per_cu(pl.kernel);
-    if (pl.splits == 1 && K % 8 == 0 && tiles > slots && tiles % slots != 0 && tail_enabled()) {
+    if (pl.splits == 1 && K % 8 == 0 && tiles > slots && tiles % slots != 0) {
         const int64_t rem = tiles % slots;
         int64_t sp = slots / rem;
         if (sp >= 2) {
@@ -2403,27 +2138,29 @@ static void launch_tail_fixup(const GemmArgs& a, int ntiles, hipStream_t s) {
     }
 }
 
-static bool use_dl_kernels();
+// direct-to-LDS kernel with 32x32x16 MFMAs (128 x 128 tiles)
+template <int BM, int BN, int WM, int WN, int EPI>
+static void launch_dl_one(const GemmArgs& a, int splits, hipStream_t s) {
+    const int ntiles = a.tiles_m * a.tiles_n;
+    const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
+    dim3 grid((unsigned)units, (unsigned)splits);
+    const bool ktail = (a.K % 64) != 0 || (a.k_split % 64) != 0;
+    // LDS ring depth 2: deeper rings measured slower here because they
+    // cost a second resident workgroup per CU (occupancy beats depth)
+    constexpr int NST = 2;
+    if (ktail)
+        hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, true, NST>), grid, dim3(WM * WN * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, false, NST>), grid, dim3(WM * WN * 64), 0, s, a);
+    launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
+}
 
-template <int BM, int BN, int WM, int WN, int EPI, bool VEC>
-static void launch_bf16_one(const GemmArgs& a, int splits, size_t lds, hipStream_t s) {
-    if (VEC && use_dl_kernels()) {
-        // direct-to-LDS kernel: its LDS ring is a static allocation
-        const int ntiles = a.tiles_m * a.tiles_n;
-        const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
-        dim3 grid((unsigned)units, (unsigned)splits);
-        const bool ktail = (a.K % 64) != 0 || (a.k_split % 64) != 0;
-        // LDS ring depth 2: deeper rings measured slower here because they
-        // cost a second resident workgroup per CU (occupancy beats depth)
-        constexpr int NST = 2;
-        if (ktail)
-            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, true, NST>), grid, dim3(WM * WN * 64), 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm_bf16_dl_kernel<BM, BN, WM, WN, EPI, false, NST>), grid, dim3(WM * WN * 64), 0, s, a);
-        launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
-        return;
-    }
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, VEC>;   // whole tiles only (no tail pieces)
+// register-staged kernel with element-wise loads (operands the 16-byte
+// buffer loads cannot serve); whole tiles only
+template <int BM, int BN, int WM, int WN, int EPI>
+static void launch_reg_one(const GemmArgs& a, int splits, hipStream_t s) {
+    const size_t lds = (size_t)2 * (BM + BN) * 64 * sizeof(uint16_t);
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI>;
     if (lds > 65536) {
         // opt in to more than 64 KiB of LDS once per instantiation
         static bool done = false;
@@ -2445,7 +2182,7 @@ static void launch_pipe_one(const GemmArgs& a, int splits, hipStream_t s) {
     dim3 grid((unsigned)units, (unsigned)splits);
     const bool kt32 = (a.K % 32) != 0 || (a.k_split % 32) != 0;
     // paired K = 64 stages: every K range a multiple of 64
-    const bool pair = BM == 256 && pair_enabled() && a.K % 64 == 0 && a.k_split % 64 == 0 &&
+    const bool pair = BM == 256 && a.K % 64 == 0 && a.k_split % 64 == 0 &&
                       (a.tail_split <= 1 || a.tail_k % 64 == 0);
     if constexpr (BM == 256) {
         if (pair) {
@@ -2461,58 +2198,37 @@ static void launch_pipe_one(const GemmArgs& a, int splits, hipStream_t s) {
     launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
 }
 
-template <int BM, int BN, int WM, int WN>
-static void launch_pipe_epi(int epi, const GemmArgs& a, int splits, hipStream_t s) {
+enum Launcher { L_PIPE = 0, L_DL = 1, L_REG = 2 };
+
+template <int L, int BM, int BN, int WM, int WN, int EPI>
+static void launch_one(const GemmArgs& a, int splits, hipStream_t s) {
+    if constexpr (L == L_PIPE) launch_pipe_one<BM, BN, WM, WN, EPI>(a, splits, s);
+    else if constexpr (L == L_DL) launch_dl_one<BM, BN, WM, WN, EPI>(a, splits, s);
+    else launch_reg_one<BM, BN, WM, WN, EPI>(a, splits, s);
+}
+
+template <int L, int BM, int BN, int WM, int WN>
+static void launch_epi(int epi, const GemmArgs& a, int splits, hipStream_t s) {
     switch (epi) {
-        case EPI_STORE_BF16: launch_pipe_one<BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, s); break;
-        case EPI_STORE_F32: launch_pipe_one<BM, BN, WM, WN, EPI_STORE_F32>(a, splits, s); break;
-        case EPI_GATED_BF16: launch_pipe_one<BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, s); break;
-        default: launch_pipe_one<BM, BN, WM, WN, EPI_SPLIT>(a, splits, s); break;
+        case EPI_STORE_BF16: launch_one<L, BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, s); break;
+        case EPI_STORE_F32: launch_one<L, BM, BN, WM, WN, EPI_STORE_F32>(a, splits, s); break;
+        case EPI_GATED_BF16: launch_one<L, BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, s); break;
+        default: launch_one<L, BM, BN, WM, WN, EPI_SPLIT>(a, splits, s); break;
     }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-static void launch_bf16_cfg(const GemmArgs& a, int splits, bool vec, size_t lds, hipStream_t s) {
-    if (vec)
-        launch_bf16_one<BM, BN, WM, WN, EPI, true>(a, splits, lds, s);
-    else
-        launch_bf16_one<BM, BN, WM, WN, EPI, false>(a, splits, lds, s);
-}
-
-template <int BM, int BN, int WM, int WN>
-static void launch_bf16_epi(int epi, const GemmArgs& a, int splits, bool vec, size_t lds, hipStream_t s) {
-    switch (epi) {
-        case EPI_STORE_BF16: launch_bf16_cfg<BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, vec, lds, s); break;
-        case EPI_STORE_F32: launch_bf16_cfg<BM, BN, WM, WN, EPI_STORE_F32>(a, splits, vec, lds, s); break;
-        case EPI_GATED_BF16: launch_bf16_cfg<BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, vec, lds, s); break;
-        default: launch_bf16_cfg<BM, BN, WM, WN, EPI_SPLIT>(a, splits, vec, lds, s); break;
-    }
-}
-
-static bool use_dl_kernels() {
-    static int use_dl = -1;
-    if (use_dl < 0) {
-        const char* e = getenv("TPSHARD_GEMM_DL");
-        use_dl = (e && atoi(e) == 0) ? 0 : 1;
-    }
-    return use_dl == 1;
-}
-
+// kern is the tile configuration (HUGE8 only for 16-byte-loadable operands)
 static void launch_bf16_kern(int kern, int epi, const GemmArgs& a, int splits, bool vec, hipStream_t s) {
-    const size_t lds = lds_bytes(kern);
-    const bool pipe = vec && pipe_enabled() && use_dl_kernels();
+    if (!vec) {
+        if (kern == K_BF16_DEC4 || kern == K_BF16_SMALL) launch_epi<L_REG, 64, 128, 1, 2>(epi, a, splits, s);
+        else launch_epi<L_REG, 128, 128, 2, 2>(epi, a, splits, s);
+        return;
+    }
     switch (kern) {
-        case K_BF16_HUGE8:
-            if (pipe) launch_pipe_epi<256, 256, 2, 4>(epi, a, splits, s);
-            else launch_bf16_epi<256, 256, 2, 4>(epi, a, splits, vec, lds, s);
-            break;
+        case K_BF16_HUGE8: launch_epi<L_PIPE, 256, 256, 2, 4>(epi, a, splits, s); break;
         case K_BF16_DEC4:
-            // same tiling as SMALL, which serves operands that DMA cannot load
-            if (pipe) launch_pipe_epi<64, 128, 1, 4>(epi, a, splits, s);
-            else launch_bf16_epi<64, 128, 1, 2>(epi, a, splits, vec, lds_bytes(K_BF16_SMALL), s);
-            break;
-        case K_BF16_SMALL: launch_bf16_epi<64, 128, 1, 2>(epi, a, splits, vec, lds, s); break;
-        default: launch_bf16_epi<128, 128, 2, 2>(epi, a, splits, vec, lds, s); break;
+        case K_BF16_SMALL: launch_epi<L_PIPE, 64, 128, 1, 4>(epi, a, splits, s); break;
+        default: launch_epi<L_DL, 128, 128, 2, 2>(epi, a, splits, s); break;
     }
 }
 
@@ -2635,15 +2351,6 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
             hipLaunchKernelGGL(stream_finalize_kernel<EPI_STORE_BF16>, fgrid, dim3(256), 0, s, o, a, kStreamWGs);
         return hipGetLastError();
     }
-    if (pl.kernel == K_BF16_DECODE && !vec) {
-        // unaligned operands: the element-wise tiled kernel, without split-K
-        GemmPlan alt = pl;
-        alt.kernel = K_BF16_SMALL;
-        alt.splits = 1;
-        alt.k_split = K;
-        alt.ws_bytes = 0;
-        return launch_gemm(alt, A, B, bias, C, M, N, K, gated, dt, out_dt, ws, s);
-    }
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(A);
     a.B = static_cast<const uint16_t*>(B);
@@ -2680,28 +2387,11 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
                                wsf, pl.splits, M, N, Nb, bb, C);
         return hipGetLastError();
     }
-    if (pl.kernel == K_BF16_DECODE) {
-        a.C = C;
-        const unsigned wgs = (unsigned)ceil_div(N, 16);
-        if (K % 64 == 0) {
-            if (gated)
-                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_GATED_BF16, 8, false>), dim3(wgs), dim3(512), 0, s, a);
-            else if (out_dt == TP_F32)
-                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_F32, 8, false>), dim3(wgs), dim3(512), 0, s, a);
-            else
-                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_BF16, 8, false>), dim3(wgs), dim3(512), 0, s, a);
-        } else {
-            if (gated)
-                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_GATED_BF16, 8, true>), dim3(wgs), dim3(512), 0, s, a);
-            else if (out_dt == TP_F32)
-                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_F32, 8, true>), dim3(wgs), dim3(512), 0, s, a);
-            else
-                hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI_STORE_BF16, 8, true>), dim3(wgs), dim3(512), 0, s, a);
-        }
-        return hipGetLastError();
-    }
+    // operands the 16-byte loads cannot serve take the element-wise kernel,
+    // 128 x 128 tiles in place of the 256 x 256 ones
+    const int kern = (!vec && pl.kernel == K_BF16_HUGE8) ? K_BF16_LARGE : pl.kernel;
     int tm, tn;
-    tiles_for(pl.kernel, M, N, gated, tm, tn);
+    tiles_for(kern, M, N, gated, tm, tn);
     a.tiles_m = tm;
     a.tiles_n = tn;
     a.C = C;
@@ -2713,7 +2403,7 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
     }
     a.vec_out = (N % 4) == 0 && (((uintptr_t)C) & 15u) == 0;
     const int epi = gated ? EPI_GATED_BF16 : (out_dt == TP_F32 ? EPI_STORE_F32 : EPI_STORE_BF16);
-    launch_bf16_kern(pl.kernel, epi, a, 1, vec, s);
+    launch_bf16_kern(kern, epi, a, 1, vec, s);
     return hipGetLastError();
 }
 

@@ -264,15 +264,6 @@ __global__ __launch_bounds__(256) void ring_reduce_scalar_kernel(PartPtrs parts,
     }
 }
 
-// TPSHARD_REDUCE_FIXED=0 keeps every t on the generic kernel (A/B timing).
-static bool fixed_enabled() {
-    static const bool on = [] {
-        const char* e = getenv("TPSHARD_REDUCE_FIXED");
-        return !(e && e[0] == '0');
-    }();
-    return on;
-}
-
 template <typename InT, typename OutT>
 static hipError_t launch_typed(const void* const* p, int t, int64_t K, void* out, int ro, hipStream_t s) {
     PartPtrs pp = {};
@@ -282,7 +273,7 @@ static hipError_t launch_typed(const void* const* p, int t, int64_t K, void* out
         g |= (uint64_t)(uintptr_t)p[r];
     }
     const int64_t chunk = ceil_div(K, t);
-    const bool fixed = (g & 15u) == 0 && fixed_enabled() && (t == 2 || t == 4 || t == 8 || t == 16);
+    const bool fixed = (g & 15u) == 0 && (t == 2 || t == 4 || t == 8 || t == 16);
     // fixed-t kernel: one 16-byte vector per lane (measured best: many short
     // workgroups); generic kernel: ~8 vectors per lane per workgroup pass.
     // At least one workgroup per chunk either way.

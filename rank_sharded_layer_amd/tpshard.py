@@ -129,11 +129,35 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _workspace(nbytes: int, device, workspace):
+def _torch_stream(stream):
+    """The torch stream object for a caller's `stream` (None: the current one)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _empty(shape, dtype, device, stream):
+    """torch.empty allocated on the stream the kernels will run on.  torch's
+    caching allocator ties a block to the stream current at allocation time
+    and reuses it for later allocations on that stream once freed; a block
+    made on another stream could be handed out again while this call's
+    kernels still use it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    s = _torch_stream(stream)
+    if s == torch.cuda.current_stream():
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(s):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(nbytes: int, device, workspace, stream=None):
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace = _empty(nbytes, torch.uint8, device, stream)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise TPError(6, f"workspace of {nbytes} bytes needed")
     return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
@@ -155,7 +179,7 @@ def tp_shard_weights(full, dim, tp_rank, tp_size, out=None, stream=None):
     rows, cols = full.shape
     shape = (rows // max(tp_size, 1), cols) if dim == 0 else (rows, cols // max(tp_size, 1))
     if out is None:
-        out = torch.empty(shape, dtype=full.dtype, device=full.device)
+        out = _empty(shape, full.dtype, full.device, stream)
     p_full = _dev(full, "full")
     p_out = _dev(out, "out", full.dtype, shape)
     _check(lib().tp_shard_weights(p_full, rows, cols, _dt(full.dtype), dim, tp_rank, tp_size,
@@ -167,7 +191,7 @@ def tp_shard_gate_up(gate, up, tp_rank, tp_size, out=None, stream=None):
     f, h = gate.shape
     shape = (2 * (f // max(tp_size, 1)), h)
     if out is None:
-        out = torch.empty(shape, dtype=gate.dtype, device=gate.device)
+        out = _empty(shape, gate.dtype, gate.device, stream)
     pg = _dev(gate, "gate")
     pu = _dev(up, "up", gate.dtype, gate.shape)
     po = _dev(out, "out", gate.dtype, shape)
@@ -196,18 +220,18 @@ def tp_load_staging_bytes(rows, cols, src_dtype, dst_dtype) -> int:
     return b.value
 
 
-def _staging(rows, cols, src_dtype, out, staging):
-    return _workspace(tp_load_staging_bytes(rows, cols, src_dtype, out.dtype), out.device, staging)
+def _staging(rows, cols, src_dtype, out, staging, stream):
+    return _workspace(tp_load_staging_bytes(rows, cols, src_dtype, out.dtype), out.device, staging, stream)
 
 
 def tp_load_shard(src, dim, tp_rank, tp_size, dtype=torch.bfloat16, out=None, staging=None, stream=None):
     rows, cols = src.shape
     shape = (rows // max(tp_size, 1), cols) if dim == 0 else (rows, cols // max(tp_size, 1))
     if out is None:
-        out = torch.empty(shape, dtype=dtype, device="cuda")
+        out = _empty(shape, dtype, "cuda", stream)
     ps = _host(src, "src")
     po = _dev(out, "out", None, shape)
-    pw, nw = _staging(shape[0], shape[1], src.dtype, out, staging)
+    pw, nw = _staging(shape[0], shape[1], src.dtype, out, staging, stream)
     _check(lib().tp_load_shard(ps, _dt(src.dtype), rows, cols, dim, tp_rank, tp_size, po, _dt(out.dtype), pw, nw,
                                _stream(stream)))
     return out
@@ -217,7 +241,7 @@ def tp_load_gate_up(src, shard_id, tp_rank, tp_size, out, staging=None, stream=N
     f, h = src.shape
     ps = _host(src, "src")
     po = _dev(out, "out", None, (2 * (f // max(tp_size, 1)), h))
-    pw, nw = _staging(f // max(tp_size, 1), h, src.dtype, out, staging)
+    pw, nw = _staging(f // max(tp_size, 1), h, src.dtype, out, staging, stream)
     _check(lib().tp_load_gate_up(ps, _dt(src.dtype), shard_id, f, h, tp_rank, tp_size, po, _dt(out.dtype), pw, nw,
                                  _stream(stream)))
     return out
@@ -230,7 +254,7 @@ def tp_load_qkv(src, shard_id, n_q, n_kv, head_dim, tp_rank, tp_size, out, stagi
     ps = _host(src, "src")
     po = _dev(out, "out", None, ((nq_r + 2 * kvc) * head_dim, h))
     rows = (nq_r if shard_id == 0 else kvc) * head_dim
-    pw, nw = _staging(rows, h, src.dtype, out, staging)
+    pw, nw = _staging(rows, h, src.dtype, out, staging, stream)
     _check(lib().tp_load_qkv(ps, _dt(src.dtype), shard_id, n_q, n_kv, head_dim, h, tp_rank, tp_size, po,
                              _dt(out.dtype), pw, nw, _stream(stream)))
     return out
@@ -249,7 +273,7 @@ def tp_shard_qkv(wq, wk, wv, n_q, n_kv, head_dim, tp_rank, tp_size, out=None, st
     _, kvc = tp_kv_heads_for_rank(n_kv, tp_rank, tp_size)
     shape = ((n_q // tp_size + 2 * kvc) * head_dim, h)
     if out is None:
-        out = torch.empty(shape, dtype=wq.dtype, device=wq.device)
+        out = _empty(shape, wq.dtype, wq.device, stream)
     pq = _dev(wq, "wq")
     pk = _dev(wk, "wk", wq.dtype, (n_kv * head_dim, h))
     pv = _dev(wv, "wv", wq.dtype, (n_kv * head_dim, h))
@@ -273,9 +297,9 @@ def tp_gate_up_act_rank(x, w_gate_up, act=None, workspace=None, stream=None):
     px = _dev(x, "x")
     pw = _dev(w_gate_up, "w_gate_up", x.dtype, (2 * f_local, h))
     if act is None:
-        act = torch.empty((n, f_local), dtype=x.dtype, device=x.device)
+        act = _empty((n, f_local), x.dtype, x.device, stream)
     pa = _dev(act, "act", x.dtype, (n, f_local))
-    pws, nws = _workspace(tp_gate_up_workspace_bytes(n, h, f_local, x.dtype), x.device, workspace)
+    pws, nws = _workspace(tp_gate_up_workspace_bytes(n, h, f_local, x.dtype), x.device, workspace, stream)
     _check(lib().tp_gate_up_act_rank(px, n, h, pw, f_local, _dt(x.dtype), pa, pws, nws,
                                      _stream(stream)))
     return act
@@ -295,9 +319,9 @@ def tp_linear_rank_forward(x, w, bias=None, out_dtype=None, y=None, workspace=No
     pw = _dev(w, "w", x.dtype, (m, k))
     pb = _dev(bias, "bias", x.dtype, (m,)) if bias is not None else None
     if y is None:
-        y = torch.empty((n, m), dtype=out_dtype, device=x.device)
+        y = _empty((n, m), out_dtype, x.device, stream)
     py = _dev(y, "y", out_dtype, (n, m))
-    pws, nws = _workspace(tp_linear_workspace_bytes(n, k, m, x.dtype), x.device, workspace)
+    pws, nws = _workspace(tp_linear_workspace_bytes(n, k, m, x.dtype), x.device, workspace, stream)
     _check(lib().tp_linear_rank_forward(px, n, k, pw, m, pb, _dt(x.dtype), py, _dt(out_dtype),
                                         pws, nws, _stream(stream)))
     return y
@@ -318,11 +342,11 @@ def tp_mlp_rank_forward(x, w_gate_up, w_down, out_dtype=None, partial=None, work
     pgu = _dev(w_gate_up, "w_gate_up", x.dtype, (2 * f_local, h))
     pd = _dev(w_down, "w_down", x.dtype, (h, f_local))
     if partial is None:
-        partial = torch.empty((n, h), dtype=out_dtype, device=x.device)
+        partial = _empty((n, h), out_dtype, x.device, stream)
     pp = _dev(partial, "partial", out_dtype, (n, h))
     need = tp_mlp_workspace_bytes(n, h, f_local, x.dtype)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _empty(need, torch.uint8, x.device, stream)
     pws = _dev(workspace, "workspace")
     nws = workspace.numel() * workspace.element_size()
     _check(lib().tp_mlp_rank_forward(px, n, h, pgu, pd, f_local, _dt(x.dtype), pp, _dt(out_dtype),
@@ -341,7 +365,7 @@ def tp_partial_reduce(partials, out=None, out_dtype=None, order=TP_ORDER_RING, s
     ptrs = (ctypes.c_void_p * t)(*[_dev(p, f"partials[{i}]", p0.dtype, p0.shape).value
                                    for i, p in enumerate(partials)])
     if out is None:
-        out = torch.empty(p0.shape, dtype=out_dtype, device=p0.device)
+        out = _empty(p0.shape, out_dtype, p0.device, stream)
     po = _dev(out, "out", out_dtype, p0.shape)
     _check(lib().tp_partial_reduce(ptrs, t, p0.numel(), _dt(p0.dtype), po, _dt(out_dtype), order,
                                    _stream(stream)))
@@ -370,9 +394,9 @@ def tp_attention_rank(qkv, nq, nkv, head_dim=128, causal=True, out=None, workspa
     n = qkv.shape[0]
     pq = _dev(qkv, "qkv", torch.bfloat16, (n, (nq + 2 * nkv) * head_dim))
     if out is None:
-        out = torch.empty((n, nq * head_dim), dtype=torch.bfloat16, device=qkv.device)
+        out = _empty((n, nq * head_dim), torch.bfloat16, qkv.device, stream)
     po = _dev(out, "out", torch.bfloat16, (n, nq * head_dim))
-    ws, wsb = _workspace(tp_attention_workspace_bytes(n, nq, nkv, head_dim, causal), qkv.device, workspace)
+    ws, wsb = _workspace(tp_attention_workspace_bytes(n, nq, nkv, head_dim, causal), qkv.device, workspace, stream)
     _check(lib().tp_attention_rank(pq, n, nq, nkv, head_dim, _dt(torch.bfloat16), 1 if causal else 0, po, ws, wsb,
                                    _stream(stream)))
     return out
@@ -393,10 +417,10 @@ def tp_logits_gather_argmax(shards, vocab, full=None, argmax=None, want_full=Tru
         ptrs.append(_dev(sh, f"shards[{r}]", torch.float32, (n, e - s)).value if e > s else None)
     arr = (ctypes.c_void_p * t)(*ptrs)
     if want_full and full is None:
-        full = torch.empty((n, vocab), dtype=torch.float32, device=dev)
+        full = _empty((n, vocab), torch.float32, dev, stream)
     pf = _dev(full, "full", torch.float32, (n, vocab)) if full is not None else None
     if argmax is None:
-        argmax = torch.empty((n,), dtype=torch.int64, device=dev)
+        argmax = _empty((n,), torch.int64, dev, stream)
     pa = _dev(argmax, "argmax", torch.int64, (n,))
     _check(lib().tp_logits_gather_argmax(arr, t, n, vocab, _dt(torch.float32), pf, pa, _stream(stream)))
     return full, argmax
@@ -426,9 +450,9 @@ def tp_rs_add_rmsnorm(partials, tp_rank, residual, weight, eps, residual_out=Non
     pr = _dev(residual, "residual", p0.dtype, rows)
     pw = _dev(weight, "weight", p0.dtype, (h,))
     if residual_out is None:
-        residual_out = torch.empty(rows, dtype=p0.dtype, device=p0.device)
+        residual_out = _empty(rows, p0.dtype, p0.device, stream)
     if out is None:
-        out = torch.empty(rows, dtype=p0.dtype, device=p0.device)
+        out = _empty(rows, p0.dtype, p0.device, stream)
     pro = _dev(residual_out, "residual_out", p0.dtype, rows)
     po = _dev(out, "out", p0.dtype, rows)
     _check(lib().tp_rs_add_rmsnorm(ptrs, t, tp_rank, n, h, _dt(p0.dtype), pr, pw, float(eps), pro, po,
@@ -451,7 +475,7 @@ def tp_vocab_embed_rank(ids, table_shard, vocab, tp_rank, tp_size, out=None, str
     pi = _dev(ids, "ids", torch.int64)
     pt = _dev(table_shard, "table_shard", None, (e - s, h))
     if out is None:
-        out = torch.empty((n, h), dtype=table_shard.dtype, device=ids.device)
+        out = _empty((n, h), table_shard.dtype, ids.device, stream)
     po = _dev(out, "out", table_shard.dtype, (n, h))
     _check(lib().tp_vocab_embed_rank(pi, n, pt, vocab, h, tp_rank, tp_size, _dt(table_shard.dtype),
                                      po, _stream(stream)))
@@ -464,9 +488,9 @@ def tp_lm_head_rank(x, table_shard, out_dtype=torch.float32, logits=None, worksp
     px = _dev(x, "x")
     pt = _dev(table_shard, "table_shard", x.dtype, (v_local, h))
     if logits is None:
-        logits = torch.empty((n, v_local), dtype=out_dtype, device=x.device)
+        logits = _empty((n, v_local), out_dtype, x.device, stream)
     pl = _dev(logits, "logits", out_dtype, (n, v_local))
-    pws, nws = _workspace(tp_linear_workspace_bytes(n, h, v_local, x.dtype), x.device, workspace)
+    pws, nws = _workspace(tp_linear_workspace_bytes(n, h, v_local, x.dtype), x.device, workspace, stream)
     _check(lib().tp_lm_head_rank(px, n, h, pt, v_local, _dt(x.dtype), pl, _dt(out_dtype), pws, nws,
                                  _stream(stream)))
     return logits

@@ -142,11 +142,66 @@ def test_gemm_errors():
     assert st == 6
     st, _ = _status(L.tp_mlp_rank_forward, DUMMY, 4, 8, DUMMY, DUMMY, 6, 1, DUMMY, 1, NULL, 0, NULL)
     assert st == 6
-    st, _ = _status(L.tp_mlp_rank_forward, DUMMY, 4, 8, DUMMY, DUMMY, 6, 1, DUMMY, 1,
-                    ctypes.c_void_p(0x1001), 1 << 20, NULL)
-    assert st == 1                    # misaligned workspace
+    st, msg = _status(L.tp_mlp_rank_forward, DUMMY, 4, 8, DUMMY, DUMMY, 6, 1, DUMMY, 1,
+                      ctypes.c_void_p(0x1001), 1 << 20, NULL)
+    assert st == 4 and "aligned" in msg   # TP_EALIGN: workspace not 256-byte aligned
+    st, msg = _status(L.tp_linear_rank_forward, DUMMY, 64, 7167, DUMMY, 8192, NULL, 1, DUMMY, 1,
+                      ctypes.c_void_p(0x1008), 1 << 30, NULL)
+    assert st == 4 and "16-byte" in msg   # split-K workspace not 16-byte aligned
     st, _ = _status(L.tp_lm_head_rank, DUMMY, 4, 8, NULL, 16, 1, DUMMY, 0, NULL, 0, NULL)
     assert st == 1
+
+
+@no_gpu
+def test_gemm_32bit_offset_guard():
+    """The bf16 kernels address a tile's operand rows with 32-bit byte
+    offsets: K beyond 2^22, or a fused gate_up table whose up rows lie 2 GiB
+    or more past its gate rows, is rejected with TP_ESHAPE before any launch
+    (the fp32 kernels index with 64 bits and take these shapes)."""
+    L = T.lib()
+    sz = ctypes.c_size_t()
+    big_k = 1 << 22
+    st, msg = _status(L.tp_linear_rank_forward, DUMMY, 4, big_k, DUMMY, 16, NULL, 1, DUMMY, 1, NULL, 0, NULL)
+    assert st == 2 and "reduction size" in msg
+    assert L.tp_linear_workspace_bytes(4, big_k, 16, 1, ctypes.byref(sz)) == 2
+    assert L.tp_linear_workspace_bytes(4, big_k - 8, 16, 1, ctypes.byref(sz)) == 0
+    assert L.tp_linear_workspace_bytes(4, big_k, 16, 0, ctypes.byref(sz)) == 0      # fp32: no limit
+    st, _ = _status(L.tp_lm_head_rank, DUMMY, 4, big_k, DUMMY, 16, 1, DUMMY, 1, NULL, 0, NULL)
+    assert st == 2
+    # gated: (f_local + 256) * h * 2 must stay under 2^31
+    h = 8192
+    f_ok = (1 << 31) // (2 * h) - 257
+    f_bad = f_ok + 1
+    assert L.tp_gate_up_workspace_bytes(64, h, f_ok, 1, ctypes.byref(sz)) == 0
+    assert L.tp_gate_up_workspace_bytes(64, h, f_bad, 1, ctypes.byref(sz)) == 2
+    st, msg = _status(L.tp_gate_up_act_rank, DUMMY, 64, h, DUMMY, f_bad, 1, DUMMY, NULL, 0, NULL)
+    assert st == 2 and "gate_up" in msg
+    st, _ = _status(L.tp_mlp_rank_forward, DUMMY, 64, h, DUMMY, DUMMY, f_bad, 1, DUMMY, 1, NULL, 0, NULL)
+    assert st == 2
+    assert L.tp_mlp_workspace_bytes(64, h, f_bad, 1, ctypes.byref(sz)) == 2
+    # a 405B-shaped MLP (h 16384, f 53248) fits even unsharded: its up rows
+    # start 1.74 GB after its gate rows
+    assert L.tp_mlp_workspace_bytes(64, 16384, 53248, 1, ctypes.byref(sz)) == 0
+    assert L.tp_mlp_workspace_bytes(64, 16384, 65536, 1, ctypes.byref(sz)) == 2
+
+
+@no_gpu
+def test_attention_alignment_errors():
+    """Every alignment rejection returns TP_EALIGN: qkv / out and the
+    workspace of the attention core must be 16-byte aligned."""
+    L = T.lib()
+    sz = ctypes.c_size_t()
+    assert L.tp_attention_workspace_bytes(8192, 4, 1, 128, 1, 1, ctypes.byref(sz)) == 0 and sz.value > 0
+    ws = ctypes.c_void_p(0x40000000)
+    st, msg = _status(L.tp_attention_rank, ctypes.c_void_p(0x1008), 8192, 4, 1, 128, 1, 1, ctypes.c_void_p(1 << 36),
+                      ws, sz.value, NULL)
+    assert st == 4 and "aligned" in msg
+    st, msg = _status(L.tp_attention_rank, ctypes.c_void_p(1 << 34), 8192, 4, 1, 128, 1, 1, ctypes.c_void_p(1 << 36),
+                      ctypes.c_void_p(0x40000004), sz.value, NULL)
+    assert st == 4 and "workspace" in msg
+    st, _ = _status(L.tp_attention_rank, ctypes.c_void_p(1 << 34), 8192, 4, 1, 128, 1, 1, ctypes.c_void_p(1 << 36),
+                    ws, sz.value - 16, NULL)
+    assert st == 6
 
 
 @no_gpu

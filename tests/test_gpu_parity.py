@@ -898,3 +898,43 @@ def test_load_qkv_and_gate_up_tables(n_q, n_kv, t):
         T.tp_load_gate_up(gate, 0, r, t, out=gu)
         torch.cuda.synchronize()
         assert torch.equal(gu.view(torch.int16), T.tp_shard_gate_up(dev[3], dev[4], r, t).view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# binding: buffers it allocates live on the caller's stream
+# --------------------------------------------------------------------------
+
+def test_mlp_on_side_stream_while_current_stream_reuses_memory():
+    """tp_mlp_rank_forward queued on a side stream behind a delay, with the
+    binding allocating (and dropping) the workspace; meanwhile the current
+    stream keeps allocating blocks of the workspace's size and filling them
+    with NaN.  Were the workspace allocated on the current stream, torch's
+    caching allocator would hand its block to those fills while the side
+    stream's kernels still read the activation and split-K partials from
+    it.  The result must equal the oracle's and the same call made on the
+    current stream."""
+    n, h, fl = 64, 4096, 2048
+    x = rnd((n, h), 1.0, 300, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.02, 301, torch.bfloat16)
+    wd = rnd((h, fl), 0.02, 302, torch.bfloat16)
+    ref_same = T.tp_mlp_rank_forward(x, wgu, wd)
+    need = T.tp_mlp_workspace_bytes(n, h, fl, torch.bfloat16)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(2_000_000)              # the MLP starts after the fills below begin
+            out = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
+        T.tp_mlp_rank_forward(x, wgu, wd, partial=out, stream=side)
+        for _ in range(64):                           # the current stream's traffic meanwhile
+            junk = torch.empty(need, dtype=torch.uint8, device=DEV)
+            junk.fill_(0xFF)                          # bf16/fp32 NaN patterns
+            torch.cuda._sleep(20_000)
+            del junk
+        outs.append(out)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_rank(to_f64(x), to_f64(wgu[:fl]), to_f64(wgu[fl:]), to_f64(wd), 0, 1)
+    for out in outs:
+        assert torch.equal(out, ref_same)
+        assert relf(to_f64(out), ref) <= TOL[torch.bfloat16]
