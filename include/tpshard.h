@@ -55,6 +55,9 @@ extern "C" {
 
 #define TP_ABI_VERSION 1
 #define TP_MAX_RANKS 64
+/* Device scratch of tp_mlp_rank_forward_noalloc, held by each GPU the
+ * library runs on until the process ends. */
+#define TP_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef enum {
     TP_OK = 0,
@@ -225,6 +228,25 @@ TP_API tp_status tp_mlp_rank_forward(const void* x, int64_t n, int64_t h, const 
                               const void* w_down, int64_t f_local, tp_dtype dt,
                               void* partial, tp_dtype out_dt,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* tp_mlp_rank_forward for callers that cannot allocate device memory: code
+ * under HIP stream capture, serving loops and harnesses that forbid
+ * allocation.  Same arguments, kernels and results as tp_mlp_rank_forward,
+ * without the workspace: the activation and split-K partials live in a
+ * library-owned device array of TP_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU,
+ * so the call allocates nothing.
+ *   Limit: shapes whose tp_mlp_workspace_bytes exceeds 64 MiB return
+ *   TP_EWORKSPACE (for example the Llama-3.1-70B decode share, 64 tokens at
+ *   TP=4, needs about 16 MB; its 8192-token prefill share at TP=8 needs
+ *   about 123 MB and must use tp_mlp_rank_forward).
+ *   Every call on one GPU uses that GPU's single array: calls that overlap
+ *   in time on one GPU (other streams, other host threads) race and must be
+ *   serialised by the caller.  Nothing in the array needs clearing between
+ *   calls: each call writes every byte it reads.
+ *   The stream must belong to the current device. */
+TP_API tp_status tp_mlp_rank_forward_noalloc(const void* x, int64_t n, int64_t h, const void* w_gate_up,
+                                             const void* w_down, int64_t f_local, tp_dtype dt,
+                                             void* partial, tp_dtype out_dt, void* stream);
 
 /* ---- sum of the t partials (the all-reduce's arithmetic, one device) ----- */
 

@@ -6,7 +6,17 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
+
+// Scratch of tp_mlp_rank_forward_noalloc: device memory the library owns, so
+// that callers which cannot allocate (code under stream capture, serving
+// loops that forbid allocation) can run the MLP share.  Each GPU the library
+// runs on holds its own copy of this array until the process ends.  In host
+// code this name is only a stand-in for the device symbol: kernels get the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[TP_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -102,6 +112,43 @@ tp_status check_ws(size_t need, void* workspace, size_t workspace_bytes, size_t 
                     workspace ? workspace_bytes : (size_t)0);
     if (((uintptr_t)workspace) & (align - 1))
         return fail(TP_EALIGN, "%s: workspace not %zu-byte aligned", fn, align);
+    return TP_OK;
+}
+
+// The two launches of the MLP share on workspace ws (act, then the split-K
+// area), laid out as L says.
+hipError_t mlp_launch(const MlpLayout& L, const void* x, int64_t n, int64_t h, const void* w_gate_up,
+                      const void* w_down, int64_t f_local, tp_dtype dt, void* partial, tp_dtype out_dt, void* ws,
+                      hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    void* act = base;
+    void* split = base + L.act_bytes;
+    hipError_t e = tpk::launch_gemm(L.gu, x, w_gate_up, nullptr, act, n, f_local, h, true, dt, dt, split, s);
+    if (e == hipSuccess) e = tpk::launch_gemm(L.down, act, w_down, nullptr, partial, n, h, f_local, false, dt, out_dt, split, s);
+    return e;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+tp_status scratch_of_current_device(void** out, const char* fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TP_EHIP, "%s: hipGetDevice: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(TP_EINVAL, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(TP_EHIP, "%s: hipGetSymbolAddress(scratch): HIP error %d (%s)", fn, (int)e,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return TP_OK;
 }
 
@@ -393,13 +440,30 @@ tp_status tp_mlp_rank_forward(const void* x, int64_t n, int64_t h, const void* w
     if (tp_status st = check_bf16_offsets(f_local, 0, false, dt, "tp_mlp_rank_forward")) return st;
     MlpLayout L = mlp_layout(n, h, f_local, dt);
     if (tp_status st = check_ws(L.total, workspace, workspace_bytes, 256, "tp_mlp_rank_forward")) return st;
-    char* ws = static_cast<char*>(workspace);
-    void* act = ws;
-    void* split = ws + L.act_bytes;
-    hipStream_t s = as_stream(stream);
-    hipError_t e = tpk::launch_gemm(L.gu, x, w_gate_up, nullptr, act, n, f_local, h, true, dt, dt, split, s);
-    if (e == hipSuccess) e = tpk::launch_gemm(L.down, act, w_down, nullptr, partial, n, h, f_local, false, dt, out_dt, split, s);
-    return hip_status(e, "tp_mlp_rank_forward");
+    return hip_status(mlp_launch(L, x, n, h, w_gate_up, w_down, f_local, dt, partial, out_dt, workspace,
+                                 as_stream(stream)),
+                      "tp_mlp_rank_forward");
+}
+
+tp_status tp_mlp_rank_forward_noalloc(const void* x, int64_t n, int64_t h, const void* w_gate_up,
+                                      const void* w_down, int64_t f_local, tp_dtype dt, void* partial,
+                                      tp_dtype out_dt, void* stream) {
+    const char* fn = "tp_mlp_rank_forward_noalloc";
+    if (!x || !w_gate_up || !w_down || !partial) return fail(TP_EINVAL, "%s: null pointer", fn);
+    if (!valid_dt(dt) || !valid_dt(out_dt) || !valid_pair(dt, out_dt))
+        return fail(TP_EDTYPE, "%s: unsupported dtype pair (%d -> %d)", fn, (int)dt, (int)out_dt);
+    if (tp_status st = check_gemm_dims(n, h, 2 * f_local, fn)) return st;
+    if (tp_status st = check_bf16_offsets(h, f_local, true, dt, fn)) return st;
+    if (tp_status st = check_bf16_offsets(f_local, 0, false, dt, fn)) return st;
+    MlpLayout L = mlp_layout(n, h, f_local, dt);
+    if (L.total > (size_t)TP_NOALLOC_SCRATCH_BYTES)
+        return fail(TP_EWORKSPACE, "%s: this shape needs %zu bytes of scratch, more than the library's %zu "
+                    "(use tp_mlp_rank_forward with a caller workspace)", fn, L.total,
+                    (size_t)TP_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (tp_status st = scratch_of_current_device(&ws, fn)) return st;
+    return hip_status(mlp_launch(L, x, n, h, w_gate_up, w_down, f_local, dt, partial, out_dt, ws, as_stream(stream)),
+                      fn);
 }
 
 // ---- reduce -------------------------------------------------------------------

@@ -59,6 +59,7 @@ _SIGS = {
     "tp_linear_rank_forward": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp, _int, _vp, _sz, _vp]),
     "tp_mlp_workspace_bytes": (_int, [_i64, _i64, _i64, _int, _szp]),
     "tp_mlp_rank_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _sz, _vp]),
+    "tp_mlp_rank_forward_noalloc": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp]),
     "tp_partial_reduce": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _vp, _int, _int, _vp]),
     "tp_ring_schedule": (_int, [_int, _i64, ctypes.POINTER(RingStep), _int, ctypes.POINTER(_int)]),
     "tp_sp_rows": (_int, [_i64, _int, _int, _i64p, _i64p]),
