@@ -64,10 +64,48 @@ class EventTimer:
         ev.record()
         self.pairs[name][-1][1] = ev
 
+    def all_ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs[name]]
+
     def ms(self, name):
-        """Average milliseconds per region."""
-        p = self.pairs[name]
-        return sum(a.elapsed_time(b) for a, b in p) / len(p)
+        """Median milliseconds per region."""
+        return median(self.all_ms(name))
+
+    def stats(self, name):
+        return stats(self.all_ms(name))
+
+
+def median(v):
+    s = sorted(v)
+    m = len(s) // 2
+    return s[m] if len(s) % 2 else 0.5 * (s[m - 1] + s[m])
+
+
+def stats(v):
+    """median / min / max (ms) of repeated measurements"""
+    return {"median": round(median(v), 5), "min": round(min(v), 5), "max": round(max(v), 5), "n": len(v)}
+
+
+def batched_ms(fn, n_calls, n_batches=7, prime=3):
+    """Per-call milliseconds of `fn(i)` over n_batches batches of n_calls
+    back-to-back calls, each batch between one event pair (the GPU never
+    waits for the host inside a batch).  Returns the per-batch averages."""
+    for i in range(prime):
+        fn(i)
+    torch.cuda.synchronize()
+    out = []
+    k = 0
+    for _ in range(n_batches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_calls):
+            fn(k)
+            k += 1
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / n_calls)
+    return out
 
 
 def gen(w, tid, shape, std):
@@ -157,28 +195,18 @@ def leg_decode(reps):
                          T.tp_gate_up_workspace_bytes(w.n, w.h, fl, w.dtype),
                          T.tp_linear_workspace_bytes(w.n, fl, w.h, w.dtype), 256),
                      dtype=torch.uint8, device=DEV)
-    parts = [gen(w, synth.T_PARTIAL + q, (w.n, w.h), 1.0) for q in range(w.tp)]
+    # the 4 ranks' 1 MiB partials, 64 sets (320 MB) rotated for the cold figure
+    psets = [[gen(w, synth.T_PARTIAL + q, (w.n, w.h), 1.0) for q in range(w.tp)]]
+    psets += [[p.clone() for p in psets[0]] for _ in range(63)]
     y = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
 
-    # Each figure is the average over a batch of back-to-back calls between
-    # one pair of events, so that the GPU never waits for the host between
-    # calls; weights rotate over the three copies (cold in the MALL).
-    def batch(fn, n_calls):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n_calls):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n_calls
-
+    # cold: weights rotate over the three copies; warm: one copy over and over
     def mlp(i):
         wgu, wd = copies[i % 3]
         T.tp_mlp_rank_forward(x, wgu, wd, partial=part, workspace=ws)
+
+    def mlp_warm(i):
+        T.tp_mlp_rank_forward(x, copies[0][0], copies[0][1], partial=part, workspace=ws)
 
     def gate_up(i):
         T.tp_gate_up_act_rank(x, copies[i % 3][0], act=act, workspace=ws)
@@ -186,28 +214,42 @@ def leg_decode(reps):
     def down(i):
         T.tp_linear_rank_forward(act, copies[i % 3][1], y=part, workspace=ws)
 
-    def reduce(i):
-        T.tp_partial_reduce(parts, out=y)
+    def reduce_warm(i):
+        T.tp_partial_reduce(psets[0], out=y)
 
-    mlp_ms = batch(mlp, reps)
-    gate_up_ms = batch(gate_up, reps)
-    down_ms = batch(down, reps)
-    reduce_ms = batch(reduce, reps)
+    def reduce_cold(i):
+        T.tp_partial_reduce(psets[i % 64], out=y)
+
+    mlp_v = batched_ms(mlp, reps)
+    warm_v = batched_ms(mlp_warm, reps)
+    gate_up_v = batched_ms(gate_up, reps)
+    down_v = batched_ms(down, reps)
+    red_warm = batched_ms(reduce_warm, reps)
+    red_cold = batched_ms(reduce_cold, 64)
     torch.cuda.synchronize()
     wbytes = (2 * fl * w.h + w.h * fl) * 2
     io = (w.n * w.h + 2 * w.n * fl + w.n * w.h) * 2      # x, act write+read, partial
     red_bytes = (w.tp + 1) * w.n * w.h * 2
+    mlp_ms, warm_ms = median(mlp_v), median(warm_v)
+
     return {
         "workload": w.name, "n": w.n, "h": w.h, "f_local": fl, "tp": w.tp,
-        "mlp_ms": mlp_ms, "gate_up_ms": gate_up_ms, "down_ms": down_ms,
+        "mlp_ms": mlp_ms, "mlp_ms_stats": stats(mlp_v),
+        "gate_up_ms": median(gate_up_v), "gate_up_ms_stats": stats(gate_up_v),
+        "down_ms": median(down_v), "down_ms_stats": stats(down_v),
         "mlp_GBps": (wbytes + io) / mlp_ms / 1e6,
         "mlp_hbm_frac": (wbytes + io) / mlp_ms / 1e6 / PEAK_HBM_GBPS,
         "algorithmic_bytes": wbytes + io,
         "mlp_TFLOPs": mlp_flops(w.n, w.h, fl) / mlp_ms / 1e9,
-        "reduce_ms": reduce_ms, "reduce_GBps": red_bytes / reduce_ms / 1e6,
-        "reduce_note": "4 x 1 MiB partials: launch/MALL bound, not an HBM-roofline claim",
-        "cold": "weights rotated over 3 rank copies (1.06 GB > 256 MB MALL)",
-        "timing": "one tp_mlp_rank_forward per step; batches of back-to-back calls between one event pair",
+        "warm_mlp_ms": warm_ms, "warm_mlp_ms_stats": stats(warm_v),
+        "warm_mlp_GBps": (wbytes + io) / warm_ms / 1e6,
+        "reduce_ms": median(red_cold), "reduce_ms_stats": stats(red_cold),
+        "reduce_GBps": red_bytes / median(red_cold) / 1e6,
+        "warm_reduce_ms": median(red_warm), "warm_reduce_ms_stats": stats(red_warm),
+        "reduce_note": "4 x 1 MiB partials: launch bound, not an HBM-roofline claim; cold = 64 partial sets "
+                       "(320 MB) rotated, warm = one set",
+        "cold": "weights rotated over 3 rank copies (1.06 GB > 256 MB MALL); warm_* = one copy repeated",
+        "timing": "median (min, max) over 7 batches of back-to-back calls, each batch between one event pair",
     }
 
 
@@ -233,9 +275,11 @@ def leg_reduce(name, reps):
     ms = tm.ms("reduce")
     msr = tm.ms("rank")
     del parts
-    return {"workload": name, "t": w.tp, "K": w.n * w.h, "ms": ms, "GBps": b / ms / 1e6,
-            "hbm_frac": b / ms / 1e6 / PEAK_HBM_GBPS, "algorithmic_bytes": b,
-            "rank_order_ms": msr, "rank_order_hbm_frac": b / msr / 1e6 / PEAK_HBM_GBPS}
+    return {"workload": name, "t": w.tp, "K": w.n * w.h, "ms": ms, "ms_stats": tm.stats("reduce"),
+            "GBps": b / ms / 1e6, "hbm_frac": b / ms / 1e6 / PEAK_HBM_GBPS, "algorithmic_bytes": b,
+            "rank_order_ms": msr, "rank_order_ms_stats": tm.stats("rank"),
+            "rank_order_hbm_frac": b / msr / 1e6 / PEAK_HBM_GBPS,
+            "cold": f"working set {(b / 2**30):.2f} GiB > 1 GiB: every call streams from HBM"}
 
 
 def leg_spnorm(reps):
@@ -289,7 +333,6 @@ def leg_vocab(reps):
     outs = [torch.empty((w.n, w.h), dtype=w.dtype, device=DEV) for _ in range(w.tp)]
     xemb = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
     v_local = shards[0].shape[0]
-    logits = torch.empty((w.n, v_local), dtype=torch.float32, device=DEV)
     tm = EventTimer()
     for i in range(2 + reps):
         t_ = tm if i >= 2 else None
@@ -303,15 +346,27 @@ def leg_vocab(reps):
         T.tp_partial_reduce(outs, out=xemb)
         if t_:
             t_.stop("reduce")
-            t_.start("lm_head")
-        T.tp_lm_head_rank(xemb, shards[1], logits=logits)
-        if t_:
-            t_.stop("lm_head")
+    # LM head: 156 MB table shard + 156 MB fp32 logits per call.  Cold: three
+    # table copies and three logits buffers in rotation (936 MB, more than
+    # the 256 MB MALL); warm: one table and one logits buffer.
+    tabs = [shards[1]] + [shards[1].clone() for _ in range(2)]
+    logits = [torch.empty((w.n, v_local), dtype=torch.float32, device=DEV) for _ in range(3)]
+
+    def lm_cold(i):
+        T.tp_lm_head_rank(xemb, tabs[i % 3], logits=logits[i % 3])
+
+    def lm_warm(i):
+        T.tp_lm_head_rank(xemb, tabs[0], logits=logits[0])
+
+    cold_v = batched_ms(lm_cold, reps)
+    warm_v = batched_ms(lm_warm, reps)
+    del tabs, logits
     torch.cuda.synchronize()
     fl = 2.0 * w.n * w.h * v_local
     by = v_local * w.h * 2 + w.n * w.h * 2 + w.n * v_local * 4
-    ms = tm.ms("lm_head")
-    # gather of both ranks' logits into [n, V] and the greedy pick
+    ms = median(cold_v)
+    # gather of both ranks' logits into [n, V] and the greedy pick (622 MB
+    # moved per call with the full copy: consecutive calls stream from HBM)
     rank_logits = [T.tp_lm_head_rank(xemb, shards[r]) for r in range(w.tp)]
     full = torch.empty((w.n, w.vocab), dtype=torch.float32, device=DEV)
     am = torch.empty((w.n,), dtype=torch.int64, device=DEV)
@@ -328,13 +383,20 @@ def leg_vocab(reps):
             tg.stop("argmax")
     torch.cuda.synchronize()
     gb = w.n * w.vocab * 4
-    return {"workload": w.name, "embed_ms_all_ranks": tm.ms("embed"), "reduce_ms": tm.ms("reduce"),
-            "lm_head_ms": ms, "lm_head_TFLOPs": fl / ms / 1e9, "lm_head_GBps": by / ms / 1e6,
+    return {"workload": w.name, "embed_ms_all_ranks": tm.ms("embed"), "embed_ms_stats": tm.stats("embed"),
+            "reduce_ms": tm.ms("reduce"), "reduce_ms_stats": tm.stats("reduce"),
+            "lm_head_ms": ms, "lm_head_ms_stats": stats(cold_v),
+            "lm_head_TFLOPs": fl / ms / 1e9, "lm_head_GBps": by / ms / 1e6,
             "lm_head_hbm_frac": by / ms / 1e6 / PEAK_HBM_GBPS,
             "lm_head_mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
-            "gather_argmax_ms": tg.ms("gather"), "gather_argmax_GBps": 2 * gb / tg.ms("gather") / 1e6,
+            "warm_lm_head_ms": median(warm_v), "warm_lm_head_ms_stats": stats(warm_v),
+            "lm_head_cold": "3 table shards + 3 logits buffers rotated (936 MB); warm = one of each",
+            "embed_note": "embedding and its shard sum: 1-3 MiB per call, launch bound (warm)",
+            "gather_argmax_ms": tg.ms("gather"), "gather_argmax_ms_stats": tg.stats("gather"),
+            "gather_argmax_GBps": 2 * gb / tg.ms("gather") / 1e6,
             "gather_argmax_hbm_frac": 2 * gb / tg.ms("gather") / 1e6 / PEAK_HBM_GBPS,
-            "argmax_only_ms": tg.ms("argmax"), "argmax_only_GBps": gb / tg.ms("argmax") / 1e6,
+            "argmax_only_ms": tg.ms("argmax"), "argmax_only_ms_stats": tg.stats("argmax"),
+            "argmax_only_GBps": gb / tg.ms("argmax") / 1e6,
             "argmax_only_hbm_frac": gb / tg.ms("argmax") / 1e6 / PEAK_HBM_GBPS}
 
 
@@ -342,7 +404,6 @@ def leg_attnproj(reps):
     w = synth.get("llama70b_attnproj_tp16")
     hd, t = w.head_dim, w.tp
     r = 5
-    x = gen(w, synth.T_X, (w.n, w.h), 1.0)
     wq = gen(w, synth.T_WQ, (w.n_q * hd, w.h), 0.02)
     wk = gen(w, synth.T_WK, (w.n_kv * hd, w.h), 0.02)
     wv = gen(w, synth.T_WV, (w.n_kv * hd, w.h), 0.02)
@@ -351,38 +412,55 @@ def leg_attnproj(reps):
     wo_r = T.tp_shard_weights(wo, 1, r, t)
     del wq, wk, wv, wo
     nq_r, nkv_r = w.n_q // t, max(w.n_kv // t, 1)
+    # cold: three token inputs and three output partials in rotation (768 MiB
+    # of x and partials, more than the 256 MB MALL); warm: one of each
+    xs = [gen(w, synth.T_X, (w.n, w.h), 1.0)] + [None, None]
+    xs[1], xs[2] = xs[0].clone(), xs[0].clone()
+    parts = [torch.empty((w.n, w.h), dtype=w.dtype, device=DEV) for _ in range(3)]
     qkv = torch.empty((w.n, wqkv.shape[0]), dtype=w.dtype, device=DEV)
     a_r = torch.empty((w.n, nq_r * hd), dtype=w.dtype, device=DEV)
     aws = torch.empty(max(T.tp_attention_workspace_bytes(w.n, nq_r, nkv_r, hd, causal=True), 16),
                       dtype=torch.uint8, device=DEV)
-    part = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
-    tm = EventTimer()
-    for i in range(2 + reps):
-        t_ = tm if i >= 2 else None
-        if t_:
-            t_.start("qkv")
-        T.tp_linear_rank_forward(x, wqkv, y=qkv)
-        if t_:
-            t_.stop("qkv")
-            t_.start("attn")
-        T.tp_attention_rank(qkv, nq_r, nkv_r, head_dim=hd, causal=True, out=a_r, workspace=aws)
-        if t_:
-            t_.stop("attn")
-            t_.start("o_proj")
-        T.tp_linear_rank_forward(a_r, wo_r, y=part)
-        if t_:
-            t_.stop("o_proj")
-    torch.cuda.synchronize()
+    res = {}
+    for mode in ("cold", "warm"):
+        tm = EventTimer()
+        for i in range(2 + reps):
+            j = i % 3 if mode == "cold" else 0
+            t_ = tm if i >= 2 else None
+            if t_:
+                t_.start("qkv")
+            T.tp_linear_rank_forward(xs[j], wqkv, y=qkv)
+            if t_:
+                t_.stop("qkv")
+                t_.start("attn")
+            T.tp_attention_rank(qkv, nq_r, nkv_r, head_dim=hd, causal=True, out=a_r, workspace=aws)
+            if t_:
+                t_.stop("attn")
+                t_.start("o_proj")
+            T.tp_linear_rank_forward(a_r, wo_r, y=parts[j])
+            if t_:
+                t_.stop("o_proj")
+        torch.cuda.synchronize()
+        res[mode] = tm
+    tm = res["cold"]
     fq = 2.0 * w.n * w.h * wqkv.shape[0]
     fo = 2.0 * w.n * a_r.shape[1] * w.h
     fa = 4.0 * nq_r * hd * w.n * (w.n + 1) / 2        # causal: QK^T and PV over s <= i
-    return {"workload": w.name, "qkv_ms": tm.ms("qkv"), "qkv_TFLOPs": fq / tm.ms("qkv") / 1e9,
-            "attn_ms": tm.ms("attn"), "attn_TFLOPs": fa / tm.ms("attn") / 1e9,
-            "attn_mfma_frac": fa / tm.ms("attn") / 1e9 / PEAK_BF16_TFLOPS,
-            "o_proj_ms": tm.ms("o_proj"), "o_proj_TFLOPs": fo / tm.ms("o_proj") / 1e9,
-            "qkv_mfma_frac": fq / tm.ms("qkv") / 1e9 / PEAK_BF16_TFLOPS,
-            "o_proj_mfma_frac": fo / tm.ms("o_proj") / 1e9 / PEAK_BF16_TFLOPS,
-            "chain": "x -> QKV projection -> attention core (causal, 4 q heads / 1 kv head) -> o_proj partial"}
+    out = {"workload": w.name, "qkv_ms": tm.ms("qkv"), "qkv_ms_stats": tm.stats("qkv"),
+           "qkv_TFLOPs": fq / tm.ms("qkv") / 1e9,
+           "attn_ms": tm.ms("attn"), "attn_ms_stats": tm.stats("attn"), "attn_TFLOPs": fa / tm.ms("attn") / 1e9,
+           "attn_mfma_frac": fa / tm.ms("attn") / 1e9 / PEAK_BF16_TFLOPS,
+           "o_proj_ms": tm.ms("o_proj"), "o_proj_ms_stats": tm.stats("o_proj"),
+           "o_proj_TFLOPs": fo / tm.ms("o_proj") / 1e9,
+           "qkv_mfma_frac": fq / tm.ms("qkv") / 1e9 / PEAK_BF16_TFLOPS,
+           "o_proj_mfma_frac": fo / tm.ms("o_proj") / 1e9 / PEAK_BF16_TFLOPS,
+           "chain": "x -> QKV projection -> attention core (causal, 4 q heads / 1 kv head) -> o_proj partial",
+           "cold": "3 token inputs and 3 partials rotated; warm_* = one of each"}
+    wt = res["warm"]
+    for k in ("qkv", "attn", "o_proj"):
+        out[f"warm_{k}_ms"] = wt.ms(k)
+        out[f"warm_{k}_ms_stats"] = wt.stats(k)
+    return out
 
 
 def leg_qwen_fp32(reps):
@@ -392,21 +470,29 @@ def leg_qwen_fp32(reps):
     up = gen(w, synth.T_UP, (w.f, w.h), 0.02)
     down = gen(w, synth.T_DOWN, (w.h, w.f), 0.02)
     shards = [(T.tp_shard_gate_up(gate, up, r, w.tp), T.tp_shard_weights(down, 1, r, w.tp)) for r in range(w.tp)]
+    # cold: 16 copies of both ranks' weights in rotation (605 MB > 256 MB MALL)
+    sets = [shards] + [[(a.clone(), b.clone()) for a, b in shards] for _ in range(15)]
     ws = torch.empty(T.tp_mlp_workspace_bytes(w.n, w.h, w.f_local, w.dtype), dtype=torch.uint8, device=DEV)
     parts = [torch.empty((w.n, w.h), dtype=w.dtype, device=DEV) for _ in range(w.tp)]
     y = torch.empty((w.n, w.h), dtype=w.dtype, device=DEV)
-    tm = EventTimer()
-    for i in range(3 + reps):
-        t_ = tm if i >= 3 else None
-        if t_:
-            t_.start("layer")
+
+    def layer(i, cold):
+        sh = sets[i % 16] if cold else shards
         for r in range(w.tp):
-            T.tp_mlp_rank_forward(x, shards[r][0], shards[r][1], partial=parts[r], workspace=ws)
+            T.tp_mlp_rank_forward(x, sh[r][0], sh[r][1], partial=parts[r], workspace=ws)
         T.tp_partial_reduce(parts, out=y)
-        if t_:
-            t_.stop("layer")
+
+    cold_v = batched_ms(lambda i: layer(i, True), reps)
+    warm_v = batched_ms(lambda i: layer(i, False), reps)
     torch.cuda.synchronize()
-    return {"workload": w.name, "all_ranks_plus_reduce_us": tm.ms("layer") * 1e3,
+    wb = (3 * w.f_local * w.h) * 4
+    return {"workload": w.name, "all_ranks_plus_reduce_us": median(cold_v) * 1e3,
+            "all_ranks_plus_reduce_us_stats": {k: (v * 1e3 if k != "n" else v) for k, v in stats(cold_v).items()},
+            "warm_all_ranks_plus_reduce_us": median(warm_v) * 1e3,
+            "warm_all_ranks_plus_reduce_us_stats": {k: (v * 1e3 if k != "n" else v)
+                                                    for k, v in stats(warm_v).items()},
+            "weight_bytes_per_rank": wb,
+            "cold": "16 copies of both ranks' weights rotated; warm = one copy",
             "note": "latency bound at this size (19 MB of fp32 weights per rank)"}
 
 
@@ -489,7 +575,7 @@ def cpu_baseline(S, budget_s=12.0):
     D = to_f64(S["wd"])
     cap = 4096
     X = to_f64(S["x"][:cap])
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = oracle_cores()
     rows = max(1, min(cores, cap))
     t0 = time.perf_counter()
     oracle.mlp_rank(X[:rows], G, U, D, 0, 1)
@@ -504,6 +590,63 @@ def cpu_baseline(S, budget_s=12.0):
     return {"value": flops / dt2 / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{more} of {w.n} token rows of the rank's MLP share (fp64, {dt2:.1f} s)",
             "full_workload_extrapolated_s": dt2 * w.n / more}
+
+
+def oracle_cores():
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def host_bf16_f64(shape, std, seed):
+    """seeded N(0, std^2) draws on the host, rounded to bf16, widened to fp64"""
+    return synth.normal(shape, std, seed, torch.bfloat16).to(torch.float64).numpy()
+
+
+def host_bf16_f32(shape, std, seed):
+    return synth.normal(shape, std, seed, torch.bfloat16).to(torch.float32).numpy()
+
+
+def cpu_oracle_legs():
+    """The fp64 oracle beside the decode and reduce legs, at full size, on
+    host-generated inputs of the same shapes and distributions (the oracle's
+    time does not depend on the values): the decode rank share (64 tokens,
+    f_local 7168) and its ring-order reduce of 4 partials of 1 MiB, and the
+    8- and 16-rank reduces of 128 MiB partials (fp32 ring simulation and the
+    fp64 sum)."""
+    import oracle
+    out = {"cores": oracle_cores()}
+    w = synth.get("llama70b_decode_tp4")
+    fl = w.f_local
+    X = host_bf16_f64((w.n, w.h), 1.0, w.seed(synth.T_X))
+    G = host_bf16_f64((fl, w.h), 0.02, w.seed(synth.T_GATE))
+    U = host_bf16_f64((fl, w.h), 0.02, w.seed(synth.T_UP))
+    D = host_bf16_f64((w.h, fl), 0.02, w.seed(synth.T_DOWN))
+    t0 = time.perf_counter()
+    oracle.mlp_rank(X, G, U, D, 0, 1)
+    dt = time.perf_counter() - t0
+    del X, G, U, D
+    parts = [host_bf16_f32((w.n, w.h), 1.0, w.seed(synth.T_PARTIAL + q)) for q in range(w.tp)]
+    t0 = time.perf_counter()
+    oracle.ring_allreduce_f32(parts)
+    dr = time.perf_counter() - t0
+    out["decode"] = {"mlp_rank_s": round(dt, 4), "mlp_rank_GFLOPs": round(mlp_flops(w.n, w.h, fl) / dt / 1e9, 2),
+                     "ring_reduce_s": round(dr, 5),
+                     "what": "fp64 rank share at full size (64 tokens) + fp32 ring-order reduce of 4 x 1 MiB"}
+    for name, key in (("llama70b_prefill_tp8", "reduce8"), ("llama70b_attnproj_tp16", "reduce16")):
+        w = synth.get(name)
+        parts = [host_bf16_f32((w.n, w.h), 1.0, w.seed(synth.T_PARTIAL + q)) for q in range(w.tp)]
+        t0 = time.perf_counter()
+        oracle.ring_allreduce_f32(parts)
+        d_ring = time.perf_counter() - t0
+        parts = [p.astype("float64") for p in parts]
+        t0 = time.perf_counter()
+        oracle.reduce_sum_f64(parts)
+        d64 = time.perf_counter() - t0
+        b = (w.tp + 1) * w.n * w.h * 2
+        out[key] = {"ring_f32_s": round(d_ring, 3), "ring_f32_GBps": round(b / d_ring / 1e9, 2),
+                    "sum_f64_s": round(d64, 3),
+                    "what": f"{w.tp} partials of [{w.n}, {w.h}] at full size: fp32 ring-order simulation and fp64 sum"}
+        del parts
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -555,10 +698,12 @@ def main():
     tm.stop("step")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = tm.ms("step") / a.steps
+    ms_step = tm.all_ms("step")[0] / a.steps
     gu_ms, dn_ms, rd_ms = tm.ms("gate_up"), tm.ms("down"), tm.ms("reduce")
+    mlp_v = [g + d for g, d in zip(tm.all_ms("gate_up"), tm.all_ms("down"))]
+    gu_mean = sum(tm.all_ms("gate_up")) / len(tm.all_ms("gate_up"))
     fl = w.f_local
-    mlp_ms = gu_ms + dn_ms
+    mlp_ms = median(mlp_v)
     flops = mlp_flops(w.n, w.h, fl)
     value = flops / mlp_ms / 1e9
     gu_flops = 2.0 * w.n * w.h * 2 * fl
@@ -604,6 +749,12 @@ def main():
     if not a.no_cpu:
         log("bench: cpu baseline (fp64 oracle)")
         cpu = cpu_baseline(S)
+        if legs:
+            log("bench: cpu oracle beside the decode and reduce legs")
+            cpu["legs"] = cpu_oracle_legs()
+            for k in ("decode", "reduce8", "reduce16"):
+                if k in legs:
+                    legs[k]["cpu_oracle"] = cpu["legs"][k]
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -613,14 +764,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n": w.n, "h": w.h, "f_local": fl, "tp": w.tp,
                    "step": "gate_up+SiLU*up GEMM, down GEMM, ring-order reduce of 8 partials",
-                   "value_over": "MLP launches (gate_up + down) inside the timed steps"},
+                   "value_over": "median over the timed steps of the MLP launches (gate_up + down)"},
         "mlp_ms": round(mlp_ms, 4), "gate_up_ms": round(gu_ms, 4), "down_ms": round(dn_ms, 4),
         "reduce_ms": round(rd_ms, 4), "reduce_GBps": round(red_bytes / rd_ms / 1e6, 1),
+        "timing": "medians over the timed steps (HIP events around each launch); *_stats give median, min, max",
+        "mlp_ms_stats": stats(mlp_v), "gate_up_ms_stats": tm.stats("gate_up"), "down_ms_stats": tm.stats("down"),
+        "reduce_ms_stats": tm.stats("reduce"),
+        "cold": "each step streams 1.2 GB of partials through the reduce, so every step starts cold in the MALL",
         "step_TFLOPs_incl_reduce": round(flops / ms_step / 1e9, 2),
         "roofline": {"kernel": "gate_up GEMM + SiLU*up epilogue", "bound": "mfma",
-                     "achieved": round(gu_flops / gu_ms / 1e9, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gu_flops / gu_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic()},
+                     "achieved": round(gu_flops / gu_mean / 1e9, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gu_flops / gu_mean / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(),
+                     "duration": "mean gate_up launch time over the timed steps (HIP events)"},
         "cpu_baseline": cpu,
         "legs": legs,
     }
