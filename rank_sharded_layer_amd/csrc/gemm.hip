@@ -1577,24 +1577,29 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
 // The decode product reads a large weight matrix once for at most 64 token
 // rows, so its time is the weight stream from HBM.  This kernel keeps LDS
 // out of that stream:
-//   * one workgroup of 8 waves per CU (two per SIMD).  Workgroup (q, g) owns
-//     K slice q (8 R elements) and the 16-row weight blocks g, g + G, ...,
-//     so at any time the G workgroups of a slice read G adjacent blocks;
-//     wave w owns the R-element K range w of the slice;
+//   * one workgroup of 4 waves per CU (one per SIMD).  Workgroup (q, g) owns
+//     K slice q (4 R elements, R = 256 for K a multiple of 1024) and the
+//     16-row weight blocks g, g + G, ..., so at any time the G workgroups of
+//     a slice read G adjacent blocks; wave w owns the R-element K range w of
+//     the slice.  Four waves per CU stream faster than eight: a probe reading
+//     a 235 MB matrix in this pattern took 41 us with 4 waves of 256 K and
+//     46.5 us with 8 (same box);
 //   * a wave loads the fragments of all 64 tokens over its K range once and
 //     keeps them in registers (R/2 VGPRs);
 //   * weights go straight from HBM into MFMA A-fragments: for K step i of a
 //     block, lane l reads the 16 bytes of block row l & 15 at K chunk
 //     4 i + (l >> 4), so one instruction reads 16 rows x 64 contiguous bytes
-//     and the R/32 instructions of a block walk along each row (the 8 waves
-//     together read 16 R contiguous bytes of every row);
+//     and the R/32 instructions of a block walk along each row (the 4 waves
+//     together read 8 R contiguous bytes of every row);
 //   * two register slots of R/32 fragments: two blocks of loads per wave
 //     are in flight (16 KiB at R = 256);
 //   * after each block the waves' fp32 partials [64 tokens][16 rows] meet in
 //     LDS, are added in wave (= K) order and stored as the workgroup's
 //     partial tile; a finalize pass adds the S slices' tiles in slice order
 //     and applies the epilogue.  No atomics: the result is deterministic.
-constexpr int RS_WAVES = 8;
+constexpr int RS_WAVES = 4;
+constexpr int RS_SLICE = 1024;      // K per workgroup: RS_WAVES waves of 256
+constexpr int RS_HOLD = 28;         // partial tiles a workgroup keeps in LDS (112 KiB)
 
 struct RsOp {
     const uint16_t* A;      // tokens [M, K]
@@ -1604,7 +1609,7 @@ struct RsOp {
     int S, G, R, rbn;       // K slices, workgroups per slice, K per wave, 16-row blocks
 };
 
-// S = ceil(K / 2048) slices, R = K per wave rounded up to the 32 of a K step
+// S = ceil(K / RS_SLICE) slices, R = K per wave rounded up to the 32 of a K step
 // (at most 256: the tokens' fragments take R/2 VGPRs), up to 256 / S
 // workgroups per slice.
 __host__ __device__ inline RsOp make_rs_op(const uint16_t* A, const uint16_t* B, float* part, int64_t M,
@@ -1616,7 +1621,7 @@ __host__ __device__ inline RsOp make_rs_op(const uint16_t* A, const uint16_t* B,
     o.M = M;
     o.K = K;
     o.Nb = Nb;
-    o.S = (int)((K + 2047) / 2048);
+    o.S = (int)((K + RS_SLICE - 1) / RS_SLICE);
     const int64_t per_slice = (K + o.S - 1) / o.S;
     o.R = (int)(((per_slice + RS_WAVES - 1) / RS_WAVES + 31) / 32 * 32);
     o.rbn = (int)((Nb + 15) / 16);
@@ -1625,8 +1630,13 @@ __host__ __device__ inline RsOp make_rs_op(const uint16_t* A, const uint16_t* B,
 }
 
 template <int NKS, bool EDGE>
-__global__ __launch_bounds__(512) void gemm_bf16_rs_kernel(RsOp o) {
+__global__ __launch_bounds__(RS_WAVES * 64) void gemm_bf16_rs_kernel(RsOp o) {
     __shared__ __attribute__((aligned(16))) float red[2][RS_WAVES][1024];
+    // the workgroup's partial tiles, written to memory in one burst after
+    // the weight stream when they fit (stores interleaved with the stream
+    // slowed it: a 235 MB probe in this pattern took 52.0 us with per-block
+    // stores and 49.4 us with the burst, same box)
+    __shared__ __attribute__((aligned(16))) float hold[RS_HOLD][1024];
     constexpr uint32_t SENT = 0x80000000u;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1694,6 +1704,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_rs_kernel(RsOp o) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     float* part = o.part + (int64_t)q * o.rbn * 1024;
+    const bool hold_all = nb <= RS_HOLD;
 
     auto block = [&](int j, auto slot_c) {
         constexpr int SL = decltype(slot_c)::value;
@@ -1717,15 +1728,17 @@ __global__ __launch_bounds__(512) void gemm_bf16_rs_kernel(RsOp o) {
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): the LDS writes are done
         bare_barrier();
-        const int e = threadIdx.x * 2;
-        float2 v = *reinterpret_cast<const float2*>(&red[j & 1][0][e]);
+        const int e = threadIdx.x * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(&red[j & 1][0][e]);
 #pragma unroll
         for (int w = 1; w < RS_WAVES; ++w) {
-            const float2 t = *reinterpret_cast<const float2*>(&red[j & 1][w][e]);
-            v.x = v.x + t.x;
-            v.y = v.y + t.y;
+            const f32x4 t = *reinterpret_cast<const f32x4*>(&red[j & 1][w][e]);
+            v = v + t;
         }
-        *reinterpret_cast<float2*>(part + (int64_t)(g + j * o.G) * 1024 + e) = v;
+        if (hold_all)
+            *reinterpret_cast<f32x4*>(&hold[j][e]) = v;
+        else
+            *reinterpret_cast<f32x4*>(part + (int64_t)(g + j * o.G) * 1024 + e) = v;
         // the next block's accumulators start after this barrier: without the
         // opaque definition the compiler hoists their MFMAs above it (they
         // start from zero), which forces a wait for every load in flight
@@ -1738,6 +1751,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_rs_kernel(RsOp o) {
         block(j + 1, S1{});
     }
     if (j < nb) block(j, S0{});
+    if (hold_all) {
+        __syncthreads();
+        const int e = threadIdx.x * 4;
+        for (int jj = 0; jj < nb; ++jj)
+            *reinterpret_cast<f32x4*>(part + (int64_t)(g + jj * o.G) * 1024 + e) =
+                *reinterpret_cast<const f32x4*>(&hold[jj][e]);
+    }
 }
 
 // Thread (token m, columns j .. j+3): adds the S slices' partials in slice
@@ -2280,8 +2300,8 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         switch (o.R / 32) {
 #define RS_LAUNCH(NKS)                                                                         \
     case NKS:                                                                                  \
-        if (edge) hipLaunchKernelGGL((gemm_bf16_rs_kernel<NKS, true>), grid, dim3(512), 0, s, o);  \
-        else hipLaunchKernelGGL((gemm_bf16_rs_kernel<NKS, false>), grid, dim3(512), 0, s, o);      \
+        if (edge) hipLaunchKernelGGL((gemm_bf16_rs_kernel<NKS, true>), grid, dim3(RS_WAVES * 64), 0, s, o);  \
+        else hipLaunchKernelGGL((gemm_bf16_rs_kernel<NKS, false>), grid, dim3(RS_WAVES * 64), 0, s, o);      \
         break;
             RS_LAUNCH(4)
             RS_LAUNCH(5)

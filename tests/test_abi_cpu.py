@@ -72,12 +72,12 @@ def test_workspace_queries():
     # 896 gated tiles = 3 rounds + 128: the last 128 tiles are cut into two
     # K pieces each, whose fp32 256 x 256 partial tiles need a workspace
     assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 128 * 2 * 256 * 256 * 4
-    # decode shapes: the weight-streaming kernel keeps per-tile fp32 partials
     # decode shapes (register-streaming kernel): one fp32 [64 x 16] partial
-    # tile per K slice of at most 2048 and 16-row weight block
-    assert T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16) == 4 * (14336 // 16) * 4096
-    assert T.tp_linear_workspace_bytes(64, 7168, 8192, torch.bfloat16) == 4 * (8192 // 16) * 4096
-    assert T.tp_linear_workspace_bytes(1, 4104, 2744, torch.bfloat16) == 3 * 172 * 4096
+    # tile per K slice of at most 1024 and 16-row weight block
+    assert T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16) == 8 * (14336 // 16) * 4096
+    assert T.tp_linear_workspace_bytes(64, 7168, 8192, torch.bfloat16) == 7 * (8192 // 16) * 4096
+    assert T.tp_linear_workspace_bytes(1, 4104, 2744, torch.bfloat16) == 5 * 172 * 4096
+    assert T.tp_gate_up_workspace_bytes(64, 8192, 4096, torch.bfloat16) == 8 * (8192 // 16) * 4096
     # few output tiles: split-K partial sums
     assert T.tp_gate_up_workspace_bytes(64, 8192, 64, torch.bfloat16) > 0
     # few output tiles and a long K: split-K partial sums need a workspace

@@ -22,12 +22,17 @@ Shapes and the kernel the planner gives each (the launch configuration the
 benchmark times):
   prefill gate_up   8192 x 8192 -> 2 x 3584   256x256 paired-stage tiles, balanced last round
   prefill down      8192 x 3584 -> 8192       256x256 paired-stage tiles, 4 full rounds
-  decode gate_up      64 x 8192 -> 2 x 7168   register-streaming split-K + slice-order finish
-  decode down         64 x 7168 -> 8192       register-streaming split-K + slice-order finish
+  decode gate_up      64 x 8192 -> 2 x 7168   register streaming, 8 K slices of 1024 + slice-order finish
+  decode down         64 x 7168 -> 8192       register streaming, 7 K slices of 1024 + slice-order finish
   QKV (TP=16)       8192 x 8192 -> 768        128x128 direct-to-LDS tiles
   o_proj (TP=16)    8192 x  512 -> 8192       256x256 paired-stage tiles, K = 512
   LM head (TP=2)     512 x 1024 -> 75968 fp32 256x256 tiles, fp32 rows staged through LDS
   fp32 MLP (TP=2)     16 x 1024 -> 2 x 1536, 16 x 1536 -> 1024   fp32 small-M kernels
+and the kernels other shapes take: the register-streaming kernel at
+narrower outputs, the LDS-ring streaming decode kernel with its finish
+pass, 64x128 split-K
+tiles (the QKV projection of one decode step at TP=16), and the
+element-wise register-staged tiles (K not a multiple of 8).
 """
 import numpy as np
 import pytest
@@ -157,3 +162,32 @@ def test_fp32_small_m_kernels_bit_exact():
     down = synth.normal((w.h, fl), 0.02, w.seed(synth.T_DOWN), torch.float32, device=DEV)
     y = T.tp_linear_rank_forward(xd, down)
     assert np.array_equal(bits(y), np.ascontiguousarray(bits(down)[:, jd].T))
+
+
+# ---- kernels of other decode-sized shapes ---------------------------------------
+
+def test_register_streaming_narrow_outputs_bit_exact():
+    """Narrower outputs with long K: K slices of 1024, fp32 partial tiles
+    added in slice order by the finish pass."""
+    check_linear_exact(64, 6144, 4000, torch.bfloat16, 401)
+    check_gate_up_exact(64, 8192, 4096, 402)
+
+
+def test_lds_ring_streaming_bit_exact():
+    """Shorter K with few 16-row blocks: the persistent LDS-ring kernel."""
+    check_gate_up_exact(64, 4000, 2040, 403)
+    check_linear_exact(64, 2040, 4000, torch.float32, 404)
+
+
+def test_split_k_64x128_tiles_bit_exact():
+    """One decode step's QKV projection at TP=16 (64 x 8192 -> 768): 64x128
+    deep-pipelined tiles with K split for occupancy and a split-order finish."""
+    check_linear_exact(64, 8192, 768, torch.bfloat16, 405)
+
+
+def test_element_wise_register_staged_tiles_bit_exact():
+    """K = 1001 is not a multiple of 8: 128x128 (M > 64) and 64x128 tiles
+    with element-wise loads."""
+    check_linear_exact(300, 1001, 520, torch.bfloat16, 406)
+    check_linear_exact(40, 1001, 520, torch.float32, 407)
+    check_gate_up_exact(40, 1001, 200, 408)

@@ -498,19 +498,20 @@ def test_stream_decode_gate_up_matches_oracle(n, h, fl):
 # --------------------------------------------------------------------------
 # register-streaming decode kernel (M <= 64 tokens, K >= 1024, at least two
 # 16-row weight blocks per workgroup): one fp32 partial tile [64][16] per
-# K slice of at most 2048 and 16-row block, added in slice order
+# K slice of at most 1024 and 16-row block, added in slice order
 # --------------------------------------------------------------------------
 
 def rs_ws(k, rows):
-    return -(-k // 2048) * -(-rows // 16) * 4096
+    return -(-k // 1024) * -(-rows // 16) * 4096
 
 
 @pytest.mark.parametrize("n", [1, 33, 64])
-@pytest.mark.parametrize("k,m", [(4104, 2744), (2048, 8200), (7168, 8192)])
+@pytest.mark.parametrize("k,m", [(4104, 2744), (6144, 4000), (7168, 4104)])
 def test_rs_decode_linear_matches_oracle(n, k, m):
-    """k = 4104: 3 slices of 8 x 192 with a ragged end; m = 2744 and 8200
-    end inside a 16-row block; (7168, 8192) is the 70B down shard at TP=4
-    (4 slices of 8 x 224)."""
+    """k = 4104: 3 slices of 8 x 192 with a ragged end; m = 2744 and 4104
+    end inside a 16-row block; k = 7168 is the 70B down shard's K at TP=4
+    (4 slices of 8 x 224).  Outputs under 6144 columns: too few 32-column
+    workgroups for the whole-K kernel."""
     assert T.tp_linear_workspace_bytes(n, k, m, torch.bfloat16) == rs_ws(k, m)
     x = rnd((n, k), 1.0, 230 + n, torch.bfloat16)
     w = rnd((m, k), 0.05, 231, torch.bfloat16)
@@ -536,6 +537,41 @@ def test_rs_decode_gate_up_matches_oracle(n, h, fl):
     ref = oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:]))
     assert relf(to_f64(act), ref) <= 1e-2
     assert relf(to_f64(act[:, -20:]), ref[:, -20:]) <= 1e-2
+    assert torch.equal(act, T.tp_gate_up_act_rank(x, wgu))     # fixed order: deterministic
+
+
+@pytest.mark.parametrize("n", [1, 33, 64])
+@pytest.mark.parametrize("k,m", [(2048, 8200), (7168, 8192), (4104, 6150), (1032, 6200)])
+def test_rs_decode_wide_linear_matches_oracle(n, k, m):
+    """Wide outputs: (7168, 8192) is the 70B down shard at TP=4 (7 slices of
+    4 x 256); m = 8200, 6150 and 6200 end inside a 16-row block; k = 4104
+    and 1032 cut the slices and the waves' K ranges raggedly (at k = 1032
+    the second slice holds 8 columns)."""
+    assert T.tp_linear_workspace_bytes(n, k, m, torch.bfloat16) == rs_ws(k, m)
+    x = rnd((n, k), 1.0, 250 + n, torch.bfloat16)
+    w = rnd((m, k), 0.05, 251, torch.bfloat16)
+    b = rnd((m,), 0.05, 252, torch.bfloat16)
+    for bias in (None, b):
+        ref = oracle.linear(to_f64(x), to_f64(w), to_f64(bias) if bias is not None else None)
+        for out_dt in (torch.bfloat16, torch.float32):
+            y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+            assert relf(to_f64(y), ref) <= 1e-2, (bias is None, out_dt)
+            assert relf(to_f64(y[:, -40:]), ref[:, -40:]) <= 1e-2
+
+
+@pytest.mark.parametrize("n", [1, 64])
+@pytest.mark.parametrize("h,fl", [(4104, 6150), (1032, 6200), (8192, 6144)])
+def test_rs_decode_wide_gate_up_matches_oracle(n, h, fl):
+    """Wide gated outputs; fl = 6150 ends inside a 16-row block, so the up
+    rows start inside one."""
+    assert T.tp_gate_up_workspace_bytes(n, h, fl, torch.bfloat16) == rs_ws(h, 2 * fl)
+    x = rnd((n, h), 1.0, 260 + n, torch.bfloat16)
+    wgu = rnd((2 * fl, h), 0.05, 261, torch.bfloat16)
+    act = T.tp_gate_up_act_rank(x, wgu)
+    xg, W = to_f64(x), to_f64(wgu)
+    ref = oracle.silu_mul(oracle.linear(xg, W[:fl]), oracle.linear(xg, W[fl:]))
+    assert relf(to_f64(act), ref) <= 1e-2
+    assert relf(to_f64(act[:, -40:]), ref[:, -40:]) <= 1e-2
     assert torch.equal(act, T.tp_gate_up_act_rank(x, wgu))     # fixed order: deterministic
 
 
