@@ -1945,6 +1945,110 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(F32Args p) {
     }
 }
 
+// fp32, few tokens (M <= 32, K <= 2048, 16-byte rows): one workgroup of 16
+// waves per 16 output columns (gated: the 16 gate rows and the same 16 up
+// rows), the waves splitting K into 16 ranges of STEPS x 16.  Per 16 K
+// values a lane loads 16 bytes of its weight row (row l & 15, K values
+// 4 (l >> 4) .. +3) and 16 bytes of its token row, and the four K values go
+// in order to four v_mfma_f32_16x16x4_f32 (fp32 products and sums, no
+// reduced-precision inputs).  Every load of a wave is issued before its
+// first MFMA: the whole product is one round trip to memory per wave.  The
+// 16 waves' sums meet in LDS and are added in wave (= K) order, so the
+// result is deterministic.
+constexpr int F32W = 16;
+
+template <bool GATED, int TB, int STEPS>
+__global__ __launch_bounds__(F32W * 64) void gemm_f32_mfma_kernel(F32Args p) {
+    constexpr int RB = GATED ? 2 : 1;
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) f32x4 red[F32W][RB][TB][64];
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t kbeg = (int64_t)wid * STEPS * 16 + kq * 4;
+    const float* wrow[RB];
+    bool wok[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        wok[rb] = n0 + r16 < p.N;
+        wrow[rb] = p.B + ((rb == 0 ? 0 : p.N) + n0 + r16) * p.K;
+    }
+    const float* xrow[TB];
+    bool xok[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        xok[tb] = tb * 16 + r16 < p.M;
+        xrow[tb] = p.A + (int64_t)(tb * 16 + r16) * p.K;
+    }
+    f4v w[STEPS][RB], x[STEPS][TB];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int64_t k = kbeg + s * 16;
+        const bool kin = k < p.K;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            w[s][rb] = (kin && wok[rb]) ? *reinterpret_cast<const f4v*>(wrow[rb] + k) : (f4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+            x[s][tb] = (kin && xok[tb]) ? *reinterpret_cast<const f4v*>(xrow[tb] + k) : (f4v){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    f32x4 acc[RB][TB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[rb][tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[s][rb][e], x[s][tb][e], acc[rb][tb], 0, 0, 0);
+    // lane l of block (rb, tb) holds weight rows 4 (l >> 4) .. +3 of the
+    // block for token 16 tb + (l & 15)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) red[wid][rb][tb][lane] = acc[rb][tb];
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t >= TB * 64) return;
+    const int tb = t >> 6, l = t & 63;
+    f32x4 v0 = red[0][0][tb][l];
+#pragma unroll
+    for (int wv = 1; wv < F32W; ++wv) v0 = v0 + red[wv][0][tb][l];
+    float v[4];
+    if constexpr (GATED) {
+        f32x4 v1 = red[0][RB - 1][tb][l];
+#pragma unroll
+        for (int wv = 1; wv < F32W; ++wv) v1 = v1 + red[wv][RB - 1][tb][l];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = silu_mul(v0[e], v1[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = v0[e];
+    }
+    const int64_t m = tb * 16 + (l & 15);
+    const int64_t c0 = n0 + 4 * (l >> 4);
+    if (m >= p.M || c0 >= p.N) return;
+    float* dst = p.C + m * p.N + c0;
+    if (!GATED && p.bias) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (c0 + e < p.N) v[e] = v[e] + p.bias[c0 + e];
+    }
+    if (c0 + 3 < p.N && ((p.N & 3) == 0) && ((((uintptr_t)p.C) & 15u) == 0)) {
+        *reinterpret_cast<f4v*>(dst) = (f4v){v[0], v[1], v[2], v[3]};
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (c0 + e < p.N) dst[e] = v[e];
+    }
+}
+
 // Finishes the tiles of a balanced last round: adds each tile's K pieces in
 // piece order and applies the epilogue (gated SiLU(g)*u, or store + bias).
 // One thread per 4 consecutive output columns of a tile row (float4 reads).
@@ -2262,6 +2366,30 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
         tiles_for(K_F32, M, N, gated, tm, tn);
         F32Args a{static_cast<const float*>(A), static_cast<const float*>(B),
                   static_cast<const float*>(bias), static_cast<float*>(C), M, N, K, Nb, tm, tn};
+        const bool f32_vec = (K % 4) == 0 && (((uintptr_t)A | (uintptr_t)B) & 15u) == 0;
+        if (M <= 32 && f32_vec && K <= 16 * 16 * 8) {
+            // one 16-wave workgroup per 16 output columns, STEPS x 16 K per wave
+            const int steps = (int)ceil_div(K, 16 * F32W);
+            const dim3 g((unsigned)ceil_div(N, 16));
+#define F32M_LAUNCH(G_, TB_)                                                                             \
+    switch (steps) {                                                                                     \
+        case 1: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 1>), g, dim3(F32W * 64), 0, s, a); break; \
+        case 2: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 2>), g, dim3(F32W * 64), 0, s, a); break; \
+        case 3: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 3>), g, dim3(F32W * 64), 0, s, a); break; \
+        case 4: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 4>), g, dim3(F32W * 64), 0, s, a); break; \
+        case 5: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 5>), g, dim3(F32W * 64), 0, s, a); break; \
+        case 6: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 6>), g, dim3(F32W * 64), 0, s, a); break; \
+        case 7: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 7>), g, dim3(F32W * 64), 0, s, a); break; \
+        default: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 8>), g, dim3(F32W * 64), 0, s, a); break; \
+    }
+            if (gated) {
+                if (M <= 16) { F32M_LAUNCH(true, 1) } else { F32M_LAUNCH(true, 2) }
+            } else {
+                if (M <= 16) { F32M_LAUNCH(false, 1) } else { F32M_LAUNCH(false, 2) }
+            }
+#undef F32M_LAUNCH
+            return hipGetLastError();
+        }
         if (M <= 32) {
             // 4 waves per workgroup, 4 B rows (gated: 2 act columns) per wave
             const int64_t units = gated ? ceil_div(N, 2) : ceil_div(N, 4);
