@@ -878,11 +878,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
     constexpr int STAGE = (BM + BN) * ROWB;
     constexpr int N_INSTR = STAGE / 1024;                // one wave instruction fills 1 KiB
     constexpr int A_INSTR = A_BYTES / 1024;
-    static_assert(N_INSTR % NW == 0, "each wave issues the same number of DMA instructions");
+    static_assert(PAIR || N_INSTR % NW == 0, "each wave issues the same number of DMA instructions");
     constexpr int PW = N_INSTR / NW;
     static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up MFMA blocks");
     constexpr uint32_t SENT = 0x80000000u;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
+    // 128 x 192 tiles keep one workgroup per CU (their tile count is sized
+    // to the CU count): the ring is padded past half of the CU's 160 KiB
+    constexpr int LDS_BYTES = (BM == 128 && BN == 192) ? 96 * 1024 : NST * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1202,7 +1205,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
             }
         return;
     }
-    if constexpr (EPI == EPI_STORE_F32) {
+    // (the staged store's slot swizzle needs BN / 4 a power of two)
+    if constexpr (EPI == EPI_STORE_F32 && (BN & (BN - 1)) == 0) {
         if (p.vec_out) {
             staged_store_f32<BM, BN, WM, WN>(p, acc, lds, m0, n0, wm, wn, lane);
             return;
@@ -2095,7 +2099,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs p, int BM, int
 // ---- planning -------------------------------------------------------------
 
 enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DEC4 = 6,
-            K_BF16_STREAM = 7, K_BF16_RS = 8 };
+            K_BF16_STREAM = 7, K_BF16_RS = 8, K_BF16_MID = 9 };
 
 // Tile configurations (BM tokens x BN weight rows):
 //   HUGE8 256x256, 2x4 waves of 128x64 (prefill-sized problems; deep-pipelined
@@ -2113,6 +2117,7 @@ static TileCfg tile_cfg(int k) {
         case K_BF16_HUGE8: return TileCfg{256, 256, 2, 4};
         case K_BF16_SMALL: return TileCfg{64, 128, 1, 2};
         case K_BF16_DEC4: return TileCfg{64, 128, 1, 4};
+        case K_BF16_MID: return TileCfg{128, 192, 2, 4};
         default: return TileCfg{128, 128, 2, 2};
     }
 }
@@ -2204,6 +2209,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     if (M > 64) {
         tiles_for(K_BF16_HUGE8, M, N, gated, tm, tn);
         pl.kernel = (int64_t)tm * tn >= 512 ? huge_kernel() : K_BF16_LARGE;
+        // fewer 256 x 256 tiles than two rounds: 128 x 192 tiles on the
+        // paired-stage kernel when they fill at least three quarters of the
+        // CUs (the QKV projection at TP=16: 8192 x 768 = 256 tiles, one per
+        // CU, where 128 x 128 tiles left a quarter of a round empty)
+        if (pl.kernel == K_BF16_LARGE && !gated && K % 64 == 0) {
+            int mm, mn;
+            tiles_for(K_BF16_MID, M, N, gated, mm, mn);
+            const int64_t mt = (int64_t)mm * mn;
+            if (mt >= 192 && (mt % 256 == 0 || mt % 256 >= 192)) pl.kernel = K_BF16_MID;
+        }
     } else {
         pl.kernel = K_BF16_DEC4;
     }
@@ -2211,7 +2226,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     const int64_t tiles = (int64_t)tm * tn;
     const int64_t Nb = gated ? 2 * N : N;
     // fewer tiles than CUs: split K so that the launch fills the machine
-    if (tiles < 256 && K >= 1024) {
+    if (tiles < 256 && K >= 1024 && pl.kernel != K_BF16_MID) {
         int64_t want = pl.kernel == K_BF16_DEC4 ? kSplitTargetDec4 / tiles : ceil_div(kSplitTarget, tiles);
         int64_t maxs = pl.kernel == K_BF16_DEC4 ? K / 256 : K / 512;
         int64_t s = want < maxs ? want : maxs;
@@ -2233,7 +2248,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     // for long K: each piece costs a 4-byte-per-element partial tile written
     // and read back, which pieces shorter than 1024 do not pay for.
     const int64_t slots = 256 * wgs_per_cu(pl.kernel);
-    if (pl.splits == 1 && K % 8 == 0 && tiles > slots && tiles % slots != 0) {
+    if (pl.splits == 1 && K % 8 == 0 && tiles > slots && tiles % slots != 0 && pl.kernel != K_BF16_MID) {
         const int64_t rem = tiles % slots;
         int64_t sp = slots / rem;
         if (sp >= 2) {
@@ -2305,6 +2320,12 @@ static void launch_pipe_one(const GemmArgs& a, int splits, hipStream_t s) {
     const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
     dim3 grid((unsigned)units, (unsigned)splits);
     const bool kt32 = (a.K % 32) != 0 || (a.k_split % 32) != 0;
+    if constexpr (BM == 128 && BN == 192) {
+        // paired stages only (the planner takes these tiles for K a
+        // multiple of 64, without split-K or tail pieces)
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false, true>), grid, dim3(WM * WN * 64), 0, s, a);
+        return;
+    } else {
     // paired K = 64 stages: every K range a multiple of 64
     const bool pair = BM == 256 && a.K % 64 == 0 && a.k_split % 64 == 0 &&
                       (a.tail_split <= 1 || a.tail_k % 64 == 0);
@@ -2320,6 +2341,7 @@ static void launch_pipe_one(const GemmArgs& a, int splits, hipStream_t s) {
     else
         hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false, false>), grid, dim3(WM * WN * 64), 0, s, a);
     launch_tail_fixup<BM, BN, EPI>(a, ntiles, s);
+    }
 }
 
 enum Launcher { L_PIPE = 0, L_DL = 1, L_REG = 2 };
@@ -2336,7 +2358,11 @@ static void launch_epi(int epi, const GemmArgs& a, int splits, hipStream_t s) {
     switch (epi) {
         case EPI_STORE_BF16: launch_one<L, BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, s); break;
         case EPI_STORE_F32: launch_one<L, BM, BN, WM, WN, EPI_STORE_F32>(a, splits, s); break;
-        case EPI_GATED_BF16: launch_one<L, BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, s); break;
+        case EPI_GATED_BF16:
+            // 128 x 192 tiles hold an odd number of 16-row blocks per wave:
+            // the planner never gives them gated products
+            if constexpr (!(BM == 128 && BN == 192)) launch_one<L, BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, s);
+            break;
         default: launch_one<L, BM, BN, WM, WN, EPI_SPLIT>(a, splits, s); break;
     }
 }
@@ -2350,6 +2376,7 @@ static void launch_bf16_kern(int kern, int epi, const GemmArgs& a, int splits, b
     }
     switch (kern) {
         case K_BF16_HUGE8: launch_epi<L_PIPE, 256, 256, 2, 4>(epi, a, splits, s); break;
+        case K_BF16_MID: launch_epi<L_PIPE, 128, 192, 2, 4>(epi, a, splits, s); break;
         case K_BF16_DEC4:
         case K_BF16_SMALL: launch_epi<L_PIPE, 64, 128, 1, 4>(epi, a, splits, s); break;
         default: launch_epi<L_DL, 128, 128, 2, 2>(epi, a, splits, s); break;
@@ -2537,7 +2564,7 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
     }
     // operands the 16-byte loads cannot serve take the element-wise kernel,
     // 128 x 128 tiles in place of the 256 x 256 ones
-    const int kern = (!vec && pl.kernel == K_BF16_HUGE8) ? K_BF16_LARGE : pl.kernel;
+    const int kern = (!vec && (pl.kernel == K_BF16_HUGE8 || pl.kernel == K_BF16_MID)) ? K_BF16_LARGE : pl.kernel;
     int tm, tn;
     tiles_for(kern, M, N, gated, tm, tn);
     a.tiles_m = tm;

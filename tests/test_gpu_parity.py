@@ -411,6 +411,26 @@ def test_tail_split_gate_up_matches_oracle(n, h, fl):
     assert torch.equal(act, again)          # fixed piece order: deterministic
 
 
+@pytest.mark.parametrize("n,k,m", [(8100, 1024, 760), (8192, 2048, 768), (8192, 640, 1536)])
+def test_mid_tiles_linear_matches_oracle(n, k, m):
+    """128 x 192 paired-stage tiles, chosen when 256 x 256 tiles would be
+    too few and 128 x 192 ones fill at least three quarters of the CUs:
+    (8100, 760) leaves ragged last tiles in both dimensions (64 x 4 tiles),
+    (8192, 1536) gives 64 x 8 = 512 tiles (two rounds).  Bias and both
+    output types; the fp32 store goes element-wise here."""
+    x = rnd((n, k), 1.0, 270, torch.bfloat16)
+    w = rnd((m, k), 0.05, 271, torch.bfloat16)
+    b = rnd((m,), 0.05, 272, torch.bfloat16)
+    rows = synth.sample_rows(n, 10, 273)
+    for bias in (None, b):
+        ref = oracle.linear(to_f64(x)[rows], to_f64(w), to_f64(bias) if bias is not None else None)
+        for out_dt in (torch.bfloat16, torch.float32):
+            y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+            assert relf(to_f64(y)[rows], ref) <= 1e-2, (bias is None, out_dt)
+            assert relf(to_f64(y[-1:]), oracle.linear(to_f64(x)[-1:], to_f64(w),
+                                                      to_f64(bias) if bias is not None else None)) <= 1e-2
+
+
 @pytest.mark.parametrize("n,k,m", [(4100, 1024, 7800), (8192, 3584, 8192)])
 def test_paired_stage_tiles_linear_matches_oracle(n, k, m):
     """256 x 256 tiles with K a multiple of 64 (paired K = 64 LDS stages):
