@@ -15,17 +15,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32): round to
+// nearest, ties to even; NaN stays NaN.
+typedef float cvt_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 cvt_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-// pack two fp32 into two bf16 (lo in the low half)
+// pack two fp32 into two bf16 (lo in the low half), one instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((cvt_f32x2){lo, hi}, cvt_bf16x2));
 }
 
 // ---- element load/store by dtype ----------------------------------------
@@ -40,10 +38,13 @@ template <> struct Elem<uint16_t> {
     static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
-// SiLU(g) * u in fp32: g * sigmoid(g) * u.  For g -> -inf, exp(-g) -> inf and
-// the quotient goes to -0; for g -> +inf the quotient goes to g.
+// SiLU(g) * u in fp32: g * sigmoid(g) * u, the quotient g / (1 + e^-g) taken
+// as g times the hardware reciprocal (1 ulp) of 1 + e^-g.  For g -> -inf,
+// e^-g -> inf, whose reciprocal is 0, and the product goes to -0; for
+// g -> +inf it goes to g.  (1 + e^-g rounds to 1 for g > 17, whose
+// reciprocal is exactly 1.)
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -840,6 +840,164 @@ __device__ __forceinline__ void staged_store_f32(const GemmArgs& p, f32x4 (&acc)
     }
 }
 
+// Direct-to-LDS loads of paired stages (K = 64, tile rows of 128 bytes):
+// one wave instruction fetches 8 tile rows x 128 contiguous bytes, whole
+// 128-byte lines.  Chunk c of tile row r sits at position c ^ ((r >> 1) & 7),
+// so the 16 rows of one fragment read fall in 16 distinct 16-byte bank
+// groups (rows alternate between the two 128-byte halves of the 256 bytes
+// the 64 banks cover); lane l of an instruction fills slot l and fetches
+// the chunk that belongs there.  A stage holds BM A rows, then BN B rows
+// (gated: BN/2 gate rows, then the same BN/2 up rows).  Rows past the end
+// of the operand get an offset past the buffer's range, which loads zeros.
+template <int BM, int BN, int NW, bool GATED>
+struct PairDma {
+    static constexpr int ROW2 = 128;                          // bytes per tile row
+    static constexpr int STAGE2 = (BM + BN) * ROW2;
+    static constexpr int N2 = STAGE2 / 1024, A2 = BM * ROW2 / 1024;
+    static_assert(N2 % NW == 0, "each wave issues the same number of DMA instructions");
+    static constexpr int PW2 = N2 / NW;                       // instructions per wave and stage
+    static constexpr uint32_t SENT = 0x80000000u;
+    uint32_t off[PW2];
+    const uint16_t* a_tile;
+    const uint16_t* b_tile;
+    int wid;
+
+    __device__ __forceinline__ PairDma(const GemmArgs& p, int64_t m0, int64_t n0, int wid_, int lane)
+        : a_tile(p.A + m0 * p.K), b_tile(p.B + n0 * p.K), wid(wid_) {
+#pragma unroll
+        for (int q = 0; q < PW2; ++q) {
+            const int j = wid * PW2 + q;
+            const int r = j * 8 + (lane >> 3);                // tile row; (r >> 1) & 7 = (4 (j & 1) + (lane >> 4)) & 7
+            const int c = (lane & 7) ^ ((4 * (j & 1) + (lane >> 4)) & 7);
+            off[q] = SENT;
+            if (j < A2) {
+                if (m0 + r < p.M) off[q] = (uint32_t)(((int64_t)r * p.K + c * 8) * 2);
+            } else {
+                const int lr = r - BM;
+                int64_t gb;
+                bool ok;
+                if (GATED) {
+                    const int half = BN / 2;
+                    const int64_t cc = n0 + (lr < half ? lr : lr - half);
+                    ok = cc < p.N;
+                    gb = lr < half ? cc : p.N + cc;
+                } else {
+                    gb = n0 + lr;
+                    ok = gb < p.Nb;
+                }
+                if (ok) off[q] = (uint32_t)(((gb - n0) * p.K + c * 8) * 2);
+            }
+        }
+    }
+
+    // stage K = k0 .. k0 + 63 into the STAGE2 bytes at buf
+    __device__ __forceinline__ void issue(int64_t k0, uint8_t* buf) const {
+        __amdgpu_buffer_rsrc_t rsa =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+        __amdgpu_buffer_rsrc_t rsb =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < PW2; ++q) {
+            const int j = wid * PW2 + q;
+            const uint32_t o = off[q];
+            auto* dst = (__attribute__((address_space(3))) void*)(buf + j * 1024);
+            if (j < A2)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, o, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, o, 0, 0, 0);
+        }
+    }
+};
+
+// s_waitcnt immediate for vmcnt(n) with lgkmcnt and expcnt left alone
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+
+// Epilogue of the direct-to-LDS kernels (16x16 blocks, acc[i][j]: weight
+// block i, token block j; lane l holds rows (output columns)
+// b_row(i) + 4 (l >> 4) + q of column (token) wm WTM + 16 j + (l & 15)).
+// A balanced-last-round K piece goes to the fp32 tail workspace in B-row
+// order; otherwise the tile goes through the epilogue (fp32 rows staged
+// through LDS when the output allows 16-byte stores).
+template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void pipe_epilogue(const GemmArgs& p, bool tail, f32x4 (&acc)[BN / WN / 16][BM / WM / 16],
+                                              uint8_t* lds, int64_t m0, int64_t n0, int wm, int wn, int lane) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    constexpr bool GATED = EPI == EPI_GATED_BF16;
+    const int mrow = lane & 15, ncol = 4 * (lane >> 4);
+    if (tail) {
+        float* t = p.tail_ws + (int64_t)(blockIdx.x - p.full_tiles) * BM * BN;
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const int lm = wm * WTM + j * 16 + mrow;
+                const int ln = b_tile_row_of<BN, WN, GATED, 16>(i, wn) + ncol;
+                *reinterpret_cast<float4*>(t + lm * BN + ln) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        return;
+    }
+    // (the staged store's slot swizzle needs BN / 4 a power of two)
+    if constexpr (EPI == EPI_STORE_F32 && (BN & (BN - 1)) == 0) {
+        if (p.vec_out) {
+            staged_store_f32<BM, BN, WM, WN>(p, acc, lds, m0, n0, wm, wn, lane);
+            return;
+        }
+    }
+    // bf16 tile wholly inside the output (no bias): 8-byte stores without
+    // per-element checks, one row address per token block and the column
+    // offsets as immediates
+    if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_GATED_BF16) {
+        constexpr int COLS = GATED ? BN / 2 : BN;
+        if (p.vec_out && !(EPI == EPI_STORE_BF16 && p.bias) && m0 + BM <= p.M && n0 + COLS <= p.N) {
+            uint16_t* const C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                uint16_t* row = C + (m0 + wm * WTM + j * 16 + mrow) * p.N + n0 + ncol;
+#pragma unroll
+                for (int i = 0; i < (GATED ? TN / 2 : TN); ++i) {
+                    float v[4];
+                    int col;
+                    if (GATED) {
+                        col = wn * (WTN / 2) + i * 16;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = silu_mul(acc[i][j][q], acc[i + TN / 2][j][q]);
+                    } else {
+                        col = b_tile_row_of<BN, WN, false, 16>(i, wn);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q];
+                    }
+                    *reinterpret_cast<uint2*>(row + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+        const int64_t gm = m0 + wm * WTM + j * 16 + mrow;
+        if (gm >= p.M) continue;
+        if (GATED) {
+#pragma unroll
+            for (int i = 0; i < TN / 2; ++i) {
+                const int64_t gn = n0 + wn * (WTN / 2) + i * 16 + ncol;
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = silu_mul(acc[i][j][q], acc[i + TN / 2][j][q]);
+                store4<EPI>(p, gm, gn, v);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const int64_t gn = n0 + b_tile_row_of<BN, WN, GATED, 16>(i, wn) + ncol;
+                float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                store4<EPI>(p, gm, gn, v);
+            }
+        }
+    }
+}
+
 // Deep-pipelined direct-to-LDS kernel with 16x16x32 MFMAs (16-byte-aligned
 // operands, K a multiple of 8), for the 256 x 256 tiles.  PAIR (every K
 // range a multiple of 64) replaces the four single stages below by two
@@ -907,64 +1065,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
         // each multiplied as two K steps of 32 (h = 0, 1).  A DMA instruction
         // then fetches 8 rows x 128 contiguous bytes: whole 128-byte lines,
         // half the L1 -> L2 requests of the 64-byte rows of single stages.
-        //   * chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16
-        //     rows of one fragment read fall in 16 distinct 16-byte bank
-        //     groups (rows alternate between the two 128-byte halves of the
-        //     256 bytes the 64 banks cover);
+        //   * the chunk layout and the DMA are those of PairDma;
         //   * pair q + 1 is DMA'd into the other buffer from the middle of
         //     step 2q - 1 (once every wave holds pair q - 1's last
         //     fragments) and certified in the middle of step 2q + 1, two K
         //     steps later; one barrier per pair;
         //   * fragments of step s + 1 are read under the MFMAs of step s.
-        constexpr int ROW2 = 2 * ROWB;                       // 128 bytes
-        constexpr int STAGE2 = (BM + BN) * ROW2;
+        using Dma = PairDma<BM, BN, NW, GATED>;
+        constexpr int ROW2 = Dma::ROW2;                      // 128 bytes
+        constexpr int STAGE2 = Dma::STAGE2;
         static_assert(2 * STAGE2 <= NST * STAGE, "two pair buffers fit the ring");
-        constexpr int N2 = STAGE2 / 1024, A2 = BM * ROW2 / 1024;
-        static_assert(N2 % NW == 0, "each wave issues the same number of DMA instructions");
-        constexpr int PW2 = N2 / NW;
-        uint32_t off2[PW2];
-#pragma unroll
-        for (int q = 0; q < PW2; ++q) {
-            const int j = wid * PW2 + q;
-            const int r = j * 8 + (lane >> 3);                // tile row; (r >> 1) & 7 = (4 (j & 1) + (lane >> 4)) & 7
-            const int c = (lane & 7) ^ ((4 * (j & 1) + (lane >> 4)) & 7);
-            off2[q] = SENT;
-            if (j < A2) {
-                if (m0 + r < p.M) off2[q] = (uint32_t)(((int64_t)r * p.K + c * 8) * 2);
-            } else {
-                const int lr = r - BM;
-                int64_t gb;
-                bool ok;
-                if (GATED) {
-                    const int half = BN / 2;
-                    const int64_t cc = n0 + (lr < half ? lr : lr - half);
-                    ok = cc < p.N;
-                    gb = lr < half ? cc : p.N + cc;
-                } else {
-                    gb = n0 + lr;
-                    ok = gb < p.Nb;
-                }
-                if (ok) off2[q] = (uint32_t)(((gb - n0) * p.K + c * 8) * 2);
-            }
-        }
-        const uint16_t* a_tile = p.A + m0 * p.K;
-        const uint16_t* b_tile = p.B + n0 * p.K;
-        auto issue_pair = [&](int64_t k0, int buf) {
-            __amdgpu_buffer_rsrc_t rsa =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(a_tile + k0), (short)0, 0x7fffffff, 0x00020000);
-            __amdgpu_buffer_rsrc_t rsb =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(b_tile + k0), (short)0, 0x7fffffff, 0x00020000);
-#pragma unroll
-            for (int q = 0; q < PW2; ++q) {
-                const int j = wid * PW2 + q;
-                const uint32_t o = off2[q];
-                auto* dst = (__attribute__((address_space(3))) void*)(lds + buf * STAGE2 + j * 1024);
-                if (j < A2)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, o, 0, 0, 0);
-                else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, o, 0, 0, 0);
-            }
-        };
+        constexpr int PW2 = Dma::PW2;
+        const Dma dma(p, m0, n0, wid, lane);
+        auto issue_pair = [&](int64_t k0, int buf) { dma.issue(k0, lds + buf * STAGE2); };
         // fragment reads: lane l reads row l & 15 of a 16-row block, chunk
         // 4 h + (l >> 4), at its swizzled position
         const int lrow = lane & 15;
@@ -994,7 +1107,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
             issue_pair(k_begin, 0);
             if (np > 1) issue_pair(k_begin + 64, 1);
             if (np > 1)
-                __builtin_amdgcn_s_waitcnt(0x0f70 | (PW2 & 15) | ((PW2 >> 4) << 14));
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(PW2));
             else
                 __builtin_amdgcn_s_waitcnt(0x0f70);
             bare_barrier();
@@ -1189,51 +1302,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_pipe_kernel(GemmArgs p
 
     }  // single stages
 
-    // results: block (i, j), lane l: rows (output columns) b_row(i) + 4 (l >> 4)
-    // + q, column (token) wm WTM + 16 j + (l & 15)
-    const int mrow = lane & 15, ncol = 4 * (lane >> 4);
-    if (u.tail) {
-        float* t = p.tail_ws + (int64_t)(blockIdx.x - p.full_tiles) * BM * BN;
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-#pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const int lm = wm * WTM + j * 16 + mrow;
-                const int ln = b_tile_row_of<BN, WN, GATED, 16>(i, wn) + ncol;
-                *reinterpret_cast<float4*>(t + lm * BN + ln) =
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-            }
-        return;
-    }
-    // (the staged store's slot swizzle needs BN / 4 a power of two)
-    if constexpr (EPI == EPI_STORE_F32 && (BN & (BN - 1)) == 0) {
-        if (p.vec_out) {
-            staged_store_f32<BM, BN, WM, WN>(p, acc, lds, m0, n0, wm, wn, lane);
-            return;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-        const int64_t gm = m0 + wm * WTM + j * 16 + mrow;
-        if (gm >= p.M) continue;
-        if (GATED) {
-#pragma unroll
-            for (int i = 0; i < TN / 2; ++i) {
-                const int64_t gn = n0 + wn * (WTN / 2) + i * 16 + ncol;
-                float v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = silu_mul(acc[i][j][q], acc[i + TN / 2][j][q]);
-                store4<EPI>(p, gm, gn, v);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const int64_t gn = n0 + b_tile_row_of<BN, WN, GATED, 16>(i, wn) + ncol;
-                float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-                store4<EPI>(p, gm, gn, v);
-            }
-        }
-    }
+    pipe_epilogue<BM, BN, WM, WN, EPI>(p, u.tail, acc, lds, m0, n0, wm, wn, lane);
 }
 
 // Adds the split-K partial sums in split order and applies the epilogue.
@@ -2122,11 +2191,6 @@ static TileCfg tile_cfg(int k) {
     }
 }
 
-static size_t lds_bytes(int k) {
-    TileCfg c = tile_cfg(k);
-    return (size_t)2 * (c.bm + c.bn) * 64 * sizeof(uint16_t);
-}
-
 // Workgroups of the direct-to-LDS kernel resident on one CU: its LDS ring
 // (2 buffers of BM + BN rows of 144 bytes) against the CU's 160 KiB.
 static int64_t wgs_per_cu(int k) {
@@ -2146,11 +2210,6 @@ static void tiles_for(int kern, int64_t M, int64_t N, bool gated, int& tm, int& 
     tm = (int)ceil_div(M, c.bm);
     tn = (int)(gated ? ceil_div(N, c.bn / 2) : ceil_div(N, c.bn));
 }
-
-// 256x256 tiles run as 8 waves of 128x64 (two waves per SIMD hide each
-// other's LDS and barrier waits; 4 waves of 128x128 would need more than
-// the 256 architectural VGPRs for the accumulators and spill).
-static int huge_kernel() { return K_BF16_HUGE8; }
 
 // CUs of an MI355X: the weight-streaming kernel runs one workgroup on each
 constexpr int kStreamWGs = 256;
@@ -2208,7 +2267,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     }
     if (M > 64) {
         tiles_for(K_BF16_HUGE8, M, N, gated, tm, tn);
-        pl.kernel = (int64_t)tm * tn >= 512 ? huge_kernel() : K_BF16_LARGE;
+        pl.kernel = (int64_t)tm * tn >= 512 ? K_BF16_HUGE8 : K_BF16_LARGE;
         // fewer 256 x 256 tiles than two rounds: 128 x 192 tiles on the
         // paired-stage kernel when they fill at least three quarters of the
         // CUs (the QKV projection at TP=16: 8192 x 768 = 256 tiles, one per

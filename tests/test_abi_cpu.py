@@ -66,9 +66,13 @@ def test_workspace_queries():
     # large-M shapes whose tiles fill whole rounds need no workspace
     # (8192 x 8192 in 256 x 256 tiles at one workgroup per CU: 1024 = 4 x 256)
     assert T.tp_linear_workspace_bytes(8192, 3584, 8192, torch.bfloat16) == 0
-    # 8192 x 3584 in 128 x 128 tiles at two per CU: 1792 = 3 x 512 + 256, the
+    # 8192 x 3584 (448 tiles of 256 x 256, under two rounds): 128 x 192 tiles,
+    # 64 x 19 = 1216 = 4 x 256 + 192, whole K per tile, no workspace
+    assert T.tp_linear_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 0
+    # gated 8192 -> 1792 (gated products never take 128 x 192 tiles): 128 x 128
+    # tiles of 64 act columns at two per CU, 64 x 28 = 1792 = 3 x 512 + 256, the
     # last 256 tiles cut into two K pieces of 4096 (fp32 128 x 128 partials)
-    assert T.tp_linear_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 256 * 2 * 128 * 128 * 4
+    assert T.tp_gate_up_workspace_bytes(8192, 8192, 1792, torch.bfloat16) == 256 * 2 * 128 * 128 * 4
     # 896 gated tiles = 3 rounds + 128: the last 128 tiles are cut into two
     # K pieces each, whose fp32 256 x 256 partial tiles need a workspace
     assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 128 * 2 * 256 * 256 * 4
