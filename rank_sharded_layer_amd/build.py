@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtpshard.so")
 
-SOURCES = ["abi.hip", "gemm.hip", "reduce.hip", "embed.hip", "shard.hip", "spnorm.hip", "gather.hip", "attn.hip", "load.hip"]
+SOURCES = ["abi.hip", "gemm.hip", "gemm_f32.hip", "reduce.hip", "embed.hip", "shard.hip", "spnorm.hip", "gather.hip", "attn.hip", "load.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

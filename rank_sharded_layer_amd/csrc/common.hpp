@@ -100,4 +100,8 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* A, const void* B, const
                        void* C, int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt,
                        tp_dtype out_dt, void* ws, hipStream_t s);
 
+// the fp32 products (gemm_f32.hip), no workspace
+hipError_t launch_gemm_f32(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
+                           int64_t K, bool gated, hipStream_t s);
+
 }  // namespace tpk

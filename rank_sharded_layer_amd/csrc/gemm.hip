@@ -24,7 +24,7 @@
 //     of tiles, grouped GROUP_M tiles tall so that the weight tile and the
 //     activation tiles a run shares stay in that XCD's L2.
 //
-// fp32 path: VALU FMA tiles (no reduced-precision fp32 modes).
+// The fp32 kernels are in gemm_f32.hip.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -39,8 +39,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GATED_BF16 = 2, EPI_SPLIT = 3,
-           EPI_GATED_F32 = 4 };
+enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GATED_BF16 = 2, EPI_SPLIT = 3 };
 
 struct GemmArgs {
     const uint16_t* A;      // [M, K]
@@ -1871,257 +1870,6 @@ __global__ __launch_bounds__(256) void rs_finalize_kernel(RsOp o, GemmArgs out) 
     store4<EPI>(out, m, j, v);
 }
 
-// ---- fp32 VALU GEMM -----------------------------------------------------
-
-struct F32Args {
-    const float* A;
-    const float* B;
-    const float* bias;
-    float* C;
-    int64_t M, N, K, Nb;
-    int tiles_m, tiles_n;
-};
-
-// 64 x 64 B-row tile (gated: 32 gate + the same 32 up rows), BK = 16, 256
-// threads each computing 4 rows x 4 B-columns; a thread's columns are
-// {2tx, 2tx+1, 32+2tx, 33+2tx} so that, gated, its gate and up values meet.
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args p) {
-    constexpr int TMT = 64, TNT = 64, BK = 16;
-    constexpr bool GATED = EPI == EPI_GATED_F32;
-    __shared__ float As[BK][TMT + 4];
-    __shared__ float Bs[BK][TNT + 4];
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int tile_m = blockIdx.x / p.tiles_n, tile_n = blockIdx.x % p.tiles_n;
-    const int64_t m0 = (int64_t)tile_m * TMT;
-    const int64_t n0 = GATED ? (int64_t)tile_n * (TNT / 2) : (int64_t)tile_n * TNT;
-    float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int v = tid + i * 256;
-            const int row = v / BK, kk = v % BK;
-            const int64_t gm = m0 + row, k = k0 + kk;
-            As[kk][row] = (gm < p.M && k < p.K) ? p.A[gm * p.K + k] : 0.0f;
-            int64_t gb;
-            bool ok;
-            if (GATED) {
-                const int64_t c = n0 + (row < 32 ? row : row - 32);
-                ok = c < p.N;
-                gb = row < 32 ? c : p.N + c;
-            } else {
-                gb = n0 + row;
-                ok = gb < p.Nb;
-            }
-            Bs[kk][row] = (ok && k < p.K) ? p.B[gb * p.K + k] : 0.0f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < BK; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][(j >> 1) * 32 + tx * 2 + (j & 1)];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t gr = m0 + ty * 4 + i;
-        if (gr >= p.M) continue;
-        if (GATED) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t gc = n0 + tx * 2 + j;
-                if (gc < p.N) p.C[gr * p.N + gc] = silu_mul(acc[i][j], acc[i][j + 2]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t gc = n0 + (j >> 1) * 32 + tx * 2 + (j & 1);
-                if (gc < p.N) p.C[gr * p.N + gc] = acc[i][j] + (p.bias ? p.bias[gc] : 0.0f);
-            }
-        }
-    }
-}
-
-// fp32, few tokens (M <= 32): each wave owns RW weight rows (gated: RW/2
-// gate rows and the same up rows) for all M tokens; lane l takes k = l,
-// l+64, ... and keeps M x RW fp32 partial dot products (sequential FMAs);
-// the 64 lanes' partials are then added in lane order through LDS
-// (deterministic).  Launch-latency-sized problems get ~N/RW waves.
-template <bool GATED, int MT>
-__global__ __launch_bounds__(256) void gemm_f32_small_kernel(F32Args p) {
-    constexpr int RW = 4;                       // B rows per wave
-    constexpr int NW = 4;                       // waves per workgroup
-    __shared__ float red[NW][MT * RW][65];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // this wave's B rows
-    const int64_t unit = (int64_t)blockIdx.x * NW + w;     // RW/2 act columns (gated) or RW rows
-    int64_t brow[RW];
-    bool bok[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-        if (GATED) {
-            const int64_t c = unit * (RW / 2) + (r % (RW / 2));
-            bok[r] = c < p.N;
-            brow[r] = r < RW / 2 ? c : p.N + c;
-        } else {
-            brow[r] = unit * RW + r;
-            bok[r] = brow[r] < p.Nb;
-        }
-    }
-    float acc[MT][RW];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < RW; ++r) acc[m][r] = 0.0f;
-    for (int64_t k = lane; k < p.K; k += 64) {
-        float wv[RW];
-#pragma unroll
-        for (int r = 0; r < RW; ++r) wv[r] = bok[r] ? p.B[brow[r] * p.K + k] : 0.0f;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const float xv = m < p.M ? p.A[(int64_t)m * p.K + k] : 0.0f;
-#pragma unroll
-            for (int r = 0; r < RW; ++r) acc[m][r] = fmaf(xv, wv[r], acc[m][r]);
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < RW; ++r) red[w][m * RW + r][lane] = acc[m][r];
-    __syncthreads();
-    // lane e of wave w finishes value e (m = e / RW, r = e % RW) of this wave
-    for (int e = lane; e < MT * RW; e += 64) {
-        float v = 0.0f;
-        for (int l = 0; l < 64; ++l) v = v + red[w][e][l];
-        red[w][e][64] = v;
-    }
-    __syncthreads();
-    for (int e = lane; e < MT * RW; e += 64) {
-        const int m = e / RW, r = e % RW;
-        if (m >= p.M) continue;
-        if (GATED) {
-            if (r >= RW / 2) continue;
-            const int64_t c = unit * (RW / 2) + r;
-            if (c < p.N) p.C[(int64_t)m * p.N + c] = silu_mul(red[w][e][64], red[w][m * RW + r + RW / 2][64]);
-        } else {
-            const int64_t c = unit * RW + r;
-            if (c < p.N) p.C[(int64_t)m * p.N + c] = red[w][e][64] + (p.bias ? p.bias[c] : 0.0f);
-        }
-    }
-}
-
-// fp32, few tokens (M <= 32, K <= 2048, 16-byte rows): one workgroup of 16
-// waves per 16 output columns (gated: the 16 gate rows and the same 16 up
-// rows), the waves splitting K into 16 ranges of STEPS x 16.  Per 16 K
-// values a lane loads 16 bytes of its weight row (row l & 15, K values
-// 4 (l >> 4) .. +3) and 16 bytes of its token row, and the four K values go
-// in order to four v_mfma_f32_16x16x4_f32 (fp32 products and sums, no
-// reduced-precision inputs).  Every load of a wave is issued before its
-// first MFMA: the whole product is one round trip to memory per wave.  The
-// 16 waves' sums meet in LDS and are added in wave (= K) order, so the
-// result is deterministic.
-constexpr int F32W = 16;
-
-template <bool GATED, int TB, int STEPS>
-__global__ __launch_bounds__(F32W * 64) void gemm_f32_mfma_kernel(F32Args p) {
-    constexpr int RB = GATED ? 2 : 1;
-    typedef float f4v __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) f32x4 red[F32W][RB][TB][64];
-    const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r16 = lane & 15, kq = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t kbeg = (int64_t)wid * STEPS * 16 + kq * 4;
-    const float* wrow[RB];
-    bool wok[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        wok[rb] = n0 + r16 < p.N;
-        wrow[rb] = p.B + ((rb == 0 ? 0 : p.N) + n0 + r16) * p.K;
-    }
-    const float* xrow[TB];
-    bool xok[TB];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        xok[tb] = tb * 16 + r16 < p.M;
-        xrow[tb] = p.A + (int64_t)(tb * 16 + r16) * p.K;
-    }
-    f4v w[STEPS][RB], x[STEPS][TB];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const int64_t k = kbeg + s * 16;
-        const bool kin = k < p.K;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-            w[s][rb] = (kin && wok[rb]) ? *reinterpret_cast<const f4v*>(wrow[rb] + k) : (f4v){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-            x[s][tb] = (kin && xok[tb]) ? *reinterpret_cast<const f4v*>(xrow[tb] + k) : (f4v){0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    f32x4 acc[RB][TB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[rb][tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb)
-                    acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[s][rb][e], x[s][tb][e], acc[rb][tb], 0, 0, 0);
-    // lane l of block (rb, tb) holds weight rows 4 (l >> 4) .. +3 of the
-    // block for token 16 tb + (l & 15)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) red[wid][rb][tb][lane] = acc[rb][tb];
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t >= TB * 64) return;
-    const int tb = t >> 6, l = t & 63;
-    f32x4 v0 = red[0][0][tb][l];
-#pragma unroll
-    for (int wv = 1; wv < F32W; ++wv) v0 = v0 + red[wv][0][tb][l];
-    float v[4];
-    if constexpr (GATED) {
-        f32x4 v1 = red[0][RB - 1][tb][l];
-#pragma unroll
-        for (int wv = 1; wv < F32W; ++wv) v1 = v1 + red[wv][RB - 1][tb][l];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = silu_mul(v0[e], v1[e]);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = v0[e];
-    }
-    const int64_t m = tb * 16 + (l & 15);
-    const int64_t c0 = n0 + 4 * (l >> 4);
-    if (m >= p.M || c0 >= p.N) return;
-    float* dst = p.C + m * p.N + c0;
-    if (!GATED && p.bias) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (c0 + e < p.N) v[e] = v[e] + p.bias[c0 + e];
-    }
-    if (c0 + 3 < p.N && ((p.N & 3) == 0) && ((((uintptr_t)p.C) & 15u) == 0)) {
-        *reinterpret_cast<f4v*>(dst) = (f4v){v[0], v[1], v[2], v[3]};
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (c0 + e < p.N) dst[e] = v[e];
-    }
-}
-
 // Finishes the tiles of a balanced last round: adds each tile's K pieces in
 // piece order and applies the epilogue (gated SiLU(g)*u, or store + bias).
 // One thread per 4 consecutive output columns of a tile row (float4 reads).
@@ -2447,55 +2195,7 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
                        void* ws, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int64_t Nb = gated ? 2 * N : N;
-    if (pl.kernel == K_F32) {
-        int tm, tn;
-        tiles_for(K_F32, M, N, gated, tm, tn);
-        F32Args a{static_cast<const float*>(A), static_cast<const float*>(B),
-                  static_cast<const float*>(bias), static_cast<float*>(C), M, N, K, Nb, tm, tn};
-        const bool f32_vec = (K % 4) == 0 && (((uintptr_t)A | (uintptr_t)B) & 15u) == 0;
-        if (M <= 32 && f32_vec && K <= 16 * 16 * 8) {
-            // one 16-wave workgroup per 16 output columns, STEPS x 16 K per wave
-            const int steps = (int)ceil_div(K, 16 * F32W);
-            const dim3 g((unsigned)ceil_div(N, 16));
-#define F32M_LAUNCH(G_, TB_)                                                                             \
-    switch (steps) {                                                                                     \
-        case 1: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 1>), g, dim3(F32W * 64), 0, s, a); break; \
-        case 2: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 2>), g, dim3(F32W * 64), 0, s, a); break; \
-        case 3: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 3>), g, dim3(F32W * 64), 0, s, a); break; \
-        case 4: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 4>), g, dim3(F32W * 64), 0, s, a); break; \
-        case 5: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 5>), g, dim3(F32W * 64), 0, s, a); break; \
-        case 6: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 6>), g, dim3(F32W * 64), 0, s, a); break; \
-        case 7: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 7>), g, dim3(F32W * 64), 0, s, a); break; \
-        default: hipLaunchKernelGGL((gemm_f32_mfma_kernel<G_, TB_, 8>), g, dim3(F32W * 64), 0, s, a); break; \
-    }
-            if (gated) {
-                if (M <= 16) { F32M_LAUNCH(true, 1) } else { F32M_LAUNCH(true, 2) }
-            } else {
-                if (M <= 16) { F32M_LAUNCH(false, 1) } else { F32M_LAUNCH(false, 2) }
-            }
-#undef F32M_LAUNCH
-            return hipGetLastError();
-        }
-        if (M <= 32) {
-            // 4 waves per workgroup, 4 B rows (gated: 2 act columns) per wave
-            const int64_t units = gated ? ceil_div(N, 2) : ceil_div(N, 4);
-            dim3 g((unsigned)ceil_div(units, 4));
-            if (gated) {
-                if (M <= 16) hipLaunchKernelGGL((gemm_f32_small_kernel<true, 16>), g, dim3(256), 0, s, a);
-                else hipLaunchKernelGGL((gemm_f32_small_kernel<true, 32>), g, dim3(256), 0, s, a);
-            } else {
-                if (M <= 16) hipLaunchKernelGGL((gemm_f32_small_kernel<false, 16>), g, dim3(256), 0, s, a);
-                else hipLaunchKernelGGL((gemm_f32_small_kernel<false, 32>), g, dim3(256), 0, s, a);
-            }
-            return hipGetLastError();
-        }
-        dim3 grid((unsigned)(tm * tn));
-        if (gated)
-            hipLaunchKernelGGL(gemm_f32_kernel<EPI_GATED_F32>, grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE_F32>, grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
+    if (pl.kernel == K_F32) return launch_gemm_f32(A, B, bias, C, M, N, K, gated, s);
     const bool vec = (K % 8) == 0 && (((uintptr_t)A | (uintptr_t)B) & 15u) == 0;
     if (pl.kernel == K_BF16_RS) {
         if (!vec || !ws || (((uintptr_t)ws) & 15u) != 0) {

@@ -28,6 +28,7 @@ benchmark times):
   o_proj (TP=16)    8192 x  512 -> 8192       256x256 paired-stage tiles, K = 512
   LM head (TP=2)     512 x 1024 -> 75968 fp32 256x256 tiles, fp32 rows staged through LDS
   fp32 MLP (TP=2)     16 x 1024 -> 2 x 1536, 16 x 1536 -> 1024   fp32 small-M kernels
+                      (8 act columns, and 4 output columns, per workgroup)
 and the kernels other shapes take: the register-streaming kernel at
 narrower outputs, the LDS-ring streaming decode kernel with its finish
 pass, 64x128 split-K
@@ -162,6 +163,32 @@ def test_fp32_small_m_kernels_bit_exact():
     down = synth.normal((w.h, fl), 0.02, w.seed(synth.T_DOWN), torch.float32, device=DEV)
     y = T.tp_linear_rank_forward(xd, down)
     assert np.array_equal(bits(y), np.ascontiguousarray(bits(down)[:, jd].T))
+
+
+@pytest.mark.parametrize("m,k,n,gated", [
+    (16, 1024, 1000, False),    # 4 columns per workgroup, ragged last block
+    (20, 100, 2100, False),     # 8 columns, two token blocks, one K step per wave
+    (16, 512, 4200, False),     # 16 columns
+    (16, 1024, 100, True),      # gated, 8 act columns (8 gate + 8 up rows), ragged
+    (32, 2048, 4100, True),     # gated, 16 act columns (two row blocks), two token blocks
+])
+def test_fp32_small_m_column_blocks_bit_exact(m, k, n, gated):
+    """The fp32 small-M kernel at every column-block width it takes (16, 8
+    or 4 output columns per workgroup) with ragged edges: one-hot tokens
+    make each output a single exact product."""
+    x, j = one_hot_rows(m, k, torch.float32, salt=5)
+    if gated:
+        gate = gate_values(n, k, torch.float32)
+        up = synth.normal((n, k), 0.02, 409, torch.float32, device=DEV)
+        y = T.tp_gate_up_act_rank(x, torch.cat([gate, up], 0).contiguous())
+        ref = gate.cpu().numpy()[:, j].T * up.cpu().numpy()[:, j].T
+    else:
+        w = synth.normal((n, k), 0.02, 410, torch.float32, device=DEV)
+        y = T.tp_linear_rank_forward(x, w)
+        ref = np.ascontiguousarray(w.cpu().numpy()[:, j].T)
+    torch.cuda.synchronize()
+    bad = np.argwhere(bits(y) != np.ascontiguousarray(ref, dtype=np.float32).view(np.uint32))
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
 # ---- kernels of other decode-sized shapes ---------------------------------------
