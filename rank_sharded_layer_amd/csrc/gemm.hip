@@ -1916,7 +1916,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs p, int BM, int
 // ---- planning -------------------------------------------------------------
 
 enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_BF16_DEC4 = 6,
-            K_BF16_STREAM = 7, K_BF16_RS = 8, K_BF16_MID = 9 };
+            K_BF16_STREAM = 7, K_BF16_RS = 8, K_BF16_MID = 9, K_BF16_W192 = 10 };
 
 // Tile configurations (BM tokens x BN weight rows):
 //   HUGE8 256x256, 2x4 waves of 128x64 (prefill-sized problems; deep-pipelined
@@ -1926,6 +1926,8 @@ enum Kern { K_F32 = 0, K_BF16_LARGE = 1, K_BF16_SMALL = 2, K_BF16_HUGE8 = 4, K_B
 //   DEC4   64x128, 1x4 waves of 64x32, deep-pipelined 16x16x32 kernel (decode,
 //          M <= 64; same tiling as SMALL, which serves it when the operands
 //          do not allow direct-to-LDS loads)
+//   W192  256x192, 2x4 waves of 128x48, paired stages, K split in two
+//          (few output columns with long K: the QKV projection at TP=16)
 //   STREAM 64x128 weight-streaming persistent kernel (decode, M <= 64, large
 //          weights): one workgroup per CU over equal ranges of (tile, K chunk)
 struct TileCfg { int bm, bn, wm, wn; };
@@ -1935,6 +1937,7 @@ static TileCfg tile_cfg(int k) {
         case K_BF16_SMALL: return TileCfg{64, 128, 1, 2};
         case K_BF16_DEC4: return TileCfg{64, 128, 1, 4};
         case K_BF16_MID: return TileCfg{128, 192, 2, 4};
+        case K_BF16_W192: return TileCfg{256, 192, 2, 4};
         default: return TileCfg{128, 128, 2, 2};
     }
 }
@@ -2020,6 +2023,25 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
         // paired-stage kernel when they fill at least three quarters of the
         // CUs (the QKV projection at TP=16: 8192 x 768 = 256 tiles, one per
         // CU, where 128 x 128 tiles left a quarter of a round empty)
+        //
+        // Before that, for long K: 256 x 192 tiles with K split in two when
+        // the two halves make one round that fills at least three quarters
+        // of the CUs.  Per flop they move 0.70x the operand bytes of 128 x 192
+        // tiles from L2 to LDS, and these launches run at the L2 -> LDS rate
+        // (~10 TB/s over all CUs); the two fp32 halves are added in order by
+        // the split finish pass.
+        if (pl.kernel == K_BF16_LARGE && !gated && K % 128 == 0 && K >= 4096) {
+            int wm, wn;
+            tiles_for(K_BF16_W192, M, N, gated, wm, wn);
+            const int64_t wt = (int64_t)wm * wn;
+            if (2 * wt <= 256 && 2 * wt >= 192) {
+                pl.kernel = K_BF16_W192;
+                pl.splits = 2;
+                pl.k_split = K / 2;
+                pl.ws_bytes = (size_t)2 * (size_t)M * (size_t)N * sizeof(float);
+                return pl;
+            }
+        }
         if (pl.kernel == K_BF16_LARGE && !gated && K % 64 == 0) {
             int mm, mn;
             tiles_for(K_BF16_MID, M, N, gated, mm, mn);
@@ -2127,9 +2149,9 @@ static void launch_pipe_one(const GemmArgs& a, int splits, hipStream_t s) {
     const int units = a.tail_split > 1 ? a.full_tiles + (ntiles - a.full_tiles) * a.tail_split : ntiles;
     dim3 grid((unsigned)units, (unsigned)splits);
     const bool kt32 = (a.K % 32) != 0 || (a.k_split % 32) != 0;
-    if constexpr (BM == 128 && BN == 192) {
-        // paired stages only (the planner takes these tiles for K a
-        // multiple of 64, without split-K or tail pieces)
+    if constexpr (BN == 192) {
+        // paired stages only (the planner takes these tiles for K ranges
+        // that are multiples of 64, without tail pieces)
         hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false, true>), grid, dim3(WM * WN * 64), 0, s, a);
         return;
     } else {
@@ -2166,9 +2188,9 @@ static void launch_epi(int epi, const GemmArgs& a, int splits, hipStream_t s) {
         case EPI_STORE_BF16: launch_one<L, BM, BN, WM, WN, EPI_STORE_BF16>(a, splits, s); break;
         case EPI_STORE_F32: launch_one<L, BM, BN, WM, WN, EPI_STORE_F32>(a, splits, s); break;
         case EPI_GATED_BF16:
-            // 128 x 192 tiles hold an odd number of 16-row blocks per wave:
+            // 192-column tiles hold an odd number of 16-row blocks per wave:
             // the planner never gives them gated products
-            if constexpr (!(BM == 128 && BN == 192)) launch_one<L, BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, s);
+            if constexpr (BN != 192) launch_one<L, BM, BN, WM, WN, EPI_GATED_BF16>(a, splits, s);
             break;
         default: launch_one<L, BM, BN, WM, WN, EPI_SPLIT>(a, splits, s); break;
     }
@@ -2184,6 +2206,7 @@ static void launch_bf16_kern(int kern, int epi, const GemmArgs& a, int splits, b
     switch (kern) {
         case K_BF16_HUGE8: launch_epi<L_PIPE, 256, 256, 2, 4>(epi, a, splits, s); break;
         case K_BF16_MID: launch_epi<L_PIPE, 128, 192, 2, 4>(epi, a, splits, s); break;
+        case K_BF16_W192: launch_epi<L_PIPE, 256, 192, 2, 4>(epi, a, splits, s); break;
         case K_BF16_DEC4:
         case K_BF16_SMALL: launch_epi<L_PIPE, 64, 128, 1, 4>(epi, a, splits, s); break;
         default: launch_epi<L_DL, 128, 128, 2, 2>(epi, a, splits, s); break;
@@ -2294,15 +2317,19 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
     a.K = K;
     a.Nb = Nb;
     a.k_split = pl.splits > 1 ? pl.k_split : K;
+    // operands the 16-byte loads cannot serve take the element-wise kernel,
+    // 128 x 128 tiles in place of the direct-to-LDS ones
+    const bool dma_tiles = pl.kernel == K_BF16_HUGE8 || pl.kernel == K_BF16_MID || pl.kernel == K_BF16_W192;
+    const int kern = (!vec && dma_tiles) ? K_BF16_LARGE : pl.kernel;
     if (pl.splits > 1) {
         // split partials are kept in B-row coordinates over all Nb rows
-        TileCfg c = tile_cfg(pl.kernel);
+        TileCfg c = tile_cfg(kern);
         a.tiles_m = (int)ceil_div(M, c.bm);
         a.tiles_n = (int)ceil_div(Nb, c.bn);
         a.N = Nb;
         a.C = ws;
         a.vec_out = (Nb % 4) == 0 && (((uintptr_t)ws) & 15u) == 0;
-        launch_bf16_kern(pl.kernel, EPI_SPLIT, a, pl.splits, vec, s);
+        launch_bf16_kern(kern, EPI_SPLIT, a, pl.splits, vec, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         int64_t blocks = ceil_div(M * N, 256);
@@ -2321,9 +2348,6 @@ hipError_t launch_gemm(const GemmPlan& pl, const void* A, const void* B, const v
                                wsf, pl.splits, M, N, Nb, bb, C);
         return hipGetLastError();
     }
-    // operands the 16-byte loads cannot serve take the element-wise kernel,
-    // 128 x 128 tiles in place of the 256 x 256 ones
-    const int kern = (!vec && (pl.kernel == K_BF16_HUGE8 || pl.kernel == K_BF16_MID)) ? K_BF16_LARGE : pl.kernel;
     int tm, tn;
     tiles_for(kern, M, N, gated, tm, tn);
     a.tiles_m = tm;

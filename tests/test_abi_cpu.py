@@ -76,6 +76,9 @@ def test_workspace_queries():
     # 896 gated tiles = 3 rounds + 128: the last 128 tiles are cut into two
     # K pieces each, whose fp32 256 x 256 partial tiles need a workspace
     assert T.tp_gate_up_workspace_bytes(8192, 8192, 3584, torch.bfloat16) == 128 * 2 * 256 * 256 * 4
+    # long K, few columns (the QKV projection at TP=16): 256 x 192 tiles, K
+    # split in two, two fp32 [M, N] partials
+    assert T.tp_linear_workspace_bytes(8192, 8192, 768, torch.bfloat16) == 2 * 8192 * 768 * 4
     # decode shapes (register-streaming kernel): one fp32 [64 x 16] partial
     # tile per K slice of at most 1024 and 16-row weight block
     assert T.tp_gate_up_workspace_bytes(64, 8192, 7168, torch.bfloat16) == 8 * (14336 // 16) * 4096

@@ -24,7 +24,7 @@ benchmark times):
   prefill down      8192 x 3584 -> 8192       256x256 paired-stage tiles, 4 full rounds
   decode gate_up      64 x 8192 -> 2 x 7168   register streaming, 8 K slices of 1024 + slice-order finish
   decode down         64 x 7168 -> 8192       register streaming, 7 K slices of 1024 + slice-order finish
-  QKV (TP=16)       8192 x 8192 -> 768        128x128 direct-to-LDS tiles
+  QKV (TP=16)       8192 x 8192 -> 768        256x192 paired-stage tiles, K split in two + split finish
   o_proj (TP=16)    8192 x  512 -> 8192       256x256 paired-stage tiles, K = 512
   LM head (TP=2)     512 x 1024 -> 75968 fp32 256x256 tiles, fp32 rows staged through LDS
   fp32 MLP (TP=2)     16 x 1024 -> 2 x 1536, 16 x 1536 -> 1024   fp32 small-M kernels

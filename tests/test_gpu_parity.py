@@ -431,6 +431,27 @@ def test_mid_tiles_linear_matches_oracle(n, k, m):
                                                       to_f64(bias) if bias is not None else None)) <= 1e-2
 
 
+@pytest.mark.parametrize("n,k,m", [(8100, 4096, 760), (8192, 8192, 768), (6000, 4224, 900)])
+def test_w192_split_tiles_linear_matches_oracle(n, k, m):
+    """256 x 192 paired-stage tiles with K split in two and the split finish
+    pass, chosen for long K when the two halves fill one round: (8100, 760)
+    leaves ragged last tiles in both dimensions (32 x 4 tiles x 2 halves),
+    (8192, 768) is the QKV projection at TP=16, (6000, 900) gives 24 x 5 x 2
+    = 240 units with K halves of 2112.  Bias and both output types."""
+    x = rnd((n, k), 1.0, 280, torch.bfloat16)
+    w = rnd((m, k), 0.05, 281, torch.bfloat16)
+    b = rnd((m,), 0.05, 282, torch.bfloat16)
+    rows = synth.sample_rows(n, 8, 283)
+    assert T.tp_linear_workspace_bytes(n, k, m, torch.bfloat16) == 2 * n * m * 4
+    for bias in (None, b):
+        ref = oracle.linear(to_f64(x)[rows], to_f64(w), to_f64(bias) if bias is not None else None)
+        for out_dt in (torch.bfloat16, torch.float32):
+            y = T.tp_linear_rank_forward(x, w, bias=bias, out_dtype=out_dt)
+            assert relf(to_f64(y)[rows], ref) <= 1e-2, (bias is None, out_dt)
+            assert relf(to_f64(y[-1:]), oracle.linear(to_f64(x)[-1:], to_f64(w),
+                                                      to_f64(bias) if bias is not None else None)) <= 1e-2
+
+
 @pytest.mark.parametrize("n,k,m", [(4100, 1024, 7800), (8192, 3584, 8192)])
 def test_paired_stage_tiles_linear_matches_oracle(n, k, m):
     """256 x 256 tiles with K a multiple of 64 (paired K = 64 LDS stages):
@@ -475,8 +496,9 @@ def test_paired_stage_tiles_gate_up_matches_oracle():
 def test_tail_split_not_used_for_short_k_or_one_round():
     # 594 tiles of 256 but K = 1024: pieces would be too short
     assert T.tp_linear_workspace_bytes(512, 1024, 75968, torch.bfloat16) == 0
-    # 384 tiles of 128 at two resident workgroups per CU: a single round
-    assert T.tp_linear_workspace_bytes(8192, 8192, 768, torch.bfloat16) == 0
+    # 256 tiles of 128 x 192 at one workgroup per CU (K = 2048, too short to
+    # split in two): a single round, no workspace
+    assert T.tp_linear_workspace_bytes(8192, 2048, 768, torch.bfloat16) == 0
 
 
 # --------------------------------------------------------------------------
