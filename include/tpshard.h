@@ -14,7 +14,9 @@
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless the comment says HOST.  The caller
  *     owns every buffer; the library keeps no pointer after a call returns and
- *     allocates no device memory (scratch space comes in through `workspace`).
+ *     allocates no device memory (scratch space comes in through `workspace`;
+ *     tp_mlp_rank_forward_noalloc uses a fixed array in the library image
+ *     instead, TP_NOALLOC_SCRATCH_BYTES per GPU).
  *   - Compute calls are asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream).  They never synchronize the device.
  *   - Tensors are dense and row-major.  A linear layer's weight is stored
