@@ -1,28 +1,38 @@
 // GEMMs of the rank shard: C[M, N] = A[M, K] . B[N, K]^T, both operands
 // contiguous along K (weights stored [out, in], x . W^T), and the fused
 // column-parallel gate_up form act = SiLU(A . G^T) * (A . U^T) with
-// B = [G ; U] (gate rows first).
+// B = [G ; U] (gate rows first).  bf16 operands, fp32 accumulation on MFMAs.
 //
-// bf16 path: MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulators.
-//   * Workgroup tile BM x BN x BK, WM x WN wavefronts, each wave owning a
-//     (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-//   * Global -> LDS: 16-byte loads, double-buffered LDS so the next K tile is
-//     fetched while MFMAs run on the current one; one barrier per K step.
-//   * LDS layout: each tile row is BK bf16 = BK/8 16-byte chunks; chunk c of
-//     row r is stored at position c ^ ((r ^ (r >> 3)) & 7), which keeps both
-//     the row-wise 16-byte stores and the MFMA fragment loads (32 rows, one
-//     chunk) free of bank conflicts for 32- and 64-bank LDS.
-//   * Gated epilogue: a tile loads BN/2 gate rows and the SAME BN/2 up rows;
-//     each wave's MFMA N-tiles are split half gate, half up, so a lane holds
-//     gate and up accumulators of the same (row, column) and applies
-//     SiLU(g) * u in registers.  Gate/up products never reach memory.
-//   * Split-K (small M): blockIdx.y picks a K range; fp32 partial sums go to
-//     a workspace and a finalize kernel adds the splits in order 0..S-1 and
-//     applies the epilogue (deterministic, no atomics).
-//   * Tile order: workgroups are dispatched round-robin over the 8 XCDs; the
+// Kernels, and the shapes plan_gemm gives them:
+//   * gemm_bf16_pipe_kernel: direct-to-LDS tiles on v_mfma_f32_16x16x32_bf16
+//     with a deep LDS pipeline -- 256 x 256 tiles for large products (paired
+//     K = 64 stages; a part-filled last round of tiles is cut into K pieces
+//     that tail_fixup_kernel adds), 256 x 192 tiles with K split in two and
+//     128 x 192 tiles for products with few output tiles, 64 x 128 tiles for
+//     the split-K tiles of small products.
+//   * gemm_bf16_dl_kernel: direct-to-LDS 128 x 128 tiles on 32x32x16 MFMAs,
+//     two workgroups per CU, for mid-sized products.
+//   * gemm_bf16_kernel: register-staged tiles with element-wise loads, for
+//     operands the 16-byte buffer loads cannot serve (unaligned, or K not a
+//     multiple of 8).
+//   * gemm_bf16_rs_kernel + rs_finalize_kernel: decode products (M <= 64)
+//     with the weights streamed from HBM straight into MFMA fragments, K
+//     cut into slices whose fp32 partial tiles the finish pass adds.
+//   * gemm_bf16_stream_kernel + stream_finalize_kernel: decode products too
+//     small in 16-row blocks for the register-streaming grid, streamed
+//     through an LDS ring.
+//   * splitk_finalize_kernel: adds split-K partials in split order and
+//     applies the epilogue.
+// Common to all of them:
+//   * gated epilogue: a tile loads BN/2 gate rows and the SAME BN/2 up rows,
+//     so a lane holds gate and up accumulators of the same (row, column) and
+//     applies SiLU(g) * u in registers; gate/up products never reach memory;
+//   * every partial sum (split-K, K pieces, K slices) is added in a fixed
+//     order by a finish pass: deterministic, no atomics;
+//   * tile order: workgroups are dispatched round-robin over the 8 XCDs; the
 //     linear block id is remapped so that each XCD receives a contiguous run
-//     of tiles, grouped GROUP_M tiles tall so that the weight tile and the
-//     activation tiles a run shares stay in that XCD's L2.
+//     of tiles, grouped GROUP_M tiles tall so that the operand panels a run
+//     shares stay in that XCD's L2.
 //
 // The fp32 kernels are in gemm_f32.hip.
 #include <stdlib.h>
@@ -257,6 +267,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[B
     }
 }
 
+// Register-staged tiles (v_mfma_f32_32x32x16_bf16): element-wise global
+// loads staged through registers into double-buffered LDS (the next K tile
+// is fetched while the MFMAs run on the current one; one barrier per K
+// step).  Each tile row is BK = 64 bf16 = 8 16-byte chunks, chunk c of row r
+// stored at position swz(r, c), which keeps the row-wise 16-byte stores and
+// the fragment loads (32 rows, one chunk) free of bank conflicts.
 // Output tile of one workgroup: BM rows of A (tokens) x BN rows of B
 // (weight rows = output columns; gated: BN/2 gate rows + the same BN/2 up
 // rows).  The weight fragment is the MFMA's A operand and the token fragment
@@ -998,10 +1014,11 @@ __device__ __forceinline__ void pipe_epilogue(const GemmArgs& p, bool tail, f32x
 }
 
 // Deep-pipelined direct-to-LDS kernel with 16x16x32 MFMAs (16-byte-aligned
-// operands, K a multiple of 8), for the 256 x 256 tiles.  PAIR (every K
-// range a multiple of 64) replaces the four single stages below by two
-// stages of K = 64, so that each DMA request is a whole 128-byte line (see
-// the PAIR branch); the rest of this comment describes single stages.
+// operands, K a multiple of 8): the 256 x 256, 256 x 192, 128 x 192 and
+// 64 x 128 tiles.  PAIR (every K range a multiple of 64; the only form the
+// 192-wide tiles take) replaces the four single stages below by two stages
+// of K = 64, so that each DMA request is a whole 128-byte line (see the PAIR
+// branch); the rest of this comment describes single stages.
 //   * MFMA shape: v_mfma_f32_16x16x32_bf16 moves half the accumulator data
 //     per flop of the 32x32x16 form; on this power-limited part that buys
 //     clock (measured ~15% more MFMA throughput on random operands).  Lane
@@ -2019,17 +2036,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool gated, tp_dtype dt) {
     if (M > 64) {
         tiles_for(K_BF16_HUGE8, M, N, gated, tm, tn);
         pl.kernel = (int64_t)tm * tn >= 512 ? K_BF16_HUGE8 : K_BF16_LARGE;
-        // fewer 256 x 256 tiles than two rounds: 128 x 192 tiles on the
-        // paired-stage kernel when they fill at least three quarters of the
-        // CUs (the QKV projection at TP=16: 8192 x 768 = 256 tiles, one per
-        // CU, where 128 x 128 tiles left a quarter of a round empty)
+        // Fewer 256 x 256 tiles than two rounds.  For long K first: 256 x 192
+        // tiles with K split in two when the two halves make one round that
+        // fills at least three quarters of the CUs (the QKV projection at
+        // TP=16: 8192 x 8192 -> 768 is 128 tiles x 2 halves).  Per flop they
+        // move 0.70x the operand bytes of 128 x 192 tiles from L2 to LDS, and
+        // these launches run at the L2 -> LDS rate (~10 TB/s over all CUs);
+        // the two fp32 halves are added in order by the split finish pass.
         //
-        // Before that, for long K: 256 x 192 tiles with K split in two when
-        // the two halves make one round that fills at least three quarters
-        // of the CUs.  Per flop they move 0.70x the operand bytes of 128 x 192
-        // tiles from L2 to LDS, and these launches run at the L2 -> LDS rate
-        // (~10 TB/s over all CUs); the two fp32 halves are added in order by
-        // the split finish pass.
+        // Otherwise 128 x 192 tiles on the paired-stage kernel when they fill
+        // at least three quarters of the CUs in every round (e.g. 8192 x 2048
+        // -> 768: 256 tiles, one per CU, where 128 x 128 tiles left a quarter
+        // of a round empty).
         if (pl.kernel == K_BF16_LARGE && !gated && K % 128 == 0 && K >= 4096) {
             int wm, wn;
             tiles_for(K_BF16_W192, M, N, gated, wm, wn);
