@@ -110,6 +110,24 @@ def test_silu_mul_matches_torch_silu_of_gate_times_up():
 # Linear layers: the pages' printed worked examples (bit-exact integers)
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("dtype", [np.float32, np.float64, np.uint16])
+def test_narrow_is_torch_narrow(dtype):
+    """The pages' loaders cut a shard with narrow(dim, start, length) and copy
+    it (Nano-vLLM walkthrough no. 22, §3 and §4): the oracle's narrow equals
+    torch.narrow on either dimension, and a cut along the other dimension
+    (a transposed reading) does not."""
+    rng = np.random.default_rng(7)
+    full = (rng.integers(0, 60000, size=(12, 10)) if dtype == np.uint16
+            else rng.standard_normal((12, 10))).astype(dtype)
+    tf = torch.from_numpy(full.astype(np.int64) if dtype == np.uint16 else full)
+    for dim, start, length in [(0, 0, 12), (0, 3, 4), (0, 11, 1), (1, 0, 10), (1, 2, 5), (1, 9, 1)]:
+        got = oracle.narrow(full, dim, start, length)
+        ref = tf.narrow(dim, start, length).numpy().astype(dtype)
+        assert got.dtype == full.dtype and np.array_equal(got, ref), (dim, start, length)
+    wrong = tf.narrow(1, 3, 4).numpy().astype(dtype)
+    assert not np.array_equal(oracle.narrow(full, 0, 3, 4)[:, :4], wrong[:4, :])
+
+
 def test_column_parallel_worked_example():
     g = gold("nano22_column_parallel.json")
     full = np.repeat(np.array(g["full_row_labels"], dtype=np.float32)[:, None],
