@@ -328,3 +328,30 @@ def test_load_errors():
     assert st == 2                    # 8 kv heads over 3 ranks
     st, _ = _status(L.tp_load_qkv, DUMMY, 0, 0, 6, 2, 4, 8, 0, 4, DUMMY, 1, DUMMY, 4096, NULL)
     assert st == 2                    # n_q 6 over 4 ranks
+
+
+def test_last_error_is_per_thread():
+    """tp_last_error() keeps each host thread's own message: a failure on one
+    thread neither overwrites nor clears another thread's, and a successful
+    host-only call clears only the caller's."""
+    import threading
+    L = T.lib()
+    assert L.tp_vocab_range(10, 5, 2, ctypes.byref(ctypes.c_int64()), ctypes.byref(ctypes.c_int64())) != 0
+    mine = L.tp_last_error().decode()
+    assert mine
+    seen = {}
+
+    def other():
+        seen["before"] = L.tp_last_error().decode()
+        st = L.tp_kv_heads_for_rank(3, 0, 2, ctypes.byref(ctypes.c_int64()), ctypes.byref(ctypes.c_int64()))
+        seen["status"] = st
+        seen["after"] = L.tp_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["before"] == ""
+    assert seen["status"] != 0 and seen["after"] and seen["after"] != mine
+    assert L.tp_last_error().decode() == mine
+    assert L.tp_vocab_range(10, 1, 2, ctypes.byref(ctypes.c_int64()), ctypes.byref(ctypes.c_int64())) == 0
+    assert L.tp_last_error().decode() == ""
