@@ -2148,13 +2148,12 @@ static void launch_reg_one(const GemmArgs& a, int splits, hipStream_t s) {
     const size_t lds = (size_t)2 * (BM + BN) * 64 * sizeof(uint16_t);
     auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI>;
     if (lds > 65536) {
-        // opt in to more than 64 KiB of LDS once per instantiation
-        static bool done = false;
-        if (!done) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            done = true;
-        }
+        // opt in to more than 64 KiB of LDS once per instantiation (a
+        // function-local static: initialised once, thread-safe)
+        static const bool opted_in = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         (int)lds) == hipSuccess;
+        (void)opted_in;
     }
     dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
     hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), lds, s, a);
